@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark: fp16 GEMM-NT at M = N = K = 8192 on one MI355X, plus GEMV and
+split-K on their workloads, with roofline fractions and the CPU oracle timed
+on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+One step is one C = A . B^T call at 8192^3 (fp16 in, fp32 accumulate, fp16
+out) on torch's current stream with A and B already resident in HBM.  The
+headline value is whole-job TFLOP/s over the timed steps (wall clock,
+bracketed by device synchronisation).  The GEMV (N = K = 8192 and 1024) and
+split-K (M = N = 1024, K = 16384) figures are reported in "extra", each
+timed with HIP events on the launching stream; GEMV rotates over enough W
+copies (> 512 MiB) that every call streams W from HBM, not from the 256 MiB
+MALL.  Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemv_fp16_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hpp", ".hip", ".def")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel + "|" + workload)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_calls(torch, fn, reps, warmup, prep=None):
+    """Average and median seconds of fn() over reps, HIP events on the current stream."""
+    for i in range(warmup):
+        if prep:
+            prep(i)
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    stream = torch.cuda.current_stream()
+    for i in range(reps):
+        if prep:
+            prep(i)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        times.append((s, e))
+    torch.cuda.synchronize()
+    ms = np.array([s.elapsed_time(e) for s, e in times])
+    return float(ms.mean()) * 1e-3, float(np.median(ms)) * 1e-3
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="rows of the 8192^3 product the CPU oracle computes")
+    ap.add_argument("--no-extra", action="store_true", help="headline GEMM only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemv_fp16_amd as gf
+    import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gf.lib()
+    torch.cuda.set_device(0)
+
+    M = N = K = 8192
+    log("generating A, B %dx%d fp16 uniform[-1,1] seed 0" % (M, K))
+    A_np = inputs.uniform_f16((M, K), 0, inputs.STREAM_A)
+    B_np = inputs.uniform_f16((N, K), 0, inputs.STREAM_B)
+    A = torch.from_numpy(A_np).cuda()
+    B = torch.from_numpy(B_np).cuda()
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    cfg = gf.gemm_default_config(M, N, K)
+    flops = 2.0 * M * N * K
+
+    def step():
+        gf.gemm_f16_nt(A, B, C)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = []
+    log("timing %d steps" % args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        step()
+        e.record(stream)
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_s = float(np.mean([s.elapsed_time(e) for s, e in evs])) * 1e-3
+    value = flops * args.steps / elapsed / 1e12
+    achieved = flops / kern_s / 1e12
+    log("gemm 8192^3: %.1f TFLOP/s wall, %.1f TFLOP/s per launch (%.3f ms)" %
+        (value, achieved, kern_s * 1e3))
+
+    out = {
+        "metric": "fp16 GEMM TFLOP/s at M=N=K=8192 (% MFMA peak); GEMV GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "gemm_f16_nt C=A.B^T M=N=K=8192, A,B fp16 uniform[-1,1] seed 0",
+                   "M": M, "N": N, "K": K, "tile": cfg},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": measured_traffic("gemm_nt_kernel", "8192^3")},
+    }
+
+    extra = {}
+    if not args.no_extra:
+        # ---- GEMM, K swept ----
+        sweep = {}
+        for k2 in (1024, 4096, 16384):
+            a2 = torch.from_numpy(inputs.uniform_f16((M, k2), 0, 0)).cuda()
+            b2 = torch.from_numpy(inputs.uniform_f16((N, k2), 0, 1)).cuda()
+            avg, med = time_calls(torch, lambda: gf.gemm_f16_nt(a2, b2, C), 10, 3)
+            sweep[str(k2)] = round(2.0 * M * N * k2 / avg / 1e12, 1)
+            log("gemm 8192x8192x%d: %.1f TFLOP/s" % (k2, sweep[str(k2)]))
+            del a2, b2
+        sweep[str(K)] = round(achieved, 1)
+        extra["gemm_k_sweep_tflops"] = sweep
+
+        # ---- GEMV ----
+        gemv = {}
+        for nk in (8192, 1024):
+            wbytes = nk * nk * 2
+            copies = max(1, -(-(640 << 20) // wbytes))
+            copies = min(copies, 64)
+            Ws = [torch.from_numpy(inputs.uniform_f16((nk, nk), i, 0)).cuda() for i in range(copies)]
+            x = torch.from_numpy(inputs.uniform_f16((nk,), 0, 1)).cuda()
+            y = torch.empty((nk,), dtype=torch.float16, device="cuda")
+            state = {"i": 0}
+
+            def prep(i, Ws=Ws, state=state):
+                state["i"] = i % len(Ws)
+
+            avg, med = time_calls(torch, lambda: gf.gemv_f16(Ws[state["i"]], x, y), 200, 20, prep)
+            bytes_ = 2.0 * nk * nk + 2.0 * nk + 2.0 * nk
+            gbs = bytes_ / med / 1e9
+            warm_avg, warm_med = time_calls(torch, lambda: gf.gemv_f16(Ws[0], x, y), 200, 20)
+            gemv[str(nk)] = {
+                "us": round(med * 1e6, 3), "GB/s": round(gbs, 1),
+                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                "w_copies_rotated": copies,
+                "cache_warm_GB/s_not_hbm": round(bytes_ / warm_med / 1e9, 1),
+                "launch": gf.gemv_default_config(nk, nk),
+            }
+            log("gemv %d: %.2f us, %.1f GB/s (warm %.1f)" %
+                (nk, med * 1e6, gbs, gemv[str(nk)]["cache_warm_GB/s_not_hbm"]))
+            del Ws
+        g8 = gemv["8192"]
+        gemv["roofline"] = {"bound": "hbm", "achieved": g8["GB/s"], "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": g8["frac_hbm_peak"],
+                            "traffic": measured_traffic("gemv_kernel", "8192^2")}
+        extra["gemv"] = gemv
+
+        # ---- split-K ----
+        sm, sk_k = 1024, 16384
+        a3 = torch.from_numpy(inputs.uniform_f16((sm, sk_k), 0, 0)).cuda()
+        b3 = torch.from_numpy(inputs.uniform_f16((sm, sk_k), 0, 1)).cuda()
+        c3 = torch.empty((sm, sm), dtype=torch.float32, device="cuda")
+        ws = torch.empty(16 * sm * sm, dtype=torch.float32, device="cuda")
+        sk = {}
+        f3 = 2.0 * sm * sm * sk_k
+        for split in (4, 8, 16):
+            for mode, name in ((gf.GF_SPLITK_ATOMIC, "atomic"), (gf.GF_SPLITK_TWOPASS, "twopass")):
+                avg, med = time_calls(torch, lambda: gf.gemm_f16_nt_splitk_ex(
+                    a3, b3, c3, split, mode, ws), 50, 5)
+                sk["%s_s%d" % (name, split)] = round(f3 / med / 1e12, 1)
+        c16 = torch.empty((sm, sm), dtype=torch.float16, device="cuda")
+        avg, med = time_calls(torch, lambda: gf.gemm_f16_nt(a3, b3, c16), 50, 5)
+        sk["no_split_fp16"] = round(f3 / med / 1e12, 1)
+        log("splitk 1024x1024x16384 TFLOP/s: %s" % sk)
+        extra["splitk_1024x1024x16384_tflops"] = sk
+        del a3, b3, c3, ws
+
+    if not args.no_cpu:
+        import oracle
+        rows = max(1, min(args.cpu_rows, M))
+        log("cpu oracle: %d rows of the 8192^3 product" % rows)
+        t = time.perf_counter()
+        oracle.gemm_nt_f16(A_np, B_np, rows=(0, rows))
+        dt = time.perf_counter() - t
+        out["cpu_baseline"] = {
+            "value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": "rows 0..%d of C = A.B^T at M=N=K=8192 (%d x 8192 outputs, double "
+                      "accumulation), %.1f s wall" % (rows - 1, rows, dt),
+        }
+        log("cpu oracle: %.3g TFLOP/s on %d threads (%.1f s)" %
+            (out["cpu_baseline"]["value"], oracle.threads(), dt))
+
+    if extra:
+        out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+"""Python binding for libgemvfp16 (fp16 GEMM-NT, split-K GEMM, GEMV on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgemvfp16.so``; torch supplies device memory and the stream.
+The functions carry the C-ABI names (include/gemvfp16.h).  A missing library
+raises at the first call; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemvfp16.so")
+
+GF_OK, GF_ERR_INVALID_ARG, GF_ERR_HIP, GF_ERR_UNSUPPORTED = 0, 1, 2, 3
+GF_SPLITK_ATOMIC, GF_SPLITK_TWOPASS = 0, 1
+
+EXPORTS = (
+    "gemm_f16_nt", "gemm_f16_nt_splitk", "gemv_f16",
+    "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex",
+    "gemm_f16_nt_cfg", "gemv_f16_cfg",
+    "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
+    "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
+)
+
+
+class GemmCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("block_m", "block_n", "block_k", "stages", "threads", "raster")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class GemvCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("rows_per_wave", "unroll", "waves")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libgemvfp16.so is not built (python -m gemv_fp16_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.gemm_f16_nt.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+    L.gemm_f16_nt_splitk.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
+    L.gemv_f16.argtypes = [vp, vp, vp, ci, ci, vp]
+    L.gemm_f16_nt_splitk_workspace_bytes.argtypes = [ci, ci, ci]
+    L.gemm_f16_nt_splitk_workspace_bytes.restype = sz
+    L.gemm_f16_nt_splitk_ex.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
+    L.gemm_f16_nt_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.POINTER(GemmCfg), vp]
+    L.gemv_f16_cfg.argtypes = [vp, vp, vp, ci, ci, ctypes.POINTER(GemvCfg), vp]
+    L.gf_gemm_config_get.argtypes = [ci, ctypes.POINTER(GemmCfg)]
+    L.gf_gemv_config_get.argtypes = [ci, ctypes.POINTER(GemvCfg)]
+    L.gf_gemm_default_config.argtypes = [ci, ci, ci, ctypes.POINTER(GemmCfg)]
+    L.gf_gemv_default_config.argtypes = [ci, ci, ctypes.POINTER(GemvCfg)]
+    L.gf_status_string.argtypes = [ci]
+    L.gf_status_string.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name not in ("gemm_f16_nt_splitk_workspace_bytes", "gf_status_string"):
+            getattr(L, name).restype = ci
+    _lib = L
+    return L
+
+
+def status_string(rc: int) -> str:
+    return lib().gf_status_string(rc).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != GF_OK:
+        raise RuntimeError("%s: %s" % (what, status_string(rc)))
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# configs
+# ---------------------------------------------------------------------------
+
+def gemm_configs() -> list[tuple[dict, bool]]:
+    """Every GEMM tile config in the library, with whether a kernel exists."""
+    L, out = lib(), []
+    for i in range(L.gf_gemm_config_count()):
+        c = GemmCfg()
+        rc = L.gf_gemm_config_get(i, ctypes.byref(c))
+        out.append((c.as_dict(), rc == GF_OK))
+    return out
+
+
+def gemv_configs() -> list[dict]:
+    L, out = lib(), []
+    for i in range(L.gf_gemv_config_count()):
+        c = GemvCfg()
+        _check(L.gf_gemv_config_get(i, ctypes.byref(c)), "gf_gemv_config_get")
+        out.append(c.as_dict())
+    return out
+
+
+def gemm_default_config(M: int, N: int, K: int) -> dict:
+    c = GemmCfg()
+    _check(lib().gf_gemm_default_config(M, N, K, ctypes.byref(c)), "gf_gemm_default_config")
+    return c.as_dict()
+
+
+def gemv_default_config(N: int, K: int) -> dict:
+    c = GemvCfg()
+    _check(lib().gf_gemv_default_config(N, K, ctypes.byref(c)), "gf_gemv_default_config")
+    return c.as_dict()
+
+
+# ---------------------------------------------------------------------------
+# operations on torch tensors
+# ---------------------------------------------------------------------------
+
+def _gemm_shapes(A, B):
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError("A must be (M, K) and B (N, K)")
+    return A.shape[0], B.shape[0], A.shape[1]
+
+
+def gemm_f16_nt(A, B, C=None, stream=None, cfg: dict | None = None):
+    """C = A . B^T (fp16 in, fp32 accumulate, fp16 out).  Returns C."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be (M, N)")
+    args = (_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"), _dev(C, torch.float16, "C"),
+            M, N, K)
+    if cfg is None:
+        _check(lib().gemm_f16_nt(*args, _stream(stream)), "gemm_f16_nt")
+    else:
+        c = GemmCfg(**cfg)
+        _check(lib().gemm_f16_nt_cfg(*args, ctypes.byref(c), _stream(stream)), "gemm_f16_nt_cfg")
+    return C
+
+
+def gemm_f16_nt_splitk_workspace_bytes(M: int, N: int, split_k: int) -> int:
+    return int(lib().gemm_f16_nt_splitk_workspace_bytes(M, N, split_k))
+
+
+def gemm_f16_nt_splitk(A, B, C32=None, split_k: int = 4, stream=None):
+    """C32 = A . B^T in fp32 via split-K with fp32 atomic combine."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    if C32 is None:
+        C32 = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C32.shape) != (M, N):
+        raise ValueError("C32 must be (M, N)")
+    _check(lib().gemm_f16_nt_splitk(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
+                                    _dev(C32, torch.float32, "C32"), M, N, K, split_k,
+                                    _stream(stream)), "gemm_f16_nt_splitk")
+    return C32
+
+
+def gemm_f16_nt_splitk_ex(A, B, C32=None, split_k: int = 4, mode: int = GF_SPLITK_TWOPASS,
+                          workspace=None, stream=None):
+    """Split-K with mode GF_SPLITK_ATOMIC or GF_SPLITK_TWOPASS (deterministic).
+
+    In two-pass mode a workspace (fp32 CUDA tensor of at least
+    gemm_f16_nt_splitk_workspace_bytes bytes) is allocated if not given."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    if C32 is None:
+        C32 = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
+    if mode == GF_SPLITK_TWOPASS:
+        need = gemm_f16_nt_splitk_workspace_bytes(M, N, split_k)
+        if workspace is None:
+            workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=A.device)
+        ws_ptr = _dev(workspace, torch.float32, "workspace")
+        ws_bytes = workspace.numel() * 4
+    _check(lib().gemm_f16_nt_splitk_ex(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
+                                       _dev(C32, torch.float32, "C32"), M, N, K, split_k, mode,
+                                       ws_ptr, ws_bytes, _stream(stream)), "gemm_f16_nt_splitk_ex")
+    return C32
+
+
+def gemv_f16(W, x, y=None, stream=None, cfg: dict | None = None):
+    """y = W . x (fp16 in, fp32 accumulate, fp16 out).  Returns y."""
+    import torch
+    if W.dim() != 2 or x.dim() != 1 or W.shape[1] != x.shape[0]:
+        raise ValueError("W must be (N, K) and x (K,)")
+    N, K = W.shape
+    if y is None:
+        y = torch.empty((N,), dtype=torch.float16, device=W.device)
+    if tuple(y.shape) != (N,):
+        raise ValueError("y must be (N,)")
+    args = (_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y"), N, K)
+    if cfg is None:
+        _check(lib().gemv_f16(*args, _stream(stream)), "gemv_f16")
+    else:
+        c = GemvCfg(**cfg)
+        _check(lib().gemv_f16_cfg(*args, ctypes.byref(c), _stream(stream)), "gemv_f16_cfg")
+    return y

@@ -1,0 +1,328 @@
+// C-ABI entry points: argument validation, config choice and launches.
+// Validation runs entirely on the host before any HIP call, so invalid
+// arguments never touch the device.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/gemvfp16.h"
+#include "configs.hpp"
+
+namespace gf {
+
+GemmLaunchFn g_gemm_table[kNumGemm][6] = {};
+
+namespace {
+
+constexpr int kDefaultPanel = 10;   // tile-rows per raster panel when raster == 1
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int validate_gemm(const void* A, const void* B, const void* C, int M, int N, int K, int c_align)
+{
+    if (M < 0 || N < 0 || K < 0) return GF_ERR_INVALID_ARG;
+    if ((int64_t)M * K > kMaxElems || (int64_t)N * K > kMaxElems || (int64_t)M * N > kMaxElems)
+        return GF_ERR_INVALID_ARG;
+    if (M > 0 && K > 0 && (!A || !aligned(A, 2))) return GF_ERR_INVALID_ARG;
+    if (N > 0 && K > 0 && (!B || !aligned(B, 2))) return GF_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && (!C || !aligned(C, c_align))) return GF_ERR_INVALID_ARG;
+    return GF_OK;
+}
+
+int find_gemm(const gf_gemm_cfg& c)
+{
+    for (int i = 0; i < kNumGemm; ++i) {
+        const GemmDesc& d = kGemmConfigs[i];
+        if (d.bm == c.block_m && d.bn == c.block_n && d.bk == c.block_k && d.stages == c.stages &&
+            d.threads == c.threads)
+            return i;
+    }
+    return -1;
+}
+
+int panel_of(int raster) { return raster <= 0 ? 0 : (raster == 1 ? kDefaultPanel : raster); }
+
+gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster)
+{
+    gf_gemm_cfg c;
+    c.block_m = bm; c.block_n = bn; c.block_k = bk; c.stages = s; c.threads = t; c.raster = raster;
+    return c;
+}
+
+// The tile config for a shape: the largest tile that still gives every CU
+// at least one workgroup.
+gf_gemm_cfg default_gemm_cfg(int M, int N, int /*K*/)
+{
+    const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+    const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
+    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 256, 1);
+    if (t128 >= 128) return make_cfg(128, 128, 64, 2, 256, 1);
+    return make_cfg(64, 64, 64, 2, 256, 1);
+}
+
+gf_gemm_cfg default_splitk_cfg(int M, int N, int K)
+{
+    (void)M; (void)N; (void)K;
+    return make_cfg(128, 128, 64, 2, 256, 1);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GF_OK : GF_ERR_HIP; }
+
+// One GEMM launch of epilogue `epi` over `slices` K slices of kt_per tiles.
+int run_gemm(const void* A, const void* B, void* C, int M, int N, int K, const gf_gemm_cfg& cfg,
+             int epi, int slices, int kt_per, bool c16_aligned, hipStream_t stream)
+{
+    const int idx = find_gemm(cfg);
+    if (idx < 0) return GF_ERR_UNSUPPORTED;
+    const bool al = aligned(A, 16) && aligned(B, 16) && (K % 8 == 0) && c16_aligned;
+    GemmLaunchFn fn = g_gemm_table[idx][epi * 2 + (al ? 1 : 0)];
+    if (!fn) return GF_ERR_UNSUPPORTED;
+    GemmArgs a;
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = C;
+    a.M = M; a.N = N; a.K = K;
+    a.kt_per_slice = kt_per;
+    a.raster = panel_of(cfg.raster);
+    return launch_status(fn(a, slices, stream));
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = i; t < n; t += stride) p[t] = 0.0f;
+}
+
+__global__ void zero_f32x4_kernel(floatx4* __restrict__ p, int64_t n4)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = i; t < n4; t += stride) p[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// C32[i] = sum over s = 0 .. slices-1, ascending, of ws[s][i].
+__global__ void splitk_reduce_x4_kernel(const floatx4* __restrict__ ws, floatx4* __restrict__ c,
+                                        int64_t n4, int slices)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = i; t < n4; t += stride) {
+        floatx4 s = ws[t];
+        for (int k = 1; k < slices; ++k) s += ws[(int64_t)k * n4 + t];
+        c[t] = s;
+    }
+}
+
+__global__ void splitk_reduce_kernel(const float* __restrict__ ws, float* __restrict__ c, int64_t n,
+                                     int slices)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = i; t < n; t += stride) {
+        float s = ws[t];
+        for (int k = 1; k < slices; ++k) s += ws[(int64_t)k * n + t];
+        c[t] = s;
+    }
+}
+
+int grid_for(int64_t n, int block)
+{
+    int64_t g = (n + block - 1) / block;
+    if (g > 8192) g = 8192;
+    return (int)(g < 1 ? 1 : g);
+}
+
+int zero_f32(float* p, int64_t n, hipStream_t stream)
+{
+    if (aligned(p, 16) && n % 4 == 0) {
+        hipLaunchKernelGGL(zero_f32x4_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, stream,
+                           reinterpret_cast<floatx4*>(p), n / 4);
+    } else {
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, p, n);
+    }
+    return launch_status(hipGetLastError());
+}
+
+int splitk_impl(const void* A, const void* B, float* C32, int M, int N, int K, int split_k,
+                int mode, void* ws, size_t ws_bytes, const gf_gemm_cfg& cfg, hipStream_t stream)
+{
+    int rc = validate_gemm(A, B, C32, M, N, K, 4);
+    if (rc) return rc;
+    if (split_k < 1 || split_k > 65535) return GF_ERR_INVALID_ARG;
+    if (mode != GF_SPLITK_ATOMIC && mode != GF_SPLITK_TWOPASS) return GF_ERR_INVALID_ARG;
+    const int64_t mn = (int64_t)M * N;
+    if (mode == GF_SPLITK_TWOPASS) {
+        if ((uint64_t)ws_bytes < (uint64_t)split_k * (uint64_t)mn * sizeof(float)) return GF_ERR_INVALID_ARG;
+        if (mn > 0 && (!ws || !aligned(ws, 4))) return GF_ERR_INVALID_ARG;
+    }
+    if (find_gemm(cfg) < 0) return GF_ERR_UNSUPPORTED;
+    if (mn == 0) return GF_OK;
+
+    // Tile-aligned slices: kt_per K tiles each; only non-empty slices run.
+    const int nkt = ceil_div(K, cfg.block_k);
+    const int kt_per = nkt > 0 ? ceil_div(nkt, split_k) : 0;
+    const int slices = nkt > 0 ? ceil_div(nkt, kt_per) : 0;
+
+    if (mode == GF_SPLITK_ATOMIC || slices == 0) {
+        rc = zero_f32(C32, mn, stream);
+        if (rc || slices == 0) return rc;
+        return run_gemm(A, B, C32, M, N, K, cfg, EPI_F32_ATOMIC, slices, kt_per, true, stream);
+    }
+    rc = run_gemm(A, B, ws, M, N, K, cfg, EPI_F32_STORE, slices, kt_per, true, stream);
+    if (rc) return rc;
+    if (aligned(ws, 16) && aligned(C32, 16) && mn % 4 == 0) {
+        hipLaunchKernelGGL(splitk_reduce_x4_kernel, dim3(grid_for(mn / 4, 256)), dim3(256), 0, stream,
+                           reinterpret_cast<const floatx4*>(ws), reinterpret_cast<floatx4*>(C32),
+                           mn / 4, slices);
+    } else {
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
+                           static_cast<const float*>(ws), C32, mn, slices);
+    }
+    return launch_status(hipGetLastError());
+}
+
+int find_gemv(const gf_gemv_cfg& c)
+{
+    for (int i = 0; i < kNumGemv; ++i) {
+        const GemvDesc& d = kGemvConfigs[i];
+        if (d.rows == c.rows_per_wave && d.unroll == c.unroll && d.waves == c.waves) return i;
+    }
+    return -1;
+}
+
+gf_gemv_cfg default_gemv_cfg(int N, int K)
+{
+    gf_gemv_cfg c;
+    if ((int64_t)N * K >= (int64_t)4096 * 4096) {
+        c.rows_per_wave = 2; c.unroll = 4; c.waves = 4;
+    } else {
+        c.rows_per_wave = 1; c.unroll = 2; c.waves = 4;
+    }
+    return c;
+}
+
+int gemv_impl(const void* W, const void* x, void* y, int N, int K, const gf_gemv_cfg& cfg,
+              hipStream_t stream)
+{
+    if (N < 0 || K < 0 || (int64_t)N * K > kMaxElems) return GF_ERR_INVALID_ARG;
+    if (N > 0 && K > 0 && (!W || !aligned(W, 2))) return GF_ERR_INVALID_ARG;
+    if (N > 0 && K > 0 && (!x || !aligned(x, 2))) return GF_ERR_INVALID_ARG;
+    if (N > 0 && (!y || !aligned(y, 2))) return GF_ERR_INVALID_ARG;
+    const int idx = find_gemv(cfg);
+    if (idx < 0) return GF_ERR_UNSUPPORTED;
+    if (N == 0) return GF_OK;
+    const bool al = aligned(W, 16) && aligned(x, 16) && K % 8 == 0;
+    GemvLaunchFn fn = g_gemv_table[idx][al ? 1 : 0];
+    if (!fn) return GF_ERR_UNSUPPORTED;
+    return launch_status(fn(static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(x),
+                            static_cast<uint16_t*>(y), N, K, stream));
+}
+
+}  // namespace
+}  // namespace gf
+
+using namespace gf;
+
+extern "C" {
+
+int gemm_f16_nt_cfg(const void* A, const void* B, void* C, int M, int N, int K,
+                    const gf_gemm_cfg* cfg, void* stream)
+{
+    if (!cfg) return GF_ERR_INVALID_ARG;
+    int rc = validate_gemm(A, B, C, M, N, K, 2);
+    if (rc) return rc;
+    if (find_gemm(*cfg) < 0) return GF_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GF_OK;
+    const int nkt = ceil_div(K, cfg->block_k);
+    return run_gemm(A, B, C, M, N, K, *cfg, EPI_F16, 1, nkt, aligned(C, 16),
+                    static_cast<hipStream_t>(stream));
+}
+
+int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void* stream)
+{
+    const gf_gemm_cfg cfg = default_gemm_cfg(M, N, K);
+    return gemm_f16_nt_cfg(A, B, C, M, N, K, &cfg, stream);
+}
+
+int gemm_f16_nt_splitk(const void* A, const void* B, float* C32, int M, int N, int K, int split_k,
+                       void* stream)
+{
+    return splitk_impl(A, B, C32, M, N, K, split_k, GF_SPLITK_ATOMIC, nullptr, 0,
+                       default_splitk_cfg(M, N, K), static_cast<hipStream_t>(stream));
+}
+
+size_t gemm_f16_nt_splitk_workspace_bytes(int M, int N, int split_k)
+{
+    if (M < 0 || N < 0 || split_k < 1) return 0;
+    return (size_t)split_k * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N, int K, int split_k,
+                          int mode, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return splitk_impl(A, B, C32, M, N, K, split_k, mode, workspace, workspace_bytes,
+                       default_splitk_cfg(M, N, K), static_cast<hipStream_t>(stream));
+}
+
+int gemv_f16_cfg(const void* W, const void* x, void* y, int N, int K, const gf_gemv_cfg* cfg,
+                 void* stream)
+{
+    if (!cfg) return GF_ERR_INVALID_ARG;
+    return gemv_impl(W, x, y, N, K, *cfg, static_cast<hipStream_t>(stream));
+}
+
+int gemv_f16(const void* W, const void* x, void* y, int N, int K, void* stream)
+{
+    const gf_gemv_cfg cfg = default_gemv_cfg(N, K);
+    return gemv_impl(W, x, y, N, K, cfg, static_cast<hipStream_t>(stream));
+}
+
+int gf_gemm_config_count(void) { return kNumGemm; }
+
+int gf_gemm_config_get(int i, gf_gemm_cfg* out)
+{
+    if (i < 0 || i >= kNumGemm || !out) return GF_ERR_INVALID_ARG;
+    const GemmDesc& d = kGemmConfigs[i];
+    *out = make_cfg(d.bm, d.bn, d.bk, d.stages, d.threads, 1);
+    // A config with no compiled kernel (illegal LDS or wave layout) is unsupported.
+    return g_gemm_table[i][EPI_F16 * 2 + 1] ? GF_OK : GF_ERR_UNSUPPORTED;
+}
+
+int gf_gemv_config_count(void) { return kNumGemv; }
+
+int gf_gemv_config_get(int i, gf_gemv_cfg* out)
+{
+    if (i < 0 || i >= kNumGemv || !out) return GF_ERR_INVALID_ARG;
+    out->rows_per_wave = kGemvConfigs[i].rows;
+    out->unroll = kGemvConfigs[i].unroll;
+    out->waves = kGemvConfigs[i].waves;
+    return GF_OK;
+}
+
+int gf_gemm_default_config(int M, int N, int K, gf_gemm_cfg* out)
+{
+    if (!out || M < 0 || N < 0 || K < 0) return GF_ERR_INVALID_ARG;
+    *out = default_gemm_cfg(M, N, K);
+    return GF_OK;
+}
+
+int gf_gemv_default_config(int N, int K, gf_gemv_cfg* out)
+{
+    if (!out || N < 0 || K < 0) return GF_ERR_INVALID_ARG;
+    *out = default_gemv_cfg(N, K);
+    return GF_OK;
+}
+
+const char* gf_status_string(int status)
+{
+    switch (status) {
+    case GF_OK: return "GF_OK";
+    case GF_ERR_INVALID_ARG: return "GF_ERR_INVALID_ARG: invalid argument";
+    case GF_ERR_HIP: return "GF_ERR_HIP: HIP runtime error at launch";
+    case GF_ERR_UNSUPPORTED: return "GF_ERR_UNSUPPORTED: no compiled kernel for this config";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

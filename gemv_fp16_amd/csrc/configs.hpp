@@ -1,0 +1,43 @@
+// Registry of the compiled kernel instantiations (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+#include "gemm_kernel.hpp"
+
+namespace gf {
+
+struct GemmDesc {
+    int bm, bn, bk, stages, threads;
+    bool core;
+};
+
+constexpr GemmDesc kGemmConfigs[] = {
+#define GF_GEMM(BM, BN, BK, S, T, CORE) {BM, BN, BK, S, T, CORE != 0},
+#include "gemm_configs.def"
+#undef GF_GEMM
+};
+constexpr int kNumGemm = sizeof(kGemmConfigs) / sizeof(kGemmConfigs[0]);
+
+struct GemvDesc {
+    int rows, unroll, waves;
+};
+
+constexpr GemvDesc kGemvConfigs[] = {
+#define GF_GEMV(R, U, W) {R, U, W},
+#include "gemv_configs.def"
+#undef GF_GEMV
+};
+constexpr int kNumGemv = sizeof(kGemvConfigs) / sizeof(kGemvConfigs[0]);
+
+typedef hipError_t (*GemmLaunchFn)(const GemmArgs&, int slices, hipStream_t);
+typedef hipError_t (*GemvLaunchFn)(const uint16_t*, const uint16_t*, uint16_t*, int, int,
+                                   hipStream_t);
+
+// [config][epilogue * 2 + aligned]; nullptr = not compiled.
+extern GemmLaunchFn g_gemm_table[kNumGemm][6];
+// [config][aligned]
+extern GemvLaunchFn g_gemv_table[kNumGemv][2];
+
+// Instantiation shards (one object file each, compiled in parallel).
+constexpr int kGemmShards = 8;
+
+}  // namespace gf

@@ -1,0 +1,142 @@
+/*
+ * gemvfp16 -- fp16 NT matrix product, split-K matrix product and GEMV for
+ * AMD Instinct MI355X (gfx950), as a C-ABI shared library (libgemvfp16.so).
+ *
+ * Common conventions for every entry point
+ *  - fp16 means IEEE binary16; fp16 buffers are passed as void* and hold raw
+ *    binary16 bit patterns.  Every matrix is row-major and contiguous.
+ *  - Every data pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *    tensor).  The caller allocates and owns every buffer; the library keeps
+ *    no pointer after the call returns and allocates nothing the caller sees.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on that stream and never synchronise; buffers
+ *    must stay alive until that work has completed.
+ *  - Outputs are overwritten (no alpha/beta) and must not alias any input.
+ *  - Return value: GF_OK, or a GF_ERR_* code (gf_status_string() names it).
+ *    Argument errors are detected on the host before anything is enqueued.
+ *    A fault that happens later on the device surfaces at the caller's next
+ *    synchronisation, as with any HIP library.  Nothing is printed.
+ *  - Degenerate shapes: M == 0 or N == 0 is a no-op returning GF_OK; K == 0
+ *    writes +0 everywhere (the empty sum).
+ *  - Any M, N, K >= 0 is accepted.  The fast path (128-bit loads and stores)
+ *    is taken when every base pointer is 16-byte aligned and K % 8 == 0
+ *    (and N % 8 == 0 for the fp16 C stores); otherwise a masked path that
+ *    needs only 2-byte alignment computes the same result.
+ *  - Each operand must be smaller than 2^31 elements.
+ */
+#ifndef GEMVFP16_H
+#define GEMVFP16_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GF_OK = 0,
+    GF_ERR_INVALID_ARG = 1,   /* bad size, NULL or misaligned pointer, bad mode */
+    GF_ERR_HIP = 2,           /* the HIP runtime reported an error at launch */
+    GF_ERR_UNSUPPORTED = 3    /* no compiled kernel for the requested config */
+};
+
+enum { GF_SPLITK_ATOMIC = 0, GF_SPLITK_TWOPASS = 1 };
+
+/*
+ * C = A . B^T.  A is M x K fp16, B is N x K fp16, C is M x N fp16.
+ * Products are accumulated in fp32 and each result is rounded once to fp16
+ * (round-to-nearest-even).
+ * Defined by the TileLang FP16 matmul autotune benchmark page, sections 1
+ * and 2 (C = A B^T with A(M,K), B(N,K), C(M,N), fp16 operands, fp32
+ * accumulation, transpose_B) and the autotune tutorial page's reference().
+ */
+int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void* stream);
+
+/*
+ * Split-K form of the same product with an fp32 output:
+ * C32 = A . B^T, A M x K fp16, B N x K fp16, C32 M x N float.
+ * K is cut into split_k contiguous slices (tile-aligned; the last may be
+ * short and any may be empty); each slice's partial product is computed by
+ * its own workgroups and added into C32 with fp32 global atomics.  C32 is
+ * zeroed by the call itself, on the stream.  The order of the atomic adds is
+ * not fixed, so results can differ in the last bits from run to run (they
+ * are exact whenever every partial sum is exactly representable).
+ * split_k must be >= 1.
+ * Defined by the "basic GEMM to SplitK" page, SplitK section (grid dimension
+ * over K slices, out_dtype float32, per-element atomic add into C).
+ */
+int gemm_f16_nt_splitk(const void* A, const void* B, float* C32, int M, int N, int K,
+                       int split_k, void* stream);
+
+/*
+ * y = W . x.  W is N x K fp16, x has K fp16 entries, y has N fp16 entries.
+ * fp32 accumulation, one rounding to fp16 (round-to-nearest-even).
+ * Defined by the TileLang GEMV page: GEMV as the degenerate (1,k) x (k,n)
+ * GEMM, kernels with A(K,), B(N,K), C(N,) accumulated in float (here x = A,
+ * W = B, y = C).
+ */
+int gemv_f16(const void* W, const void* x, void* y, int N, int K, void* stream);
+
+/* ---- extensions ------------------------------------------------------ */
+
+/* Bytes of workspace gemm_f16_nt_splitk_ex needs in GF_SPLITK_TWOPASS mode:
+ * split_k * M * N * sizeof(float) (0 for invalid arguments). */
+size_t gemm_f16_nt_splitk_workspace_bytes(int M, int N, int split_k);
+
+/*
+ * Split-K with a choice of combine.  mode = GF_SPLITK_ATOMIC behaves exactly
+ * like gemm_f16_nt_splitk (workspace ignored, may be NULL).
+ * mode = GF_SPLITK_TWOPASS: pass 1 stores slice s's partial tile into
+ * workspace[s][M][N] (fp32, caller-owned device memory of at least
+ * gemm_f16_nt_splitk_workspace_bytes(M, N, split_k) bytes, 16-byte aligned);
+ * pass 2 sums the slices in ascending s into C32.  The two-pass result is
+ * bitwise reproducible from run to run.
+ * Returns GF_ERR_INVALID_ARG for a bad mode or a NULL / short workspace in
+ * two-pass mode.
+ */
+int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N, int K,
+                          int split_k, int mode, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Tile configuration of the GEMM kernel (used by the offline sweep).
+ * block_m x block_n x block_k tile, `stages` LDS buffers (1..3), `threads`
+ * per workgroup (256 or 512), raster = 1 for the grouped, XCD-aware
+ * workgroup order, 0 for plain row-major tile order. */
+typedef struct gf_gemm_cfg {
+    int block_m, block_n, block_k, stages, threads, raster;
+} gf_gemm_cfg;
+
+/* GEMV launch shape: rows per wave, 16-byte W loads in flight per row and
+ * lane, waves per workgroup. */
+typedef struct gf_gemv_cfg {
+    int rows_per_wave, unroll, waves;
+} gf_gemv_cfg;
+
+/* gemm_f16_nt with an explicit tile config; GF_ERR_UNSUPPORTED when the
+ * library holds no kernel for it.  Same semantics as gemm_f16_nt. */
+int gemm_f16_nt_cfg(const void* A, const void* B, void* C, int M, int N, int K,
+                    const gf_gemm_cfg* cfg, void* stream);
+
+/* gemv_f16 with an explicit launch shape; GF_ERR_UNSUPPORTED when the
+ * library holds no kernel for it.  Same semantics as gemv_f16. */
+int gemv_f16_cfg(const void* W, const void* x, void* y, int N, int K,
+                 const gf_gemv_cfg* cfg, void* stream);
+
+/* Enumerate the compiled configs: count, then the i-th (0 <= i < count).
+ * The _get calls return GF_ERR_INVALID_ARG for an index out of range. */
+int gf_gemm_config_count(void);
+int gf_gemm_config_get(int i, gf_gemm_cfg* out);
+int gf_gemv_config_count(void);
+int gf_gemv_config_get(int i, gf_gemv_cfg* out);
+
+/* The config gemm_f16_nt / gemv_f16 would pick for a shape. */
+int gf_gemm_default_config(int M, int N, int K, gf_gemm_cfg* out);
+int gf_gemv_default_config(int N, int K, gf_gemv_cfg* out);
+
+/* Static string naming a status code. */
+const char* gf_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GEMVFP16_H */

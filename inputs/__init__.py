@@ -31,18 +31,67 @@ STREAM_A = 0
 STREAM_B = 1
 
 
-def _mix(z: np.ndarray) -> np.ndarray:
-    z = (z ^ (z >> np.uint64(30))) * _M1
-    z = (z ^ (z >> np.uint64(27))) * _M2
-    return z ^ (z >> np.uint64(31))
+_CHUNK = 1 << 20
+
+
+def _mix_inplace(z: np.ndarray, t: np.ndarray) -> None:
+    """SplitMix64 finaliser applied to z in place (t is scratch of z's size)."""
+    np.right_shift(z, np.uint64(30), out=t)
+    np.bitwise_xor(z, t, out=z)
+    np.multiply(z, _M1, out=z)
+    np.right_shift(z, np.uint64(27), out=t)
+    np.bitwise_xor(z, t, out=z)
+    np.multiply(z, _M2, out=z)
+    np.right_shift(z, np.uint64(31), out=t)
+    np.bitwise_xor(z, t, out=z)
+
+
+def _fill(seed: int, stream_id: int, count: int, start: int, emit) -> None:
+    """Draw outputs start .. start+count-1 chunk by chunk; emit(lo, hi, z)."""
+    key = np.uint64(((seed << 48) + (stream_id << 40)) & 0xFFFFFFFFFFFFFFFF)
+    z = np.empty(min(count, _CHUNK), dtype=np.uint64)
+    t = np.empty_like(z)
+    for lo in range(0, count, _CHUNK):
+        hi = min(count, lo + _CHUNK)
+        zz, tt = z[: hi - lo], t[: hi - lo]
+        zz[:] = np.arange(start + lo + 1, start + hi + 1, dtype=np.uint64)
+        np.multiply(zz, GAMMA, out=zz)          # (i + 1) * GAMMA mod 2^64
+        np.add(zz, key, out=zz)
+        _mix_inplace(zz, tt)
+        emit(lo, hi, zz)
 
 
 def splitmix64(seed: int, stream_id: int, count: int, start: int = 0) -> np.ndarray:
     """``count`` 64-bit outputs of stream (seed, stream_id) from index ``start``."""
-    key = np.uint64(((seed << 48) + (stream_id << 40)) & 0xFFFFFFFFFFFFFFFF)
-    idx = np.arange(start + 1, start + count + 1, dtype=np.uint64)
-    with np.errstate(over="ignore"):
-        return _mix(key + idx * GAMMA)
+    out = np.empty(count, dtype=np.uint64)
+
+    def emit(lo, hi, z):
+        out[lo:hi] = z
+
+    _fill(seed, stream_id, count, start, emit)
+    return out
+
+
+def _draw(seed: int, stream_id: int, count: int, integer: bool) -> np.ndarray:
+    out = np.empty(count, dtype=np.float16)
+    u = np.empty(min(count, _CHUNK), dtype=np.float64)
+
+    def emit(lo, hi, z):
+        uu = u[: hi - lo]
+        np.right_shift(z, np.uint64(11), out=z)
+        uu[:] = z                                # exact: 53-bit integers
+        np.multiply(uu, 2.0 ** -53, out=uu)      # u in [0, 1)
+        if integer:
+            np.multiply(uu, 5.0, out=uu)
+            np.floor(uu, out=uu)
+            np.subtract(uu, 2.0, out=uu)         # floor(5u) - 2
+        else:
+            np.multiply(uu, 2.0, out=uu)
+            np.subtract(uu, 1.0, out=uu)         # 2u - 1
+        out[lo:hi] = uu                          # round-to-nearest-even to fp16
+
+    _fill(seed, stream_id, count, 0, emit)
+    return out
 
 
 def uniform01(seed: int, stream_id: int, count: int, start: int = 0) -> np.ndarray:
@@ -53,15 +102,13 @@ def uniform01(seed: int, stream_id: int, count: int, start: int = 0) -> np.ndarr
 def uniform_f16(shape, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarray:
     """fp16 values, uniform on [-1, 1], as a float16 array of ``shape``."""
     n = int(np.prod(shape)) if len(shape) else 1
-    u = uniform01(seed, stream_id, n)
-    return (2.0 * u - 1.0).astype(np.float16).reshape(shape)
+    return _draw(seed, stream_id, n, integer=False).reshape(shape)
 
 
 def integer_f16(shape, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarray:
     """fp16 values drawn from {-2, -1, 0, 1, 2}, as a float16 array of ``shape``."""
     n = int(np.prod(shape)) if len(shape) else 1
-    u = uniform01(seed, stream_id, n)
-    return (np.floor(5.0 * u) - 2.0).astype(np.float16).reshape(shape)
+    return _draw(seed, stream_id, n, integer=True).reshape(shape)
 
 
 def make(kind: str, shape, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarray:

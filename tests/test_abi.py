@@ -1,0 +1,131 @@
+"""Boundary checks that need no GPU: the C-ABI library loads, exports every
+symbol include/gemvfp16.h declares, and its host-side argument validation
+returns the documented status codes.  No call here reaches a kernel launch:
+every call either fails validation or is a documented no-op (M or N == 0)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemv_fp16_amd as gf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemvfp16.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gf.LIB_PATH):
+        from gemv_fp16_amd import build
+        build.build()
+    return gf.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("gemm_f16_nt", "gemm_f16_nt_splitk", "gemv_f16"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(gf.EXPORTS)
+
+
+def test_status_strings(L):
+    for rc in (0, 1, 2, 3):
+        assert gf.status_string(rc).startswith(("GF_OK", "GF_ERR"))
+    assert gf.status_string(99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below stops on the host
+ODD = ctypes.c_void_p(0x10001)
+NULL = ctypes.c_void_p(0)
+
+
+def test_gemm_validation(L):
+    s = NULL
+    assert L.gemm_f16_nt(FAKE, FAKE, FAKE, -1, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt(FAKE, FAKE, FAKE, 4, -1, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt(FAKE, FAKE, FAKE, 4, 4, -1, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt(NULL, FAKE, FAKE, 4, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt(FAKE, NULL, FAKE, 4, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt(FAKE, FAKE, NULL, 4, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt(ODD, FAKE, FAKE, 4, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt(FAKE, FAKE, ODD, 4, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    # too large: M*K >= 2^31 elements
+    assert L.gemm_f16_nt(FAKE, FAKE, FAKE, 65536, 4, 65536, s) == gf.GF_ERR_INVALID_ARG
+    # empty outputs are no-ops, NULL allowed where the extent is empty
+    assert L.gemm_f16_nt(NULL, FAKE, NULL, 0, 4, 4, s) == gf.GF_OK
+    assert L.gemm_f16_nt(FAKE, NULL, NULL, 4, 0, 4, s) == gf.GF_OK
+    assert L.gemm_f16_nt(NULL, NULL, NULL, 0, 0, 0, s) == gf.GF_OK
+
+
+def test_gemm_cfg_validation(L):
+    good = gf.GemmCfg(128, 128, 64, 2, 256, 1)
+    bad = gf.GemmCfg(128, 128, 48, 2, 256, 1)
+    illegal = gf.GemmCfg(256, 256, 64, 3, 256, 1)     # 192 KiB of LDS
+    assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 4, 4, 4, None, NULL) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 0, 4, 4, ctypes.byref(good), NULL) == gf.GF_OK
+    assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 0, 4, 4, ctypes.byref(bad), NULL) == gf.GF_ERR_UNSUPPORTED
+    assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 4, 4, 4, ctypes.byref(illegal), NULL) == gf.GF_ERR_UNSUPPORTED
+
+
+def test_splitk_validation(L):
+    s = NULL
+    assert L.gemm_f16_nt_splitk(FAKE, FAKE, FAKE, 4, 4, 4, 0, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt_splitk(FAKE, FAKE, FAKE, 4, 4, 4, -3, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt_splitk(FAKE, FAKE, ctypes.c_void_p(0x10002), 4, 4, 4, 2, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nt_splitk(FAKE, FAKE, FAKE, 0, 4, 4, 2, s) == gf.GF_OK
+    ex = L.gemm_f16_nt_splitk_ex
+    assert ex(FAKE, FAKE, FAKE, 4, 4, 4, 2, 7, NULL, 0, s) == gf.GF_ERR_INVALID_ARG      # bad mode
+    assert ex(FAKE, FAKE, FAKE, 4, 4, 4, 2, gf.GF_SPLITK_TWOPASS, NULL, 0, s) == gf.GF_ERR_INVALID_ARG
+    need = L.gemm_f16_nt_splitk_workspace_bytes(4, 4, 2)
+    assert need == 2 * 4 * 4 * 4
+    assert ex(FAKE, FAKE, FAKE, 4, 4, 4, 2, gf.GF_SPLITK_TWOPASS, FAKE, need - 1, s) == gf.GF_ERR_INVALID_ARG
+    assert ex(FAKE, FAKE, FAKE, 4, 0, 4, 2, gf.GF_SPLITK_TWOPASS, NULL, 0, s) == gf.GF_OK
+    assert L.gemm_f16_nt_splitk_workspace_bytes(-1, 4, 2) == 0
+    assert L.gemm_f16_nt_splitk_workspace_bytes(4, 4, 0) == 0
+
+
+def test_gemv_validation(L):
+    s = NULL
+    assert L.gemv_f16(FAKE, FAKE, FAKE, -1, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemv_f16(FAKE, FAKE, FAKE, 4, -1, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemv_f16(NULL, FAKE, FAKE, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemv_f16(FAKE, NULL, FAKE, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemv_f16(FAKE, FAKE, NULL, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemv_f16(FAKE, FAKE, ODD, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemv_f16(NULL, NULL, NULL, 0, 4, s) == gf.GF_OK
+    c = gf.GemvCfg(3, 3, 3)
+    assert L.gemv_f16_cfg(FAKE, FAKE, FAKE, 0, 4, ctypes.byref(c), s) == gf.GF_ERR_UNSUPPORTED
+    assert L.gemv_f16_cfg(FAKE, FAKE, FAKE, 0, 4, None, s) == gf.GF_ERR_INVALID_ARG
+
+
+def test_config_tables(L):
+    cfgs = gf.gemm_configs()
+    assert len(cfgs) == 108                       # 3 x 3 x 2 x 3 x 2 sweep grid
+    legal = [c for c, ok in cfgs if ok]
+    assert len(legal) >= 90
+    for c, ok in cfgs:
+        lds = c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * 2
+        if lds > 160 * 1024:
+            assert not ok, c
+    assert len(gf.gemv_configs()) >= 30
+    d = gf.gemm_default_config(8192, 8192, 8192)
+    assert (d["block_m"], d["block_n"]) == (256, 256)
+    assert any(c == {**d, "raster": 1} for c, ok in cfgs if ok)
+    assert gf.gemv_default_config(8192, 8192) in gf.gemv_configs()
+    bad = gf.GemmCfg()
+    assert L.gf_gemm_config_get(-1, ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
+    assert L.gf_gemm_config_get(108, ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG

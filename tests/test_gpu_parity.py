@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (fp16 outputs): integer inputs in {-2..2} bit-exact; uniform[-1,1]
+inputs within 1 fp16 ulp(C_ref) + 1e-3.  Split-K fp32 outputs: integer
+inputs bit-exact, uniform within 1e-5 * sqrt(K) * max|C_ref|.  Two-pass
+split-K is bitwise reproducible.  Full-size shapes are checked on sampled
+entries that the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import gemv_fp16_amd as gf
+import inputs
+import oracle
+from tests.util import (check_f16_tolerance, check_f32_splitk_tolerance, dev, host_u16,
+                        sample_ij)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gf.lib()                         # fail loudly if the HIP library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+_cache = {}
+
+
+def operands(kind, M, N, K, seed=0):
+    key = (kind, M, N, K, seed)
+    if key not in _cache:
+        A = inputs.make(kind, (M, K), seed, inputs.STREAM_A)
+        B = inputs.make(kind, (N, K), seed, inputs.STREAM_B)
+        _cache.clear()
+        _cache[key] = (A, B)
+    return _cache[key]
+
+
+def run_gemm(A, B, cfg=None):
+    C = gf.gemm_f16_nt(dev(A), dev(B), cfg=cfg)
+    torch.cuda.synchronize()
+    return host_u16(C)
+
+
+def check_gemm_full(A, B, kind, what, cfg=None):
+    got = run_gemm(A, B, cfg)
+    ref = oracle.gemm_nt_f16(A, B)
+    if kind == "integer":
+        assert np.array_equal(got, ref), what + ": integer inputs not bit-exact"
+    else:
+        check_f16_tolerance(got, ref, what)
+
+
+# ---------------------------------------------------------------------------
+# fp16 GEMM-NT
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["uniform", "integer"])
+def test_gemm_256_cube(kind):
+    """256^3, seed 0: uniform within tolerance, integers bit-exact."""
+    A, B = operands(kind, 256, 256, 256)
+    _say("gemm 256^3 %s" % kind)
+    check_gemm_full(A, B, kind, "gemm 256^3 " + kind)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 1), (1, 1, 8), (17, 33, 65), (257, 129, 200), (64, 64, 64), (100, 300, 8),
+    (129, 65, 1000), (3, 700, 24), (700, 3, 24), (256, 256, 7), (512, 384, 136),
+])
+@pytest.mark.parametrize("kind", ["uniform", "integer"])
+def test_gemm_ragged_shapes(M, N, K, kind):
+    A, B = operands(kind, M, N, K, seed=M + N + K)
+    _say("gemm ragged %dx%dx%d %s" % (M, N, K, kind))
+    check_gemm_full(A, B, kind, "gemm %dx%dx%d %s" % (M, N, K, kind))
+
+
+def test_gemm_zero_k_writes_zeros():
+    C = torch.full((5, 7), 3.0, dtype=torch.float16, device="cuda")
+    gf.gemm_f16_nt(torch.empty((5, 0), dtype=torch.float16, device="cuda"),
+                   torch.empty((7, 0), dtype=torch.float16, device="cuda"), C)
+    torch.cuda.synchronize()
+    assert np.all(host_u16(C) == 0)
+
+
+def test_gemm_unaligned_pointers_take_masked_path():
+    """Operands offset by one element (2-byte aligned only) still match."""
+    A, B = operands("uniform", 96, 80, 128, seed=11)
+    big_a = torch.zeros(96 * 128 + 1, dtype=torch.float16, device="cuda")
+    big_b = torch.zeros(80 * 128 + 1, dtype=torch.float16, device="cuda")
+    big_a[1:] = dev(A).reshape(-1)
+    big_b[1:] = dev(B).reshape(-1)
+    a_view = big_a[1:].view(96, 128)
+    b_view = big_b[1:].view(80, 128)
+    assert a_view.data_ptr() % 16 != 0
+    C = gf.gemm_f16_nt(a_view, b_view)
+    torch.cuda.synchronize()
+    check_f16_tolerance(host_u16(C), oracle.gemm_nt_f16(A, B), "unaligned")
+
+
+def test_gemm_every_compiled_config():
+    """Every legal tile config, on a shape with ragged tails for all tiles."""
+    M, N, K = 320, 192, 160
+    Au, Bu = operands("uniform", M, N, K, seed=3)
+    ref_u = oracle.gemm_nt_f16(Au, Bu)
+    Ai = inputs.integer_f16((M, K), 3, 0)
+    Bi = inputs.integer_f16((N, K), 3, 1)
+    ref_i = oracle.gemm_nt_f16(Ai, Bi)
+    dAu, dBu, dAi, dBi = dev(Au), dev(Bu), dev(Ai), dev(Bi)
+    n = 0
+    for cfg, ok in gf.gemm_configs():
+        if not ok:
+            continue
+        for raster in (0, 1):
+            c = dict(cfg, raster=raster)
+            _say("cfg %s" % c)
+            Cu = gf.gemm_f16_nt(dAu, dBu, cfg=c)
+            Ci = gf.gemm_f16_nt(dAi, dBi, cfg=c)
+            torch.cuda.synchronize()
+            check_f16_tolerance(host_u16(Cu), ref_u, "cfg %s" % c)
+            assert np.array_equal(host_u16(Ci), ref_i), "cfg %s integer" % c
+            n += 1
+    assert n >= 180
+
+
+def test_gemm_power_of_two_scaling_bit_exact():
+    """Doubling A doubles every fp32 partial sum exactly, so C doubles."""
+    A, B = operands("uniform", 384, 256, 512, seed=5)
+    C1 = run_gemm(A, B).view(np.float16).astype(np.float64)
+    C2 = run_gemm((A.astype(np.float32) * 2).astype(np.float16), B).view(np.float16).astype(np.float64)
+    normal = np.abs(C1) >= 2.0 ** -13
+    assert np.array_equal(C2[normal], 2 * C1[normal])
+
+
+@pytest.mark.parametrize("K", [1024, 4096, 8192, 16384])
+def test_gemm_8192_sampled(K):
+    """M = N = 8192, K swept, default (bench) launch: sampled entries."""
+    M = N = 8192
+    A, B = operands("uniform", M, N, K)
+    _say("gemm 8192x8192x%d uniform" % K)
+    got = run_gemm(A, B)
+    ij = sample_ij(M, N, 4000, seed=K)
+    ref16, _ = oracle.gemm_nt_entries(A, B, ij)
+    check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "8192x8192x%d" % K)
+
+
+def test_gemm_8192_integer_sampled():
+    M = N = K = 8192
+    A, B = operands("integer", M, N, K)
+    _say("gemm 8192^3 integer")
+    got = run_gemm(A, B)
+    ij = sample_ij(M, N, 4000, seed=1)
+    ref16, _ = oracle.gemm_nt_entries(A, B, ij)
+    assert np.array_equal(got[ij[:, 0], ij[:, 1]], ref16)
+
+
+# ---------------------------------------------------------------------------
+# split-K, fp32 out
+# ---------------------------------------------------------------------------
+
+def run_splitk(A, B, split_k, mode):
+    dA, dB = dev(A), dev(B)
+    if mode == "atomic":
+        C = gf.gemm_f16_nt_splitk(dA, dB, split_k=split_k)
+    else:
+        C = gf.gemm_f16_nt_splitk_ex(dA, dB, split_k=split_k, mode=gf.GF_SPLITK_TWOPASS)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+@pytest.mark.parametrize("mode", ["atomic", "twopass"])
+@pytest.mark.parametrize("split_k", [4, 8, 16])
+def test_splitk_1024_16384(split_k, mode):
+    """The split-K workload: M = N = 1024, K = 16384, sampled entries."""
+    M = N = 1024
+    K = 16384
+    A, B = operands("uniform", M, N, K)
+    _say("splitk 1024x1024x16384 s=%d %s" % (split_k, mode))
+    got = run_splitk(A, B, split_k, mode)
+    ij = sample_ij(M, N, 4000, seed=split_k)
+    _, ref32 = oracle.gemm_nt_entries(A, B, ij)
+    check_f32_splitk_tolerance(got[ij[:, 0], ij[:, 1]], ref32, K, "splitk s=%d %s" % (split_k, mode))
+    Ai, Bi = operands("integer", M, N, K)
+    got_i = run_splitk(Ai, Bi, split_k, mode)
+    _, ref_i = oracle.gemm_nt_entries(Ai, Bi, ij)
+    assert np.array_equal(got_i[ij[:, 0], ij[:, 1]], ref_i)
+
+
+@pytest.mark.parametrize("mode", ["atomic", "twopass"])
+@pytest.mark.parametrize("M,N,K,split_k", [
+    (256, 256, 4096, 4), (100, 70, 1000, 3), (100, 70, 1000, 7), (65, 33, 64, 16),
+    (17, 9, 1001, 5), (128, 128, 8, 1), (1, 1, 1, 1), (40, 24, 0, 4),
+])
+def test_splitk_full_small(M, N, K, split_k, mode):
+    A, B = operands("uniform", M, N, K, seed=M * N + K)
+    got = run_splitk(A, B, split_k, mode)
+    ref = oracle.gemm_nt_f32(A, B)
+    check_f32_splitk_tolerance(got, ref, K, "splitk %dx%dx%d s=%d %s" % (M, N, K, split_k, mode))
+    Ai = inputs.integer_f16((M, K), 1, 0)
+    Bi = inputs.integer_f16((N, K), 1, 1)
+    assert np.array_equal(run_splitk(Ai, Bi, split_k, mode), oracle.gemm_nt_f32(Ai, Bi))
+
+
+def test_splitk_twopass_bitwise_deterministic():
+    A, B = operands("uniform", 512, 512, 8192, seed=2)
+    r1 = run_splitk(A, B, 16, "twopass")
+    r2 = run_splitk(A, B, 16, "twopass")
+    assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------
+
+def run_gemv(W, x, cfg=None):
+    y = gf.gemv_f16(dev(W), dev(x), cfg=cfg)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("NK", [1024, 8192])
+@pytest.mark.parametrize("kind", ["uniform", "integer"])
+def test_gemv_workloads(NK, kind):
+    W = inputs.make(kind, (NK, NK), 0, inputs.STREAM_A)
+    x = inputs.make(kind, (NK,), 0, inputs.STREAM_B)
+    _say("gemv %d %s" % (NK, kind))
+    got = run_gemv(W, x)
+    ref = oracle.gemv_f16(W, x)
+    if kind == "integer":
+        assert np.array_equal(got, ref)
+    else:
+        check_f16_tolerance(got, ref, "gemv %d" % NK)
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (1, 8), (7, 13), (1000, 1000), (1000, 1001),
+                                 (33, 4104), (4097, 520), (5, 0)])
+def test_gemv_ragged(N, K):
+    W = inputs.uniform_f16((N, K), N + K, 0)
+    x = inputs.uniform_f16((K,), N + K, 1)
+    check_f16_tolerance(run_gemv(W, x), oracle.gemv_f16(W, x), "gemv %dx%d" % (N, K))
+
+
+def test_gemv_every_config():
+    N, K = 1000, 3000          # ragged rows and a ragged chunk tail
+    W = inputs.uniform_f16((N, K), 4, 0)
+    x = inputs.uniform_f16((K,), 4, 1)
+    ref = oracle.gemv_f16(W, x)
+    Wi = inputs.integer_f16((N, K), 4, 0)
+    xi = inputs.integer_f16((K,), 4, 1)
+    ref_i = oracle.gemv_f16(Wi, xi)
+    dW, dx, dWi, dxi = dev(W), dev(x), dev(Wi), dev(xi)
+    for cfg in gf.gemv_configs():
+        y = gf.gemv_f16(dW, dx, cfg=cfg)
+        yi = gf.gemv_f16(dWi, dxi, cfg=cfg)
+        torch.cuda.synchronize()
+        check_f16_tolerance(host_u16(y), ref, "gemv cfg %s" % cfg)
+        assert np.array_equal(host_u16(yi), ref_i), "gemv cfg %s integer" % cfg
+
+
+def test_gemv_matches_gemm_one_row_on_integers():
+    W = inputs.integer_f16((300, 512), 8, 0)
+    x = inputs.integer_f16((512,), 8, 1)
+    assert np.array_equal(run_gemv(W, x), run_gemm(x[None, :], W)[0])
