@@ -10,7 +10,8 @@ out) on torch's current stream with A and B already resident in HBM.  The
 headline value is whole-job TFLOP/s over the timed steps (wall clock,
 bracketed by device synchronisation).  The GEMV (N = K = 8192 and 1024) and
 split-K (M = N = 1024, K = 16384) figures are reported in "extra", each
-timed with HIP events on the launching stream; GEMV rotates over enough W
+timed with HIP events on the launching stream around batches of
+back-to-back launches; GEMV rotates over enough W
 copies (> 512 MiB) that every call streams W from HBM, not from the 256 MiB
 MALL.  Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -61,27 +62,24 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def time_calls(torch, fn, reps, warmup, prep=None):
-    """Average and median seconds of fn() over reps, HIP events on the current stream."""
-    for i in range(warmup):
-        if prep:
-            prep(i)
+def time_batch(torch, fn, reps, warmup, trials=3):
+    """Seconds per call: HIP events on the current stream around `reps`
+    back-to-back calls (median of `trials` batches), after `warmup` calls."""
+    for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    times = []
     stream = torch.cuda.current_stream()
-    for i in range(reps):
-        if prep:
-            prep(i)
+    res = []
+    for _ in range(trials):
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record(stream)
-        fn()
+        for _ in range(reps):
+            fn()
         e.record(stream)
-        times.append((s, e))
-    torch.cuda.synchronize()
-    ms = np.array([s.elapsed_time(e) for s, e in times])
-    return float(ms.mean()) * 1e-3, float(np.median(ms)) * 1e-3
+        torch.cuda.synchronize()
+        res.append(s.elapsed_time(e) * 1e-3 / reps)
+    return float(np.median(res))
 
 
 def main():
@@ -120,8 +118,7 @@ def main():
     cfg = gf.gemm_default_config(M, N, K)
     flops = 2.0 * M * N * K
 
-    def step():
-        gf.gemm_f16_nt(A, B, C)
+    step = gf.prepare_gemm_f16_nt(A, B, C)
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -173,8 +170,8 @@ def main():
         for k2 in (1024, 4096, 16384):
             a2 = torch.from_numpy(inputs.uniform_f16((M, k2), 0, 0)).cuda()
             b2 = torch.from_numpy(inputs.uniform_f16((N, k2), 0, 1)).cuda()
-            avg, med = time_calls(torch, lambda: gf.gemm_f16_nt(a2, b2, C), 10, 3)
-            sweep[str(k2)] = round(2.0 * M * N * k2 / avg / 1e12, 1)
+            t2 = time_batch(torch, gf.prepare_gemm_f16_nt(a2, b2, C), 10, 3)
+            sweep[str(k2)] = round(2.0 * M * N * k2 / t2 / 1e12, 1)
             log("gemm 8192x8192x%d: %.1f TFLOP/s" % (k2, sweep[str(k2)]))
             del a2, b2
         sweep[str(K)] = round(achieved, 1)
@@ -189,24 +186,26 @@ def main():
             Ws = [torch.from_numpy(inputs.uniform_f16((nk, nk), i, 0)).cuda() for i in range(copies)]
             x = torch.from_numpy(inputs.uniform_f16((nk,), 0, 1)).cuda()
             y = torch.empty((nk,), dtype=torch.float16, device="cuda")
-            state = {"i": 0}
+            calls = [gf.prepare_gemv_f16(w, x, y) for w in Ws]
+            state = [0]
 
-            def prep(i, Ws=Ws, state=state):
-                state["i"] = i % len(Ws)
+            def cold(calls=calls, state=state):
+                calls[state[0] % len(calls)]()
+                state[0] += 1
 
-            avg, med = time_calls(torch, lambda: gf.gemv_f16(Ws[state["i"]], x, y), 200, 20, prep)
+            t_cold = time_batch(torch, cold, 200, 20)
+            t_warm = time_batch(torch, calls[0], 200, 20)
             bytes_ = 2.0 * nk * nk + 2.0 * nk + 2.0 * nk
-            gbs = bytes_ / med / 1e9
-            warm_avg, warm_med = time_calls(torch, lambda: gf.gemv_f16(Ws[0], x, y), 200, 20)
+            gbs = bytes_ / t_cold / 1e9
             gemv[str(nk)] = {
-                "us": round(med * 1e6, 3), "GB/s": round(gbs, 1),
+                "us": round(t_cold * 1e6, 3), "GB/s": round(gbs, 1),
                 "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                 "w_copies_rotated": copies,
-                "cache_warm_GB/s_not_hbm": round(bytes_ / warm_med / 1e9, 1),
+                "cache_warm_GB/s_not_hbm": round(bytes_ / t_warm / 1e9, 1),
                 "launch": gf.gemv_default_config(nk, nk),
             }
             log("gemv %d: %.2f us, %.1f GB/s (warm %.1f)" %
-                (nk, med * 1e6, gbs, gemv[str(nk)]["cache_warm_GB/s_not_hbm"]))
+                (nk, t_cold * 1e6, gbs, gemv[str(nk)]["cache_warm_GB/s_not_hbm"]))
             del Ws
         g8 = gemv["8192"]
         gemv["roofline"] = {"bound": "hbm", "achieved": g8["GB/s"], "peak": PEAK_HBM_GBS,
@@ -224,12 +223,12 @@ def main():
         f3 = 2.0 * sm * sm * sk_k
         for split in (4, 8, 16):
             for mode, name in ((gf.GF_SPLITK_ATOMIC, "atomic"), (gf.GF_SPLITK_TWOPASS, "twopass")):
-                avg, med = time_calls(torch, lambda: gf.gemm_f16_nt_splitk_ex(
+                t3 = time_batch(torch, lambda: gf.gemm_f16_nt_splitk_ex(
                     a3, b3, c3, split, mode, ws), 50, 5)
-                sk["%s_s%d" % (name, split)] = round(f3 / med / 1e12, 1)
+                sk["%s_s%d" % (name, split)] = round(f3 / t3 / 1e12, 1)
         c16 = torch.empty((sm, sm), dtype=torch.float16, device="cuda")
-        avg, med = time_calls(torch, lambda: gf.gemm_f16_nt(a3, b3, c16), 50, 5)
-        sk["no_split_fp16"] = round(f3 / med / 1e12, 1)
+        t3 = time_batch(torch, lambda: gf.gemm_f16_nt(a3, b3, c16), 50, 5)
+        sk["no_split_fp16"] = round(f3 / t3 / 1e12, 1)
         log("splitk 1024x1024x16384 TFLOP/s: %s" % sk)
         extra["splitk_1024x1024x16384_tflops"] = sk
         del a3, b3, c3, ws

@@ -221,3 +221,67 @@ def gemv_f16(W, x, y=None, stream=None, cfg: dict | None = None):
         c = GemvCfg(**cfg)
         _check(lib().gemv_f16_cfg(*args, ctypes.byref(c), _stream(stream)), "gemv_f16_cfg")
     return y
+
+
+# ---------------------------------------------------------------------------
+# pre-marshalled calls: the checks and pointer extraction happen once, so a
+# timing loop pays only the ctypes call per launch
+# ---------------------------------------------------------------------------
+
+def prepare_gemm_f16_nt(A, B, C, stream=None, cfg: dict | None = None):
+    """Zero-argument callable that launches C = A . B^T on `stream`."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be (M, N)")
+    args = (_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"), _dev(C, torch.float16, "C"),
+            M, N, K)
+    s = _stream(stream)
+    L = lib()
+    if cfg is None:
+        fn = L.gemm_f16_nt
+
+        def call():
+            rc = fn(*args, s)
+            if rc:
+                _check(rc, "gemm_f16_nt")
+    else:
+        c = GemmCfg(**cfg)
+        ref = ctypes.byref(c)
+        fn = L.gemm_f16_nt_cfg
+
+        def call():
+            rc = fn(*args, ref, s)
+            if rc:
+                _check(rc, "gemm_f16_nt_cfg")
+    call.keep = (A, B, C, args)
+    return call
+
+
+def prepare_gemv_f16(W, x, y, stream=None, cfg: dict | None = None):
+    """Zero-argument callable that launches y = W . x on `stream`."""
+    import torch
+    if W.dim() != 2 or x.dim() != 1 or W.shape[1] != x.shape[0] or tuple(y.shape) != (W.shape[0],):
+        raise ValueError("W must be (N, K), x (K,), y (N,)")
+    N, K = W.shape
+    args = (_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y"), N, K)
+    s = _stream(stream)
+    L = lib()
+    if cfg is None:
+        fn = L.gemv_f16
+
+        def call():
+            rc = fn(*args, s)
+            if rc:
+                _check(rc, "gemv_f16")
+    else:
+        c = GemvCfg(**cfg)
+        ref = ctypes.byref(c)
+        fn = L.gemv_f16_cfg
+
+        def call():
+            rc = fn(*args, ref, s)
+            if rc:
+                _check(rc, "gemv_f16_cfg")
+    call.keep = (W, x, y, args)
+    return call

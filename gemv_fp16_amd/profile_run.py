@@ -1,0 +1,70 @@
+"""Launch one operation a fixed number of times, for an external profiler.
+
+    rocprofv3 --kernel-trace --stats -- python3 -m gemv_fp16_amd.profile_run gemm
+    rocprofv3 --pmc FETCH_SIZE -- python3 -m gemv_fp16_amd.profile_run gemv
+
+Ops (inputs are the seeded uniform[-1,1] fp16 workloads):
+  gemm    C = A . B^T at M = N = K = 8192 (default tile config)
+  gemv    y = W . x at N = K = 8192, rotating 5 W copies (640 MiB)
+  splitk  C32 at M = N = 1024, K = 16384, split 8, atomic and two-pass
+  copy    torch copy of a 512 MiB buffer: a plain copy kernel of known size,
+          the calibration for the HBM byte counters
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("op", choices=["gemm", "gemv", "splitk", "copy"])
+    ap.add_argument("--iters", type=int, default=10)
+    ap.add_argument("--m", type=int, default=8192)
+    ap.add_argument("--n", type=int, default=8192)
+    ap.add_argument("--k", type=int, default=8192)
+    a = ap.parse_args(argv)
+
+    import torch
+    import gemv_fp16_amd as gf
+    import inputs
+
+    torch.cuda.set_device(0)
+    if a.op == "gemm":
+        A = torch.from_numpy(inputs.uniform_f16((a.m, a.k), 0, 0)).cuda()
+        B = torch.from_numpy(inputs.uniform_f16((a.n, a.k), 0, 1)).cuda()
+        C = torch.empty((a.m, a.n), dtype=torch.float16, device="cuda")
+        call = gf.prepare_gemm_f16_nt(A, B, C)
+        for _ in range(a.iters):
+            call()
+    elif a.op == "gemv":
+        Ws = [torch.from_numpy(inputs.uniform_f16((a.n, a.k), i, 0)).cuda() for i in range(5)]
+        x = torch.from_numpy(inputs.uniform_f16((a.k,), 0, 1)).cuda()
+        y = torch.empty((a.n,), dtype=torch.float16, device="cuda")
+        calls = [gf.prepare_gemv_f16(w, x, y) for w in Ws]
+        for i in range(a.iters):
+            calls[i % len(calls)]()
+    elif a.op == "splitk":
+        A = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, 0)).cuda()
+        B = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, 1)).cuda()
+        C = torch.empty((1024, 1024), dtype=torch.float32, device="cuda")
+        ws = torch.empty(8 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        for _ in range(a.iters):
+            gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_ATOMIC, ws)
+            gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_TWOPASS, ws)
+    else:
+        src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")   # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(a.iters):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile_run %s: %d iterations done" % (a.op, a.iters), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+"""Offline tile-config sweep for gemm_f16_nt and gemv_f16 (one GPU).
+
+    python -m gemv_fp16_amd.sweep gemm --m 8192 --n 8192 --k 8192 --out sweep.json
+    python -m gemv_fp16_amd.sweep gemv --n 8192 --k 8192 --out sweep_gemv.json
+
+A plain host loop in the spirit of the autotune grid on the TileLang FP16
+matmul benchmark page (section 2.1: block_M, block_N, block_K, pipeline
+stages, threads per block, rasterisation on/off; every candidate is built,
+warmed up and timed, the lowest latency wins).  Here the candidates are the
+tile configs compiled into the library (the grid minus the ones whose LDS or
+wave layout does not fit a CU, reported as "unsupported").
+
+Gate: before timing, each candidate's output on integer inputs in {-2..2}
+must equal, bit for bit, the output of the library's default config (those
+results are exact, so every correct kernel agrees), and on uniform inputs it
+must stay within 1 fp16 ulp + 1e-3 of it.  Timing: HIP events around
+`--reps` back-to-back launches after `--warmup` launches; the median of
+`--trials` such batches is recorded.  Results are appended as JSON lines to
+`--out` as they are measured; a rerun skips (shape, config) records already
+present, so an interrupted sweep resumes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def _u16(t):
+    import torch
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _ulp(bits):
+    v = np.abs(bits.view(np.float16).astype(np.float64))
+    e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    return np.where(v > 0, 2.0 ** (np.maximum(e, -14) - 10), 2.0 ** -24)
+
+
+def _close(got, ref):
+    g = got.view(np.float16).astype(np.float64)
+    r = ref.view(np.float16).astype(np.float64)
+    return bool(np.all(np.abs(g - r) <= _ulp(ref) + 1e-3))
+
+
+def _time_batch(torch, fn, reps, warmup, trials):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    res = []
+    for _ in range(trials):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        res.append(s.elapsed_time(e) * 1e-3 / reps)
+    return float(np.median(res)), float(np.min(res))
+
+
+def _done(path):
+    seen = set()
+    if path and os.path.exists(path):
+        for line in open(path):
+            try:
+                r = json.loads(line)
+                seen.add(json.dumps([r["op"], r["shape"], r["config"]], sort_keys=True))
+            except (ValueError, KeyError):
+                pass
+    return seen
+
+
+def _emit(path, rec):
+    line = json.dumps(rec, sort_keys=True)
+    print(line, flush=True)
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
+def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
+    import torch
+    import gemv_fp16_amd as gf
+    import inputs
+    A = torch.from_numpy(inputs.uniform_f16((M, K), 0, 0)).cuda()
+    B = torch.from_numpy(inputs.uniform_f16((N, K), 0, 1)).cuda()
+    Ai = torch.from_numpy(inputs.integer_f16((M, K), 0, 0)).cuda()
+    Bi = torch.from_numpy(inputs.integer_f16((N, K), 0, 1)).cuda()
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ref_u = _u16(gf.gemm_f16_nt(A, B))
+    ref_i = _u16(gf.gemm_f16_nt(Ai, Bi))
+    default = gf.gemm_default_config(M, N, K)
+    seen = _done(out)
+    flops = 2.0 * M * N * K
+    shape = [M, N, K]
+    for cfg, ok in gf.gemm_configs():
+        for raster in rasters:
+            c = dict(cfg, raster=raster)
+            key = json.dumps(["gemm", shape, c], sort_keys=True)
+            if key in seen:
+                continue
+            rec = {"op": "gemm", "shape": shape, "config": c}
+            if not ok:
+                rec["status"] = "unsupported"
+                _emit(out, rec)
+                continue
+            try:
+                ci = _u16(gf.gemm_f16_nt(Ai, Bi, cfg=c))
+                cu = _u16(gf.gemm_f16_nt(A, B, cfg=c))
+            except RuntimeError as e:
+                rec["status"] = "error: %s" % e
+                _emit(out, rec)
+                continue
+            if not np.array_equal(ci, ref_i) or not _close(cu, ref_u):
+                rec["status"] = "mismatch"
+                _emit(out, rec)
+                continue
+            med, mn = _time_batch(torch, gf.prepare_gemm_f16_nt(A, B, C, cfg=c), reps, warmup, trials)
+            rec.update(status="ok", median_ms=round(med * 1e3, 5), min_ms=round(mn * 1e3, 5),
+                       tflops=round(flops / med / 1e12, 2), is_default=(c == default))
+            _emit(out, rec)
+
+
+def sweep_gemv(N, K, reps, warmup, trials, out):
+    import torch
+    import gemv_fp16_amd as gf
+    import inputs
+    wbytes = N * K * 2
+    copies = max(1, min(64, -(-(640 << 20) // max(wbytes, 1))))
+    Ws = [torch.from_numpy(inputs.uniform_f16((N, K), i, 0)).cuda() for i in range(copies)]
+    x = torch.from_numpy(inputs.uniform_f16((K,), 0, 1)).cuda()
+    Wi = torch.from_numpy(inputs.integer_f16((N, K), 0, 0)).cuda()
+    xi = torch.from_numpy(inputs.integer_f16((K,), 0, 1)).cuda()
+    y = torch.empty((N,), dtype=torch.float16, device="cuda")
+    ref_u = _u16(gf.gemv_f16(Ws[0], x))
+    ref_i = _u16(gf.gemv_f16(Wi, xi))
+    default = gf.gemv_default_config(N, K)
+    seen = _done(out)
+    shape = [N, K]
+    nbytes = 2.0 * N * K + 2.0 * K + 2.0 * N
+    for c in gf.gemv_configs():
+        key = json.dumps(["gemv", shape, c], sort_keys=True)
+        if key in seen:
+            continue
+        rec = {"op": "gemv", "shape": shape, "config": c}
+        yi = _u16(gf.gemv_f16(Wi, xi, cfg=c))
+        yu = _u16(gf.gemv_f16(Ws[0], x, cfg=c))
+        if not np.array_equal(yi, ref_i) or not _close(yu, ref_u):
+            rec["status"] = "mismatch"
+            _emit(out, rec)
+            continue
+        calls = [gf.prepare_gemv_f16(w, x, y, cfg=c) for w in Ws]
+        state = [0]
+
+        def call():
+            calls[state[0] % copies]()
+            state[0] += 1
+
+        med, mn = _time_batch(torch, call, reps, warmup, trials)
+        rec.update(status="ok", median_us=round(med * 1e6, 3), min_us=round(mn * 1e6, 3),
+                   gbs=round(nbytes / med / 1e9, 1), w_copies=copies, is_default=(c == default))
+        _emit(out, rec)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("op", choices=["gemm", "gemv"])
+    ap.add_argument("--m", type=int, default=8192)
+    ap.add_argument("--n", type=int, default=8192)
+    ap.add_argument("--k", type=int, default=8192)
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--raster", type=int, nargs="*", default=[0, 1])
+    ap.add_argument("--out", default="")
+    a = ap.parse_args(argv)
+    t = time.time()
+    if a.op == "gemm":
+        sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster))
+    else:
+        sweep_gemv(a.n, a.k, a.reps, a.warmup, a.trials, a.out)
+    print("sweep done in %.1f s" % (time.time() - t), file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()
