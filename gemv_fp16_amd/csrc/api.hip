@@ -50,14 +50,17 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster)
 }
 
 // The tile config for a shape: the largest tile that still gives every CU
-// at least one workgroup.
+// at least one workgroup.  For the large case the offline sweep at
+// M = N = K = 8192 ranks 256 x 256 x 64 / 2 stages first, with 256 and 512
+// threads within run-to-run noise of each other and plain tile order ahead
+// of the grouped order.
 gf_gemm_cfg default_gemm_cfg(int M, int N, int /*K*/)
 {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 256, 1);
-    if (t128 >= 128) return make_cfg(128, 128, 64, 2, 256, 1);
-    return make_cfg(64, 64, 64, 2, 256, 1);
+    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 512, 0);
+    if (t128 >= 128) return make_cfg(128, 128, 64, 2, 256, 0);
+    return make_cfg(64, 64, 64, 2, 256, 0);
 }
 
 gf_gemm_cfg default_splitk_cfg(int M, int N, int K)

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gf {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -38,6 +40,24 @@ __device__ __forceinline__ void lds_barrier()
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so
+// every index in the body is a constant (no runtime indexing of register
+// arrays, no dependence on the unroller's size limits).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_impl<I + 1, N>(f);
+    }
+}
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl<0, N>(f);
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -13,9 +13,12 @@
 //    wave instruction writes 64 consecutive 16-byte LDS slots; the LDS layout
 //    swizzle is applied by choosing which global chunk each lane fetches.
 //  * LDS layout: per stage, A tile [BM][BK] then B tile [BN][BK], fp16,
-//    rows of BK/8 chunks; chunk c of row r sits at slot c ^ swz(r).  swz
-//    spreads the 8 rows read together by one MFMA operand fetch over eight
-//    different 16-byte bank groups.
+//    rows of BK/8 chunks; chunk c of row r sits at slot c ^ swz(r).  The LDS
+//    serves a 128-bit read 16 lanes (256 bytes, all 64 banks) at a time, and
+//    the 16 lanes of an MFMA operand fetch read the same chunk of 16
+//    consecutive rows; swz(r) = (r / (16 / CH)) % CH puts those 16 chunks in
+//    16 different 16-byte bank slots (rows that share a 256-byte window get
+//    the same key, rows in different windows get different keys).
 //  * Pipeline: STAGES LDS buffers in a ring; STAGES-1 tiles are in flight
 //    while one is consumed; one workgroup barrier per K tile.
 //  * Contraction: waves form a WM x WN grid over the tile; each wave owns a
@@ -56,7 +59,7 @@ struct GemmCfg {
     static constexpr int KS = (MT == 32) ? 16 : 32;                          // MFMA K
     static constexpr int FM = WTM / MT, FN = WTN / MT;
     static constexpr int CH = BK / 8;                        // 16-byte chunks per row
-    static constexpr int ROWS_PER_SWZ = 8 / CH;              // rows sharing one swizzle key
+    static constexpr int ROWS_PER_SWZ = 16 / CH;             // rows sharing one swizzle key
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LPS = (BM + BN) * CH / NT;          // 16-byte loads per thread per stage
@@ -83,28 +86,68 @@ __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
 // Operand staging
 // ---------------------------------------------------------------------------
 
-// Issue the direct-to-LDS loads of one K tile into one stage buffer.
-// MASK_K: chunks with k >= K read the zero chunk instead (last, ragged tile).
-template <class Cfg, bool MASK_K>
-__device__ __forceinline__ void issue_tile_dma(const GemmArgs& a, GF_LDS char* stage, int m0,
-                                               int n0, int k0, int tid, int wave)
-{
+// Direct-to-LDS loader of one thread.  Load r (0 <= r < LPS) of a K tile
+// fills LDS slot r * NT + tid; a wave instruction fills 64 consecutive slots,
+// so the LDS address is wave-uniform and the swizzle is applied on the global
+// side.  Because NT / CH rows and the A/B boundary are multiples of the
+// 16-row swizzle period, the K chunk c a thread fetches is the same for all
+// r; only the row changes.  The row offsets are computed once per tile
+// position.
+template <class Cfg>
+struct DmaLoader {
+    uint32_t voff[Cfg::LPS];   // byte offset of load r's chunk at k = 0 (row clamped)
+    int c8;                    // this thread's K offset inside a tile: c * 8
+
+    __device__ __forceinline__ void init(const GemmArgs& a, int m0, int n0, int tid)
+    {
+        const int row0 = tid / Cfg::CH;
+        c8 = ((tid % Cfg::CH) ^ swz_key(row0, Cfg::ROWS_PER_SWZ, Cfg::CH)) * 8;
 #pragma unroll
-    for (int r = 0; r < Cfg::LPS; ++r) {
-        const int slot = r * Cfg::NT + tid;            // LDS slot this lane fills
-        const int wslot = r * Cfg::NT + wave * kWave;  // first slot of this wave instruction
-        const bool is_a = wslot < Cfg::BM * Cfg::CH;   // wave-uniform
-        const int s = is_a ? slot : slot - Cfg::BM * Cfg::CH;
-        const int row = s / Cfg::CH;
-        const int c = (s % Cfg::CH) ^ swz_key(row, Cfg::ROWS_PER_SWZ, Cfg::CH);
-        const int grow = is_a ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
-        const uint16_t* base = is_a ? a.A : a.B;
-        const int kk = k0 + c * 8;
-        const void* src = base + (size_t)grow * a.K + kk;
-        if (MASK_K && kk >= a.K) src = (const void*)g_zero16;
-        __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)(stage + wslot * 16), 16, 0, 0);
+        for (int r = 0; r < Cfg::LPS; ++r) {
+            const int slot = r * Cfg::NT + tid;
+            const bool is_a = slot < Cfg::BM * Cfg::CH;
+            const int s = is_a ? slot : slot - Cfg::BM * Cfg::CH;
+            const int row = s / Cfg::CH;
+            const int grow = is_a ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
+            voff[r] = (uint32_t)(grow * a.K + c8) * 2u;
+        }
     }
-}
+
+    // Load r of the K tile whose first byte column is k0b = 2 * k0; every
+    // chunk must lie inside K.  Uniform base + 32-bit offset (saddr form).
+    __device__ __forceinline__ void issue(const GemmArgs& a, GF_LDS char* stage, uint32_t k0b, int r,
+                                          int wave) const
+    {
+        const int wslot = r * Cfg::NT + wave * kWave;    // wave-uniform
+        const bool is_a = wslot < Cfg::BM * Cfg::CH;     // wave-uniform
+        const char* base = (const char*)(is_a ? a.A : a.B);
+        __builtin_amdgcn_global_load_lds(base + (voff[r] + k0b), (GF_LDS void*)(stage + wslot * 16),
+                                         16, 0, 0);
+    }
+
+    __device__ __forceinline__ void issue_all(const GemmArgs& a, GF_LDS char* stage, int k0,
+                                              int wave) const
+    {
+#pragma unroll
+        for (int r = 0; r < Cfg::LPS; ++r) issue(a, stage, (uint32_t)k0 * 2u, r, wave);
+    }
+
+    // The same tile where it runs past K: chunks at k >= K read 16 zero bytes.
+    __device__ __forceinline__ void issue_all_masked(const GemmArgs& a, GF_LDS char* stage, int k0,
+                                                     int wave) const
+    {
+        const bool valid = k0 + c8 < a.K;
+#pragma unroll
+        for (int r = 0; r < Cfg::LPS; ++r) {
+            const int wslot = r * Cfg::NT + wave * kWave;
+            const bool is_a = wslot < Cfg::BM * Cfg::CH;
+            const char* base = (const char*)(is_a ? a.A : a.B);
+            const void* src = valid ? (const void*)(base + voff[r] + (size_t)k0 * 2)
+                                    : (const void*)g_zero16;
+            __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)(stage + wslot * 16), 16, 0, 0);
+        }
+    }
+};
 
 // Masked staging through registers for operands that are not 16-byte
 // aligned or whose K is not a multiple of 8: element loads with bounds
@@ -173,31 +216,103 @@ struct Mfma<16> {
 };
 
 template <class Cfg>
+__device__ __forceinline__ void load_frags(const GF_LDS char* As, const GF_LDS char* Bs, int off,
+                                           half8 (&af)[Cfg::FM], half8 (&bf)[Cfg::FN])
+{
+#pragma unroll
+    for (int fm = 0; fm < Cfg::FM; ++fm)
+        af[fm] = *(const GF_LDS half8*)(As + fm * Cfg::MT * (Cfg::BK * 2) + off);
+#pragma unroll
+    for (int fn = 0; fn < Cfg::FN; ++fn)
+        bf[fn] = *(const GF_LDS half8*)(Bs + fn * Cfg::MT * (Cfg::BK * 2) + off);
+}
+
+// sched_group_barrier instruction classes
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+
+// All MFMA steps of one K tile, with two kinds of memory traffic woven into
+// the MFMA stream instead of being issued in bursts:
+//  * fragments are double-buffered in registers: the LDS reads of step ks+1
+//    go out between the first MFMAs of step ks;
+//  * the direct-to-LDS loads of a later K tile (when LOAD) are spread
+//    one per few MFMAs over the first half of the steps.  A burst of them
+//    backs up the address path and stalls the issuing wave, and with it the
+//    wave's matrix core.
+template <class Cfg, bool LOAD>
 __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, int wn, int lane,
-                                             typename Mfma<Cfg::MT>::acc_t (&acc)[Cfg::FM][Cfg::FN])
+                                             typename Mfma<Cfg::MT>::acc_t (&acc)[Cfg::FM][Cfg::FN],
+                                             const GemmArgs& a, const DmaLoader<Cfg>& ld,
+                                             GF_LDS char* lstage, uint32_t k0b, int wave)
 {
     constexpr int MT = Cfg::MT;
+    constexpr int KSTEPS = Cfg::BK / Cfg::KS;
+    constexpr int NM = Cfg::FM * Cfg::FN;                  // MFMAs per step
+    constexpr int ND = Cfg::FM + Cfg::FN;                  // fragment reads per step
+    constexpr int LSTEPS = KSTEPS >= 2 ? KSTEPS / 2 : 1;   // steps that carry tile loads
+    constexpr int NV = (Cfg::LPS + LSTEPS - 1) / LSTEPS;   // tile loads per such step
+    constexpr int SP = NM / NV > 0 ? NM / NV : 1;          // MFMAs between two tile loads
     const int lrow = lane % MT;      // operand row (A) / column (B) this lane feeds
     const int lk = lane / MT;        // which 8-element K group of the MFMA step
     const int key = swz_key(lrow, Cfg::ROWS_PER_SWZ, Cfg::CH);
     const GF_LDS char* As = stage + (wm * Cfg::WTM + lrow) * (Cfg::BK * 2);
     const GF_LDS char* Bs = stage + Cfg::A_BYTES + (wn * Cfg::WTN + lrow) * (Cfg::BK * 2);
-#pragma unroll
-    for (int ks = 0; ks < Cfg::BK / Cfg::KS; ++ks) {
-        const int chunk = ks * (Cfg::KS / 8) + lk;
-        const int off = ((chunk ^ key) * 16);
-        half8 af[Cfg::FM], bf[Cfg::FN];
-#pragma unroll
-        for (int fm = 0; fm < Cfg::FM; ++fm)
-            af[fm] = *(const GF_LDS half8*)(As + fm * MT * (Cfg::BK * 2) + off);
-#pragma unroll
-        for (int fn = 0; fn < Cfg::FN; ++fn)
-            bf[fn] = *(const GF_LDS half8*)(Bs + fn * MT * (Cfg::BK * 2) + off);
-#pragma unroll
-        for (int fm = 0; fm < Cfg::FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < Cfg::FN; ++fn)
-                acc[fm][fn] = Mfma<MT>::run(af[fm], bf[fn], acc[fm][fn]);
+    half8 af[2][Cfg::FM], bf[2][Cfg::FN];
+    load_frags<Cfg>(As, Bs, ((lk ^ key) * 16), af[0], bf[0]);
+    static_for<KSTEPS>([&](auto ks_c) {
+        constexpr int ks = decltype(ks_c)::value;
+        constexpr int cur = ks & 1;
+        const int noff = (((ks + 1) * (Cfg::KS / 8) + lk) ^ key) * 16;
+        // Which tile load (if any) follows MFMA i of this step.
+        auto load_at = [](int i) constexpr {
+            return (LOAD && ks < LSTEPS && i % SP == 0 && i / SP < NV &&
+                    ks * NV + i / SP < Cfg::LPS) ? ks * NV + i / SP : -1;
+        };
+        static_for<NM>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int fm = i / Cfg::FN, fn = i % Cfg::FN;
+            acc[fm][fn] = Mfma<MT>::run(af[cur][fm], bf[cur][fn], acc[fm][fn]);
+            if constexpr (ks + 1 < KSTEPS && i < ND) {
+                if constexpr (i < Cfg::FM)
+                    af[cur ^ 1][i] = *(const GF_LDS half8*)(As + i * MT * (Cfg::BK * 2) + noff);
+                else
+                    bf[cur ^ 1][i - Cfg::FM] =
+                        *(const GF_LDS half8*)(Bs + (i - Cfg::FM) * MT * (Cfg::BK * 2) + noff);
+            }
+            if constexpr (load_at(i) >= 0)
+                ld.issue(a, lstage, k0b, load_at(i), wave);
+        });
+        // Fragment reads that found no MFMA to follow (FM * FN < FM + FN).
+        static_for<ND>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            if constexpr (ks + 1 < KSTEPS && i >= NM) {
+                if constexpr (i < Cfg::FM)
+                    af[cur ^ 1][i] = *(const GF_LDS half8*)(As + i * MT * (Cfg::BK * 2) + noff);
+                else
+                    bf[cur ^ 1][i - Cfg::FM] =
+                        *(const GF_LDS half8*)(Bs + (i - Cfg::FM) * MT * (Cfg::BK * 2) + noff);
+            }
+        });
+        static_for<NM>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if constexpr (ks + 1 < KSTEPS && i < ND)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            if constexpr (load_at(i) >= 0)
+                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    // Tile loads that found no slot in the MFMA stream (only when a step has
+    // more loads than MFMAs).
+    if constexpr (LOAD && NV > (NM + SP - 1) / SP) {
+        static_for<LSTEPS>([&](auto ks_c) {
+            constexpr int ks = decltype(ks_c)::value;
+            static_for<NV>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                if constexpr (j >= (NM + SP - 1) / SP && ks * NV + j < Cfg::LPS)
+                    ld.issue(a, lstage, k0b, ks * NV + j, wave);
+            });
+        });
     }
 }
 
@@ -208,6 +323,7 @@ __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, i
 template <class Cfg, int EPI, bool ALIGNED>
 __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
 {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     typedef Mfma<Cfg::MT> MF;
     typedef typename MF::acc_t acc_t;
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
@@ -245,13 +361,18 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
             for (int i = 0; i < MF::NACC; ++i) acc[fm][fn][i] = 0.0f;
 
     auto stage_ptr = [&](int s) { return smem + s * Cfg::STAGE_BYTES; };
-    auto issue = [&](int s, int kt) {
-        const int k0 = (kt_begin + kt) * Cfg::BK;
+    auto k0_of = [&](int kt) { return (kt_begin + kt) * Cfg::BK; };
+    DmaLoader<Cfg> ld;
+    if constexpr (ALIGNED) ld.init(a, m0, n0, tid);
+    // Whole-tile load, used where nothing can overlap it (pipeline prologue,
+    // single-stage configs, and the masked unaligned path).
+    auto burst = [&](int s, int kt) {
+        const int k0 = k0_of(kt);
         if constexpr (ALIGNED) {
             if (k0 + Cfg::BK <= a.K)
-                issue_tile_dma<Cfg, false>(a, stage_ptr(s), m0, n0, k0, tid, wave);
+                ld.issue_all(a, stage_ptr(s), k0, wave);
             else
-                issue_tile_dma<Cfg, true>(a, stage_ptr(s), m0, n0, k0, tid, wave);
+                ld.issue_all_masked(a, stage_ptr(s), k0, wave);
         } else {
             load_tile_masked<Cfg>(a, stage_ptr(s), m0, n0, k0, tid);
         }
@@ -260,25 +381,44 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
     if constexpr (Cfg::STAGES == 1) {
         for (int kt = 0; kt < nk; ++kt) {
             lds_barrier();                       // everyone is done with the buffer
-            issue(0, kt);
+            burst(0, kt);
             wait_vmcnt<0>();
             lds_barrier();
-            compute_tile<Cfg>(stage_ptr(0), wm, wn, lane, acc);
+            compute_tile<Cfg, false>(stage_ptr(0), wm, wn, lane, acc, a, ld, nullptr, 0, wave);
         }
     } else {
 #pragma unroll
         for (int s = 0; s < Cfg::STAGES - 1; ++s)
-            if (s < nk) issue(s, s);
-        for (int kt = 0; kt < nk; ++kt) {
+            if (s < nk) burst(s, s);
+        // Steady state: the tile fetched during tile kt is kt + STAGES - 1 and
+        // lies wholly inside K, so its loads can be woven into the MFMA stream.
+        // The last STAGES - 1 tiles (and a ragged final tile's fetch) run in a
+        // separate drain loop; keeping the two loop bodies apart keeps the
+        // register allocator from merging their live ranges.
+        int fast_end = 0;
+        if constexpr (ALIGNED) {
+            const int nfull = (nk > 0 && k0_of(nk - 1) + Cfg::BK > a.K) ? nk - 1 : nk;
+            fast_end = max(0, nfull - (Cfg::STAGES - 1));
+        }
+        int kt = 0;
+        for (; kt < fast_end; ++kt) {
+            wait_vmcnt<Cfg::LPS * (Cfg::STAGES - 2)>();    // tile kt landed
+            lds_barrier();                       // tile kt visible; tile kt-1 consumed
+            const int kn = kt + Cfg::STAGES - 1;
+            compute_tile<Cfg, ALIGNED>(stage_ptr(kt % Cfg::STAGES), wm, wn, lane, acc, a, ld,
+                                       stage_ptr(kn % Cfg::STAGES), (uint32_t)k0_of(kn) * 2u, wave);
+        }
+        for (; kt < nk; ++kt) {
             // Tile kt has landed once at most STAGES-2 younger tiles are pending.
             if (kt + Cfg::STAGES - 2 < nk)
                 wait_vmcnt<Cfg::LPS * (Cfg::STAGES - 2)>();
             else
                 wait_vmcnt<0>();
-            lds_barrier();                       // tile kt visible; tile kt-1 consumed
-            if (kt + Cfg::STAGES - 1 < nk)
-                issue((kt + Cfg::STAGES - 1) % Cfg::STAGES, kt + Cfg::STAGES - 1);
-            compute_tile<Cfg>(stage_ptr(kt % Cfg::STAGES), wm, wn, lane, acc);
+            lds_barrier();
+            const int kn = kt + Cfg::STAGES - 1;
+            if (kn < nk) burst(kn % Cfg::STAGES, kn);
+            compute_tile<Cfg, false>(stage_ptr(kt % Cfg::STAGES), wm, wn, lane, acc, a, ld, nullptr,
+                                     0, wave);
         }
     }
 
@@ -351,6 +491,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
                         W[(size_t)grow * a.N + gcol] = acc[fm][fn][i];
                 }
     }
+#endif
 }
 
 // Host-side launch of one instantiation: grid = (tiles, slices).

@@ -28,6 +28,9 @@ def main(argv=None):
     ap.add_argument("--m", type=int, default=8192)
     ap.add_argument("--n", type=int, default=8192)
     ap.add_argument("--k", type=int, default=8192)
+    ap.add_argument("--cfg", default="",
+                    help="gemm tile config block_m,block_n,block_k,stages,threads,raster "
+                         "(default: the library's choice)")
     a = ap.parse_args(argv)
 
     import torch
@@ -39,7 +42,11 @@ def main(argv=None):
         A = torch.from_numpy(inputs.uniform_f16((a.m, a.k), 0, 0)).cuda()
         B = torch.from_numpy(inputs.uniform_f16((a.n, a.k), 0, 1)).cuda()
         C = torch.empty((a.m, a.n), dtype=torch.float16, device="cuda")
-        call = gf.prepare_gemm_f16_nt(A, B, C)
+        cfg = None
+        if a.cfg:
+            v = [int(t) for t in a.cfg.split(",")]
+            cfg = dict(zip(("block_m", "block_n", "block_k", "stages", "threads", "raster"), v))
+        call = gf.prepare_gemm_f16_nt(A, B, C, cfg=cfg)
         for _ in range(a.iters):
             call()
     elif a.op == "gemv":

@@ -85,7 +85,12 @@ def _emit(path, rec):
             f.write(line + "\n")
 
 
-def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
+def _parse_only(only):
+    """'bm,bn,bk,stages,threads;...' -> set of tuples (empty = all configs)."""
+    return {tuple(int(v) for v in item.split(",")) for item in only.split(";") if item.strip()}
+
+
+def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
     import torch
     import gemv_fp16_amd as gf
     import inputs
@@ -100,7 +105,11 @@ def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
     seen = _done(out)
     flops = 2.0 * M * N * K
     shape = [M, N, K]
+    keep = _parse_only(only)
     for cfg, ok in gf.gemm_configs():
+        if keep and (cfg["block_m"], cfg["block_n"], cfg["block_k"], cfg["stages"],
+                     cfg["threads"]) not in keep:
+            continue
         for raster in rasters:
             c = dict(cfg, raster=raster)
             key = json.dumps(["gemm", shape, c], sort_keys=True)
@@ -180,10 +189,11 @@ def main(argv=None):
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--raster", type=int, nargs="*", default=[0, 1])
     ap.add_argument("--out", default="")
+    ap.add_argument("--only", default="", help="gemm configs 'bm,bn,bk,stages,threads;...'")
     a = ap.parse_args(argv)
     t = time.time()
     if a.op == "gemm":
-        sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster))
+        sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster), a.only)
     else:
         sweep_gemv(a.n, a.k, a.reps, a.warmup, a.trials, a.out)
     print("sweep done in %.1f s" % (time.time() - t), file=sys.stderr, flush=True)

@@ -114,7 +114,7 @@ def test_gemv_validation(L):
 
 def test_config_tables(L):
     cfgs = gf.gemm_configs()
-    assert len(cfgs) == 108                       # 3 x 3 x 2 x 3 x 2 sweep grid
+    assert len(cfgs) == 108 + 16                  # 3x3x2x3x2 grid + deep BK=32 pipelines
     legal = [c for c, ok in cfgs if ok]
     assert len(legal) >= 90
     for c, ok in cfgs:
@@ -125,7 +125,8 @@ def test_config_tables(L):
     d = gf.gemm_default_config(8192, 8192, 8192)
     assert (d["block_m"], d["block_n"]) == (256, 256)
     assert any(c == {**d, "raster": 1} for c, ok in cfgs if ok)
+    assert d["raster"] in (0, 1)
     assert gf.gemv_default_config(8192, 8192) in gf.gemv_configs()
     bad = gf.GemmCfg()
     assert L.gf_gemm_config_get(-1, ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
-    assert L.gf_gemm_config_get(108, ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
+    assert L.gf_gemm_config_get(len(cfgs), ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
