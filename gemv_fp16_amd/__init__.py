@@ -27,7 +27,7 @@ EXPORTS = (
 
 class GemmCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
-                ("block_m", "block_n", "block_k", "stages", "threads", "raster")]
+                ("block_m", "block_n", "block_k", "stages", "threads", "raster", "schedule")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -34,7 +34,7 @@ int find_gemm(const gf_gemm_cfg& c)
     for (int i = 0; i < kNumGemm; ++i) {
         const GemmDesc& d = kGemmConfigs[i];
         if (d.bm == c.block_m && d.bn == c.block_n && d.bk == c.block_k && d.stages == c.stages &&
-            d.threads == c.threads)
+            d.threads == c.threads && d.sched == c.schedule)
             return i;
     }
     return -1;
@@ -42,10 +42,11 @@ int find_gemm(const gf_gemm_cfg& c)
 
 int panel_of(int raster) { return raster <= 0 ? 0 : (raster == 1 ? kDefaultPanel : raster); }
 
-gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster)
+gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched = 0)
 {
     gf_gemm_cfg c;
     c.block_m = bm; c.block_n = bn; c.block_k = bk; c.stages = s; c.threads = t; c.raster = raster;
+    c.schedule = sched;
     return c;
 }
 
@@ -287,7 +288,7 @@ int gf_gemm_config_get(int i, gf_gemm_cfg* out)
 {
     if (i < 0 || i >= kNumGemm || !out) return GF_ERR_INVALID_ARG;
     const GemmDesc& d = kGemmConfigs[i];
-    *out = make_cfg(d.bm, d.bn, d.bk, d.stages, d.threads, 1);
+    *out = make_cfg(d.bm, d.bn, d.bk, d.stages, d.threads, 1, d.sched);
     // A config with no compiled kernel (illegal LDS or wave layout) is unsupported.
     return g_gemm_table[i][EPI_F16 * 2 + 1] ? GF_OK : GF_ERR_UNSUPPORTED;
 }

@@ -6,12 +6,12 @@
 namespace gf {
 
 struct GemmDesc {
-    int bm, bn, bk, stages, threads;
+    int bm, bn, bk, stages, threads, sched;
     bool core;
 };
 
 constexpr GemmDesc kGemmConfigs[] = {
-#define GF_GEMM(BM, BN, BK, S, T, CORE) {BM, BN, BK, S, T, CORE != 0},
+#define GF_GEMM(BM, BN, BK, S, T, SCHED, CORE) {BM, BN, BK, S, T, SCHED, CORE != 0},
 #include "gemm_configs.def"
 #undef GF_GEMM
 };

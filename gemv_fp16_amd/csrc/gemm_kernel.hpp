@@ -47,9 +47,12 @@ struct GemmArgs {
 // 16 zero bytes: the source of direct-to-LDS chunks that lie beyond K.
 static __device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
 
-template <int BM_, int BN_, int BK_, int STAGES_, int NT_>
+// SCHED 0: every wave interleaves its loads with its MFMAs.  SCHED 1: two
+// wave groups alternate memory and MFMA phases ("ping-pong"; 8 waves, 2x4
+// wave grid, at least 2 stages).
+template <int BM_, int BN_, int BK_, int STAGES_, int NT_, int SCHED_ = 0>
 struct GemmCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, NT = NT_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, NT = NT_, SCHED = SCHED_;
     static constexpr int NWAVES = NT / kWave;
     // Square-ish wave grid; the longer tile side gets more waves.
     static constexpr int WM = (NWAVES == 4) ? 2 : (NWAVES == 8 ? (BM > BN ? 4 : 2) : 1);
@@ -74,7 +77,8 @@ struct GemmCfg {
         (NWAVES == 4 || NWAVES == 8) && WTM % MT == 0 && WTN % MT == 0 && WTM >= 16 &&
         WTN >= 16 && BK % KS == 0 && (CH == 4 || CH == 8) && ((BM + BN) * CH) % NT == 0 &&
         (BM * CH) % kWave == 0 && STAGES >= 1 && STAGES <= 4 && LDS_BYTES <= 160 * 1024 &&
-        LPS * (STAGES > 2 ? STAGES - 2 : 0) < 64 && (WTM * (WTN / 8)) % kWave == 0;
+        LPS * (STAGES > 2 ? STAGES - 2 : 0) < 64 && (WTM * (WTN / 8)) % kWave == 0 &&
+        (SCHED == 0 || (NWAVES == 8 && WM == 2 && STAGES >= 2 && LPS * (STAGES - 1) < 64));
 };
 
 __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
@@ -317,6 +321,44 @@ __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, i
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong phases (SCHED 1)
+// ---------------------------------------------------------------------------
+
+// Memory phase, part 1: every fragment this wave needs for one K tile, read
+// from LDS into registers (FM + FN reads per MFMA step).
+template <class Cfg>
+__device__ __forceinline__ void read_tile_frags(const GF_LDS char* stage, int wm, int wn, int lane,
+                                                half8 (&af)[Cfg::BK / Cfg::KS][Cfg::FM],
+                                                half8 (&bf)[Cfg::BK / Cfg::KS][Cfg::FN])
+{
+    constexpr int MT = Cfg::MT;
+    const int lrow = lane % MT, lk = lane / MT;
+    const int key = swz_key(lrow, Cfg::ROWS_PER_SWZ, Cfg::CH);
+    const GF_LDS char* As = stage + (wm * Cfg::WTM + lrow) * (Cfg::BK * 2);
+    const GF_LDS char* Bs = stage + Cfg::A_BYTES + (wn * Cfg::WTN + lrow) * (Cfg::BK * 2);
+    static_for<Cfg::BK / Cfg::KS>([&](auto ks_c) {
+        constexpr int ks = decltype(ks_c)::value;
+        load_frags<Cfg>(As, Bs, (((ks * (Cfg::KS / 8) + lk) ^ key) * 16), af[ks], bf[ks]);
+    });
+}
+
+// MFMA phase: the whole K tile from registers, nothing else in the stream.
+template <class Cfg>
+__device__ __forceinline__ void mfma_tile(typename Mfma<Cfg::MT>::acc_t (&acc)[Cfg::FM][Cfg::FN],
+                                          const half8 (&af)[Cfg::BK / Cfg::KS][Cfg::FM],
+                                          const half8 (&bf)[Cfg::BK / Cfg::KS][Cfg::FN])
+{
+    static_for<Cfg::BK / Cfg::KS>([&](auto ks_c) {
+        constexpr int ks = decltype(ks_c)::value;
+        static_for<Cfg::FM * Cfg::FN>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            constexpr int fm = i / Cfg::FN, fn = i % Cfg::FN;
+            acc[fm][fn] = Mfma<Cfg::MT>::run(af[ks][fm], bf[ks][fn], acc[fm][fn]);
+        });
+    });
+}
+
+// ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
 
@@ -378,7 +420,68 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         }
     };
 
-    if constexpr (Cfg::STAGES == 1) {
+    if constexpr (Cfg::SCHED == 1 && ALIGNED) {
+        // Ping-pong.  Group g = wm (waves 0-3 own tile rows [0, WTM), waves
+        // 4-7 the rest); the two waves on a SIMD belong to different groups.
+        // Both groups run the same loop -- M phase (read this tile's
+        // fragments into registers, issue this wave's share of the loads of
+        // tile t + D, D = STAGES - 1), barrier, C phase (MFMAs only), barrier
+        // -- with group 1 one phase behind group 0, so that on every SIMD one
+        // wave multiplies while the other moves data.  Stage (t + D) % STAGES
+        // last held tile t - 1, which both groups finished reading before
+        // the barrier that opens group 0's M phase of tile t.
+        // Every wave waits for its own loads of tile t + 1 before the barrier
+        // that ends each phase of tile t, so that tile is complete when the
+        // next M phase reads it.
+        constexpr int D = Cfg::STAGES - 1;
+        constexpr int KST = Cfg::BK / Cfg::KS;
+        const int g = wm;
+        half8 af[KST][Cfg::FM], bf[KST][Cfg::FN];
+        auto issue_tile = [&](int t) {
+            const int k0 = k0_of(t);
+            if (k0 + Cfg::BK <= a.K)
+                ld.issue_all(a, stage_ptr(t % Cfg::STAGES), k0, wave);
+            else
+                ld.issue_all_masked(a, stage_ptr(t % Cfg::STAGES), k0, wave);
+        };
+        for (int t = 0; t < D; ++t)
+            if (t < nk) issue_tile(t);
+        wait_vmcnt<0>();
+        lds_barrier();                           // tiles 0 .. D-1 resident
+        if (g == 1) lds_barrier();               // group 1 starts one phase later
+        // Steady state: tile t + D exists and lies inside K.  Loads of up to
+        // D tiles may be pending; tile t + 1 must be done at each barrier, so
+        // D - 1 younger tiles stay in flight.  The tail loop below takes the
+        // last tiles (and a ragged final tile's loads) and drains everything;
+        // the two loops are kept apart so that no wait sits under a branch
+        // (a scalar s_waitcnt in a flattened branch would run on both sides).
+        const int nfull = (nk > 0 && k0_of(nk - 1) + Cfg::BK > a.K) ? nk - 1 : nk;
+        const int steady_end = max(0, nfull - D);
+        int t = 0;
+        for (; t < steady_end; ++t) {
+            read_tile_frags<Cfg>(stage_ptr(t % Cfg::STAGES), wm, wn, lane, af, bf);
+            ld.issue_all(a, stage_ptr((t + D) % Cfg::STAGES), k0_of(t + D), wave);
+            wait_vmcnt<Cfg::LPS * (D - 1)>();
+            lds_barrier();
+            __builtin_amdgcn_s_setprio(1);
+            mfma_tile<Cfg>(acc, af, bf);
+            __builtin_amdgcn_s_setprio(0);
+            wait_vmcnt<Cfg::LPS * (D - 1)>();
+            lds_barrier();
+        }
+        for (; t < nk; ++t) {
+            read_tile_frags<Cfg>(stage_ptr(t % Cfg::STAGES), wm, wn, lane, af, bf);
+            if (t + D < nk) issue_tile(t + D);
+            wait_vmcnt<0>();
+            lds_barrier();
+            __builtin_amdgcn_s_setprio(1);
+            mfma_tile<Cfg>(acc, af, bf);
+            __builtin_amdgcn_s_setprio(0);
+            wait_vmcnt<0>();
+            lds_barrier();
+        }
+        if (g == 0) lds_barrier();               // matches group 1's extra barrier
+    } else if constexpr (Cfg::STAGES == 1) {
         for (int kt = 0; kt < nk; ++kt) {
             lds_barrier();                       // everyone is done with the buffer
             burst(0, kt);

@@ -16,7 +16,7 @@ void register_from()
     if constexpr (I < kNumGemm) {
         if constexpr (I % kGemmShards == GF_SHARD) {
             constexpr GemmDesc d = kGemmConfigs[I];
-            typedef GemmCfg<d.bm, d.bn, d.bk, d.stages, d.threads> C;
+            typedef GemmCfg<d.bm, d.bn, d.bk, d.stages, d.threads, d.sched> C;
             if constexpr (C::kValid) {
                 g_gemm_table[I][EPI_F16 * 2 + 1] = &launch_gemm<C, EPI_F16, true>;
                 if constexpr (d.core) {

@@ -29,7 +29,7 @@ def main(argv=None):
     ap.add_argument("--n", type=int, default=8192)
     ap.add_argument("--k", type=int, default=8192)
     ap.add_argument("--cfg", default="",
-                    help="gemm tile config block_m,block_n,block_k,stages,threads,raster "
+                    help="gemm tile config block_m,block_n,block_k,stages,threads,raster[,schedule] "
                          "(default: the library's choice)")
     a = ap.parse_args(argv)
 
@@ -45,7 +45,8 @@ def main(argv=None):
         cfg = None
         if a.cfg:
             v = [int(t) for t in a.cfg.split(",")]
-            cfg = dict(zip(("block_m", "block_n", "block_k", "stages", "threads", "raster"), v))
+            cfg = dict(zip(("block_m", "block_n", "block_k", "stages", "threads", "raster",
+                            "schedule"), v + [0] * (7 - len(v))))
         call = gf.prepare_gemm_f16_nt(A, B, C, cfg=cfg)
         for _ in range(a.iters):
             call()

@@ -86,8 +86,13 @@ def _emit(path, rec):
 
 
 def _parse_only(only):
-    """'bm,bn,bk,stages,threads;...' -> set of tuples (empty = all configs)."""
-    return {tuple(int(v) for v in item.split(",")) for item in only.split(";") if item.strip()}
+    """'bm,bn,bk,stages,threads[,schedule];...' -> set of tuples (empty = all)."""
+    out = set()
+    for item in only.split(";"):
+        if item.strip():
+            v = [int(t) for t in item.split(",")]
+            out.add(tuple(v + [0] * (6 - len(v))))
+    return out
 
 
 def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
@@ -108,7 +113,7 @@ def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
     keep = _parse_only(only)
     for cfg, ok in gf.gemm_configs():
         if keep and (cfg["block_m"], cfg["block_n"], cfg["block_k"], cfg["stages"],
-                     cfg["threads"]) not in keep:
+                     cfg["threads"], cfg["schedule"]) not in keep:
             continue
         for raster in rasters:
             c = dict(cfg, raster=raster)
@@ -189,7 +194,7 @@ def main(argv=None):
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--raster", type=int, nargs="*", default=[0, 1])
     ap.add_argument("--out", default="")
-    ap.add_argument("--only", default="", help="gemm configs 'bm,bn,bk,stages,threads;...'")
+    ap.add_argument("--only", default="", help="gemm configs 'bm,bn,bk,stages,threads[,schedule];...'")
     a = ap.parse_args(argv)
     t = time.time()
     if a.op == "gemm":

@@ -88,7 +88,8 @@ size_t gemm_f16_nt_splitk_workspace_bytes(int M, int N, int split_k);
  * like gemm_f16_nt_splitk (workspace ignored, may be NULL).
  * mode = GF_SPLITK_TWOPASS: pass 1 stores slice s's partial tile into
  * workspace[s][M][N] (fp32, caller-owned device memory of at least
- * gemm_f16_nt_splitk_workspace_bytes(M, N, split_k) bytes, 16-byte aligned);
+ * gemm_f16_nt_splitk_workspace_bytes(M, N, split_k) bytes, at least 4-byte
+ * aligned; with 16-byte alignment and M*N % 4 == 0 the reduce uses float4);
  * pass 2 sums the slices in ascending s into C32.  The two-pass result is
  * bitwise reproducible from run to run.
  * Returns GF_ERR_INVALID_ARG for a bad mode or a NULL / short workspace in
@@ -99,11 +100,14 @@ int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N
                           void* stream);
 
 /* Tile configuration of the GEMM kernel (used by the offline sweep).
- * block_m x block_n x block_k tile, `stages` LDS buffers (1..3), `threads`
- * per workgroup (256 or 512), raster = 1 for the grouped, XCD-aware
- * workgroup order, 0 for plain row-major tile order. */
+ * block_m x block_n x block_k tile, `stages` LDS buffers (1..4), `threads`
+ * per workgroup (256 or 512).  raster: 0 = plain row-major tile order;
+ * 1 = XCD-aware grouped order with panels of 10 tile-rows; n >= 2 = the
+ * same with panels of n tile-rows.  schedule: 0 = every wave interleaves
+ * its operand loads with its MFMAs; 1 = two wave groups alternate a memory
+ * phase and an MFMA-only phase ("ping-pong", 512 threads only). */
 typedef struct gf_gemm_cfg {
-    int block_m, block_n, block_k, stages, threads, raster;
+    int block_m, block_n, block_k, stages, threads, raster, schedule;
 } gf_gemm_cfg;
 
 /* GEMV launch shape: rows per wave, 16-byte W loads in flight per row and

@@ -72,13 +72,15 @@ def test_gemm_validation(L):
 
 
 def test_gemm_cfg_validation(L):
-    good = gf.GemmCfg(128, 128, 64, 2, 256, 1)
-    bad = gf.GemmCfg(128, 128, 48, 2, 256, 1)
-    illegal = gf.GemmCfg(256, 256, 64, 3, 256, 1)     # 192 KiB of LDS
+    good = gf.GemmCfg(128, 128, 64, 2, 256, 1, 0)
+    bad = gf.GemmCfg(128, 128, 48, 2, 256, 1, 0)
+    illegal = gf.GemmCfg(256, 256, 64, 3, 256, 1, 0)  # 192 KiB of LDS
+    badsched = gf.GemmCfg(128, 128, 64, 2, 256, 1, 1)  # ping-pong needs 512 threads
     assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 4, 4, 4, None, NULL) == gf.GF_ERR_INVALID_ARG
     assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 0, 4, 4, ctypes.byref(good), NULL) == gf.GF_OK
     assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 0, 4, 4, ctypes.byref(bad), NULL) == gf.GF_ERR_UNSUPPORTED
     assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 4, 4, 4, ctypes.byref(illegal), NULL) == gf.GF_ERR_UNSUPPORTED
+    assert L.gemm_f16_nt_cfg(FAKE, FAKE, FAKE, 4, 4, 4, ctypes.byref(badsched), NULL) == gf.GF_ERR_UNSUPPORTED
 
 
 def test_splitk_validation(L):
@@ -114,7 +116,8 @@ def test_gemv_validation(L):
 
 def test_config_tables(L):
     cfgs = gf.gemm_configs()
-    assert len(cfgs) == 108 + 16                  # 3x3x2x3x2 grid + deep BK=32 pipelines
+    assert len(cfgs) == 108 + 16 + 6              # 3x3x2x3x2 grid + deep BK=32 + ping-pong
+    assert sum(1 for c, ok in cfgs if ok and c["schedule"] == 1) >= 5
     legal = [c for c, ok in cfgs if ok]
     assert len(legal) >= 90
     for c, ok in cfgs:
@@ -125,6 +128,9 @@ def test_config_tables(L):
     d = gf.gemm_default_config(8192, 8192, 8192)
     assert (d["block_m"], d["block_n"]) == (256, 256)
     assert any(c == {**d, "raster": 1} for c, ok in cfgs if ok)
+    for c, ok in cfgs:
+        if c["schedule"] == 1:
+            assert c["threads"] == 512
     assert d["raster"] in (0, 1)
     assert gf.gemv_default_config(8192, 8192) in gf.gemv_configs()
     bad = gf.GemmCfg()
