@@ -34,7 +34,7 @@ class GemmCfg(ctypes.Structure):
 
 
 class GemvCfg(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int) for n in ("rows_per_wave", "unroll", "waves")]
+    _fields_ = [(n, ctypes.c_int) for n in ("rows_per_wave", "unroll", "waves", "blocks")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -195,13 +195,22 @@ int find_gemv(const gf_gemv_cfg& c)
     return -1;
 }
 
+// Launch shape for a GEMV.  From the offline sweep at N = K = 8192: a grid of
+// 512 eight-wave workgroups whose waves split K (2 rows per step, 2 loads
+// per row in flight) is best when K/8 divides into 8 x 64 x 2 chunks; other
+// large shapes use one row per wave with 8 loads in flight; small ones are
+// launch-bound and take one chunk per lane at a time.
 gf_gemv_cfg default_gemv_cfg(int N, int K)
 {
     gf_gemv_cfg c;
     if ((int64_t)N * K >= (int64_t)4096 * 4096) {
-        c.rows_per_wave = 2; c.unroll = 4; c.waves = 4;
+        if (K % 8 == 0 && (K / 8) % (8 * 64 * 2) == 0 && K <= 32768) {
+            c.rows_per_wave = 2; c.unroll = 2; c.waves = 8; c.blocks = 512;
+        } else {
+            c.rows_per_wave = 1; c.unroll = 8; c.waves = 8; c.blocks = 0;
+        }
     } else {
-        c.rows_per_wave = 1; c.unroll = 2; c.waves = 4;
+        c.rows_per_wave = 1; c.unroll = 1; c.waves = 8; c.blocks = 0;
     }
     return c;
 }
@@ -209,7 +218,7 @@ gf_gemv_cfg default_gemv_cfg(int N, int K)
 int gemv_impl(const void* W, const void* x, void* y, int N, int K, const gf_gemv_cfg& cfg,
               hipStream_t stream)
 {
-    if (N < 0 || K < 0 || (int64_t)N * K > kMaxElems) return GF_ERR_INVALID_ARG;
+    if (N < 0 || K < 0 || (int64_t)N * K > kMaxElems || cfg.blocks < 0) return GF_ERR_INVALID_ARG;
     if (N > 0 && K > 0 && (!W || !aligned(W, 2))) return GF_ERR_INVALID_ARG;
     if (N > 0 && K > 0 && (!x || !aligned(x, 2))) return GF_ERR_INVALID_ARG;
     if (N > 0 && (!y || !aligned(y, 2))) return GF_ERR_INVALID_ARG;
@@ -220,7 +229,7 @@ int gemv_impl(const void* W, const void* x, void* y, int N, int K, const gf_gemv
     GemvLaunchFn fn = g_gemv_table[idx][al ? 1 : 0];
     if (!fn) return GF_ERR_UNSUPPORTED;
     return launch_status(fn(static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(x),
-                            static_cast<uint16_t*>(y), N, K, stream));
+                            static_cast<uint16_t*>(y), N, K, cfg.blocks, stream));
 }
 
 }  // namespace
@@ -301,6 +310,7 @@ int gf_gemv_config_get(int i, gf_gemv_cfg* out)
     out->rows_per_wave = kGemvConfigs[i].rows;
     out->unroll = kGemvConfigs[i].unroll;
     out->waves = kGemvConfigs[i].waves;
+    out->blocks = 0;
     return GF_OK;
 }
 

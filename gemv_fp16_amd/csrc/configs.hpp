@@ -29,7 +29,7 @@ constexpr GemvDesc kGemvConfigs[] = {
 constexpr int kNumGemv = sizeof(kGemvConfigs) / sizeof(kGemvConfigs[0]);
 
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs&, int slices, hipStream_t);
-typedef hipError_t (*GemvLaunchFn)(const uint16_t*, const uint16_t*, uint16_t*, int, int,
+typedef hipError_t (*GemvLaunchFn)(const uint16_t*, const uint16_t*, uint16_t*, int, int, int,
                                    hipStream_t);
 
 // [config][epilogue * 2 + aligned]; nullptr = not compiled.

@@ -142,7 +142,7 @@ def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
             _emit(out, rec)
 
 
-def sweep_gemv(N, K, reps, warmup, trials, out):
+def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,)):
     import torch
     import gemv_fp16_amd as gf
     import inputs
@@ -159,7 +159,8 @@ def sweep_gemv(N, K, reps, warmup, trials, out):
     seen = _done(out)
     shape = [N, K]
     nbytes = 2.0 * N * K + 2.0 * K + 2.0 * N
-    for c in gf.gemv_configs():
+    cands = [dict(c0, blocks=nb) for c0 in gf.gemv_configs() for nb in blocks]
+    for c in cands:
         key = json.dumps(["gemv", shape, c], sort_keys=True)
         if key in seen:
             continue
@@ -173,7 +174,7 @@ def sweep_gemv(N, K, reps, warmup, trials, out):
         calls = [gf.prepare_gemv_f16(w, x, y, cfg=c) for w in Ws]
         state = [0]
 
-        def call():
+        def call(calls=calls, state=state):
             calls[state[0] % copies]()
             state[0] += 1
 
@@ -195,12 +196,13 @@ def main(argv=None):
     ap.add_argument("--raster", type=int, nargs="*", default=[0, 1])
     ap.add_argument("--out", default="")
     ap.add_argument("--only", default="", help="gemm configs 'bm,bn,bk,stages,threads[,schedule];...'")
+    ap.add_argument("--blocks", type=int, nargs="*", default=[0], help="gemv grid bounds (0 = none)")
     a = ap.parse_args(argv)
     t = time.time()
     if a.op == "gemm":
         sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster), a.only)
     else:
-        sweep_gemv(a.n, a.k, a.reps, a.warmup, a.trials, a.out)
+        sweep_gemv(a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.blocks))
     print("sweep done in %.1f s" % (time.time() - t), file=sys.stderr, flush=True)
 
 

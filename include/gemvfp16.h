@@ -111,9 +111,17 @@ typedef struct gf_gemm_cfg {
 } gf_gemm_cfg;
 
 /* GEMV launch shape: rows per wave, 16-byte W loads in flight per row and
- * lane, waves per workgroup. */
+ * lane, waves per workgroup, and blocks:
+ *   0     = one row group per wave, the grid covers N;
+ *   b > 0 = at most b workgroups that walk the row groups grid-stride.  When
+ *           the fast path applies, K <= 32768 and (K/8) is a multiple of
+ *           waves*64*unroll, a workgroup owns rows_per_wave rows at a time
+ *           and its waves split K (partials summed through LDS); otherwise,
+ *           with K <= 32768 and the fast path, each wave owns its rows and x
+ *           is staged in LDS once per workgroup; otherwise as for 0.
+ * Every shape gives the same result up to fp32 summation order. */
 typedef struct gf_gemv_cfg {
-    int rows_per_wave, unroll, waves;
+    int rows_per_wave, unroll, waves, blocks;
 } gf_gemv_cfg;
 
 /* gemm_f16_nt with an explicit tile config; GF_ERR_UNSUPPORTED when the

@@ -109,7 +109,9 @@ def test_gemv_validation(L):
     assert L.gemv_f16(FAKE, FAKE, NULL, 4, 4, s) == gf.GF_ERR_INVALID_ARG
     assert L.gemv_f16(FAKE, FAKE, ODD, 4, 4, s) == gf.GF_ERR_INVALID_ARG
     assert L.gemv_f16(NULL, NULL, NULL, 0, 4, s) == gf.GF_OK
-    c = gf.GemvCfg(3, 3, 3)
+    neg = gf.GemvCfg(1, 2, 4, -1)
+    assert L.gemv_f16_cfg(FAKE, FAKE, FAKE, 4, 4, ctypes.byref(neg), s) == gf.GF_ERR_INVALID_ARG
+    c = gf.GemvCfg(3, 3, 3, 0)
     assert L.gemv_f16_cfg(FAKE, FAKE, FAKE, 0, 4, ctypes.byref(c), s) == gf.GF_ERR_UNSUPPORTED
     assert L.gemv_f16_cfg(FAKE, FAKE, FAKE, 0, 4, None, s) == gf.GF_ERR_INVALID_ARG
 
@@ -132,7 +134,8 @@ def test_config_tables(L):
         if c["schedule"] == 1:
             assert c["threads"] == 512
     assert d["raster"] in (0, 1)
-    assert gf.gemv_default_config(8192, 8192) in gf.gemv_configs()
+    dg = gf.gemv_default_config(8192, 8192)
+    assert {**dg, "blocks": 0} in gf.gemv_configs() and dg["blocks"] >= 0
     bad = gf.GemmCfg()
     assert L.gf_gemm_config_get(-1, ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
     assert L.gf_gemm_config_get(len(cfgs), ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG

@@ -261,12 +261,37 @@ def test_gemv_every_config():
     xi = inputs.integer_f16((K,), 4, 1)
     ref_i = oracle.gemv_f16(Wi, xi)
     dW, dx, dWi, dxi = dev(W), dev(x), dev(Wi), dev(xi)
-    for cfg in gf.gemv_configs():
-        y = gf.gemv_f16(dW, dx, cfg=cfg)
-        yi = gf.gemv_f16(dWi, dxi, cfg=cfg)
-        torch.cuda.synchronize()
-        check_f16_tolerance(host_u16(y), ref, "gemv cfg %s" % cfg)
-        assert np.array_equal(host_u16(yi), ref_i), "gemv cfg %s integer" % cfg
+    for cfg0 in gf.gemv_configs():
+        for blocks in (0, 7, 256):        # one group per wave / grid-stride with x in LDS
+            cfg = dict(cfg0, blocks=blocks)
+            y = gf.gemv_f16(dW, dx, cfg=cfg)
+            yi = gf.gemv_f16(dWi, dxi, cfg=cfg)
+            torch.cuda.synchronize()
+            check_f16_tolerance(host_u16(y), ref, "gemv cfg %s" % cfg)
+            assert np.array_equal(host_u16(yi), ref_i), "gemv cfg %s integer" % cfg
+
+
+@pytest.mark.parametrize("N,K", [(8192, 8192), (1001, 4096), (33, 1024), (1000, 1001),
+                                 (3, 40000), (4097, 520)])
+@pytest.mark.parametrize("kind", ["uniform", "integer"])
+def test_gemv_bounded_grid(N, K, kind):
+    """Bounded-grid launches: the waves-split-K kernel (K/8 a multiple of
+    waves * 64 * unroll), the LDS-staged-x row-per-wave kernel, and the
+    global-x fallback (K too large for LDS), on the workload and ragged
+    shapes."""
+    W = inputs.make(kind, (N, K), 11, 0)
+    x = inputs.make(kind, (K,), 11, 1)
+    ref = oracle.gemv_f16(W, x)
+    for cfg in (dict(rows_per_wave=1, unroll=8, waves=4, blocks=512),
+                dict(rows_per_wave=2, unroll=4, waves=4, blocks=256),
+                dict(rows_per_wave=1, unroll=2, waves=8, blocks=3),
+                dict(rows_per_wave=4, unroll=2, waves=2, blocks=100),
+                dict(rows_per_wave=1, unroll=1, waves=2, blocks=5)):
+        got = run_gemv(W, x, cfg)
+        if kind == "integer":
+            assert np.array_equal(got, ref), "gemv %dx%d %s" % (N, K, cfg)
+        else:
+            check_f16_tolerance(got, ref, "gemv %dx%d %s" % (N, K, cfg))
 
 
 def test_gemv_matches_gemm_one_row_on_integers():
