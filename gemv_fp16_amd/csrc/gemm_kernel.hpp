@@ -49,7 +49,10 @@ static __device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0
 
 // SCHED 0: every wave interleaves its loads with its MFMAs.  SCHED 1: two
 // wave groups alternate memory and MFMA phases ("ping-pong"; 8 waves, 2x4
-// wave grid, at least 2 stages).
+// wave grid, at least 2 stages).  SCHED 2: one wave per SIMD (4 waves) with
+// the tile barrier placed before the last MFMA step of each K tile, so that
+// the next tile's first fragments and the loads into the freed stage are
+// issued under that step's MFMAs.  SCHED 3: SCHED 2 with 16x16x32 MFMAs.
 template <int BM_, int BN_, int BK_, int STAGES_, int NT_, int SCHED_ = 0>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, NT = NT_, SCHED = SCHED_;
@@ -58,7 +61,8 @@ struct GemmCfg {
     static constexpr int WM = (NWAVES == 4) ? 2 : (NWAVES == 8 ? (BM > BN ? 4 : 2) : 1);
     static constexpr int WN = NWAVES / WM;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int MT = (WTM % 32 == 0 && WTN % 32 == 0) ? 32 : 16;  // MFMA tile
+    static constexpr int MT =                                // MFMA tile
+        (SCHED != 3 && WTM % 32 == 0 && WTN % 32 == 0) ? 32 : 16;
     static constexpr int KS = (MT == 32) ? 16 : 32;                          // MFMA K
     static constexpr int FM = WTM / MT, FN = WTN / MT;
     static constexpr int CH = BK / 8;                        // 16-byte chunks per row
@@ -78,7 +82,10 @@ struct GemmCfg {
         WTN >= 16 && BK % KS == 0 && (CH == 4 || CH == 8) && ((BM + BN) * CH) % NT == 0 &&
         (BM * CH) % kWave == 0 && STAGES >= 1 && STAGES <= 4 && LDS_BYTES <= 160 * 1024 &&
         LPS * (STAGES > 2 ? STAGES - 2 : 0) < 64 && (WTM * (WTN / 8)) % kWave == 0 &&
-        (SCHED == 0 || (NWAVES == 8 && WM == 2 && STAGES >= 2 && LPS * (STAGES - 1) < 64));
+        (SCHED == 0 ||
+         (SCHED == 1 && NWAVES == 8 && WM == 2 && STAGES >= 2 && LPS * (STAGES - 1) < 64) ||
+         ((SCHED == 2 || SCHED == 3) && NWAVES == 4 && STAGES >= 2 && (BK / KS) % 2 == 0 &&
+          LPS % 2 == 0 && LPS * STAGES < 64));
 };
 
 __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
@@ -97,10 +104,19 @@ __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
 // 16-row swizzle period, the K chunk c a thread fetches is the same for all
 // r; only the row changes.  The row offsets are computed once per tile
 // position.
+#ifndef GF_DMA_BUFFER
+#define GF_DMA_BUFFER 1
+#endif
+
 template <class Cfg>
 struct DmaLoader {
     uint32_t voff[Cfg::LPS];   // byte offset of load r's chunk at k = 0 (row clamped)
     int c8;                    // this thread's K offset inside a tile: c * 8
+#if GF_DMA_BUFFER
+    // Buffer descriptors of A and B (raw, byte-addressed): the tile's K
+    // offset travels in the scalar offset, the row/chunk offset in voff.
+    __amdgpu_buffer_rsrc_t ra, rb;
+#endif
 
     __device__ __forceinline__ void init(const GemmArgs& a, int m0, int n0, int tid)
     {
@@ -115,6 +131,13 @@ struct DmaLoader {
             const int grow = is_a ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
             voff[r] = (uint32_t)(grow * a.K + c8) * 2u;
         }
+#if GF_DMA_BUFFER
+        constexpr int kRawBufferWord3 = 0x00020000;
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, (int)((uint32_t)a.M * (uint32_t)a.K * 2u),
+                                               kRawBufferWord3);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)a.B, 0, (int)((uint32_t)a.N * (uint32_t)a.K * 2u),
+                                               kRawBufferWord3);
+#endif
     }
 
     // Load r of the K tile whose first byte column is k0b = 2 * k0; every
@@ -124,9 +147,15 @@ struct DmaLoader {
     {
         const int wslot = r * Cfg::NT + wave * kWave;    // wave-uniform
         const bool is_a = wslot < Cfg::BM * Cfg::CH;     // wave-uniform
+#if GF_DMA_BUFFER
+        (void)a;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (GF_LDS void*)(stage + wslot * 16), 16,
+                                                 voff[r], k0b, 0, 0);
+#else
         const char* base = (const char*)(is_a ? a.A : a.B);
         __builtin_amdgcn_global_load_lds(base + (voff[r] + k0b), (GF_LDS void*)(stage + wslot * 16),
                                          16, 0, 0);
+#endif
     }
 
     __device__ __forceinline__ void issue_all(const GemmArgs& a, GF_LDS char* stage, int k0,
@@ -134,6 +163,32 @@ struct DmaLoader {
     {
 #pragma unroll
         for (int r = 0; r < Cfg::LPS; ++r) issue(a, stage, (uint32_t)k0 * 2u, r, wave);
+    }
+
+    // Loads R0 .. R1-1 of the K tile at k0; where the tile runs past K,
+    // chunks at k >= K read 16 zero bytes (so do all chunks of a tile that
+    // lies wholly beyond K).
+    template <int R0, int R1>
+    __device__ __forceinline__ void issue_range(const GemmArgs& a, GF_LDS char* stage, int k0,
+                                                int wave) const
+    {
+        if (k0 + Cfg::BK <= a.K) {
+            static_for<R1 - R0>([&](auto j) {
+                issue(a, stage, (uint32_t)k0 * 2u, R0 + decltype(j)::value, wave);
+            });
+        } else {
+            const bool valid = k0 + c8 < a.K;
+            static_for<R1 - R0>([&](auto j) {
+                constexpr int r = R0 + decltype(j)::value;
+                const int wslot = r * Cfg::NT + wave * kWave;
+                const bool is_a = wslot < Cfg::BM * Cfg::CH;
+                const char* base = (const char*)(is_a ? a.A : a.B);
+                const void* src = valid ? (const void*)(base + voff[r] + (size_t)k0 * 2)
+                                        : (const void*)g_zero16;
+                __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)(stage + wslot * 16), 16, 0,
+                                                 0);
+            });
+        }
     }
 
     // The same tile where it runs past K: chunks at k >= K read 16 zero bytes.
@@ -320,6 +375,67 @@ __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, i
     }
 }
 
+// One MFMA step of SCHED 2/3: the FM x FN MFMAs on fragment buffer CUR,
+// with the reads of the following step's fragments (rows As / Bs, byte
+// offset noff, possibly in another stage) into buffer CUR ^ 1 and the
+// direct-to-LDS loads R0 .. R1-1 of the tile at k0b woven into the stream.
+#ifndef GF_RPM
+#define GF_RPM 1
+#endif
+template <class Cfg, int CUR, int R0, int R1, int RPM = GF_RPM>
+__device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[Cfg::FM][Cfg::FN],
+                                          half8 (&af)[2][Cfg::FM], half8 (&bf)[2][Cfg::FN],
+                                          const GF_LDS char* As, const GF_LDS char* Bs, int noff,
+                                          const GemmArgs& a, const DmaLoader<Cfg>& ld,
+                                          GF_LDS char* lstage, uint32_t k0b, int wave)
+{
+    constexpr int MT = Cfg::MT;
+    constexpr int NM = Cfg::FM * Cfg::FN, ND = Cfg::FM + Cfg::FN, NL = R1 - R0;
+    constexpr int SP = NL > 0 ? (NM >= NL ? NM / (NL > 0 ? NL : 1) : 1) : NM + 1;  // MFMAs per load
+    constexpr int NLS = NL > 0 ? (NM + SP - 1) / SP : 0;                // loads in the stream
+    auto load_at = [](int i) constexpr {
+        return (i % SP == 0 && i / SP < NL) ? R0 + i / SP : -1;
+    };
+    // Read j fetches the fragment that the next step needs j-th: the MFMAs
+    // run row by row (A[fm] x B[0..FN-1]), so B0 and A0 first, then the
+    // rest of B, then A1 .. A[FM-1].  Each MFMA then waits only for its own
+    // operands instead of for the whole batch.
+    auto read = [&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        constexpr bool is_b = (j == 0) || (j >= 2 && j <= Cfg::FN);
+        constexpr int f = (j == 0 || j == 1) ? 0 : (is_b ? j - 1 : j - Cfg::FN);
+        if constexpr (is_b)
+            bf[CUR ^ 1][f] = *(const GF_LDS half8*)(Bs + f * MT * (Cfg::BK * 2) + noff);
+        else
+            af[CUR ^ 1][f] = *(const GF_LDS half8*)(As + f * MT * (Cfg::BK * 2) + noff);
+    };
+    static_for<NM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int fm = i / Cfg::FN, fn = i % Cfg::FN;
+        acc[fm][fn] = Mfma<MT>::run(af[CUR][fm], bf[CUR][fn], acc[fm][fn]);
+        static_for<RPM>([&](auto q_c) {
+            constexpr int j = i * RPM + decltype(q_c)::value;
+            if constexpr (j < ND) read(std::integral_constant<int, j>{});
+        });
+        if constexpr (load_at(i) >= 0) ld.issue(a, lstage, k0b, load_at(i), wave);
+    });
+    static_for<ND>([&](auto j_c) {
+        if constexpr (decltype(j_c)::value >= NM * RPM) read(j_c);
+    });
+    static_for<NL>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        if constexpr (j >= NLS) ld.issue(a, lstage, k0b, R0 + j, wave);
+    });
+    static_for<NM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int nr = (i + 1) * RPM <= ND ? RPM : (i * RPM < ND ? ND - i * RPM : 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nr, 0);
+        if constexpr (load_at(i) >= 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // Ping-pong phases (SCHED 1)
 // ---------------------------------------------------------------------------
@@ -481,6 +597,87 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
             lds_barrier();
         }
         if (g == 0) lds_barrier();               // matches group 1's extra barrier
+    } else if constexpr ((Cfg::SCHED == 2 || Cfg::SCHED == 3) && ALIGNED) {
+        // One wave per SIMD.  Tile t sits in stage t % S.  Barrier B(t) comes
+        // before the last MFMA step of tile t: by then every wave has read
+        // all of tile t's fragments (the last step's were read during the
+        // step before), and each wave has waited for its own loads of tile
+        // t + 1, so after B(t) tile t + 1 is complete and stage t % S is free.
+        // Under the last step's MFMAs each wave then reads tile t + 1's
+        // first fragments and issues the first half of tile t + S's loads
+        // into stage t % S; the second half follows in tile t + 1's first
+        // step.  At B(t) the loads of tiles t + 2 .. t + S - 1 may still be
+        // in flight: S - 2 tiles.  Loads are issued for every tile index,
+        // also past the slice (masked ones read zeros), so that the count
+        // of loads in flight, and with it every wait, is the same in every
+        // iteration; no wait sits under a branch.
+        constexpr int S = Cfg::STAGES;
+        constexpr int KST = Cfg::BK / Cfg::KS;
+        constexpr int H = Cfg::LPS / 2;            // loads issued under the last step
+        constexpr int MT = Cfg::MT;
+        const int lrow = lane % MT, lk = lane / MT;
+        const int key = swz_key(lrow, Cfg::ROWS_PER_SWZ, Cfg::CH);
+        auto a_rows = [&](int s) {
+            return (const GF_LDS char*)stage_ptr(s) + (wm * Cfg::WTM + lrow) * (Cfg::BK * 2);
+        };
+        auto b_rows = [&](int s) {
+            return (const GF_LDS char*)stage_ptr(s) + Cfg::A_BYTES +
+                   (wn * Cfg::WTN + lrow) * (Cfg::BK * 2);
+        };
+        auto frag_off = [&](int ks) { return ((ks * (Cfg::KS / 8) + lk) ^ key) * 16; };
+        half8 af[2][Cfg::FM], bf[2][Cfg::FN];
+        if (nk > 0) {
+#pragma unroll
+            for (int t = 0; t < S - 1; ++t)
+                ld.template issue_range<0, Cfg::LPS>(a, stage_ptr(t), k0_of(t), wave);
+        }
+        wait_vmcnt<Cfg::LPS * (S - 2)>();       // tile 0 landed
+        lds_barrier();
+        if (nk > 0) ld.template issue_range<0, H>(a, stage_ptr(S - 1), k0_of(S - 1), wave);
+        load_frags<Cfg>(a_rows(0), b_rows(0), frag_off(0), af[0], bf[0]);
+        // Steady state: tiles t + S - 1 and t + S lie wholly inside K, so
+        // their loads go into the MFMA stream unmasked.
+        const int nfull = (nk > 0 && k0_of(nk - 1) + Cfg::BK > a.K) ? nk - 1 : nk;
+        const int steady_end = max(0, nfull - S);
+        int t = 0;
+        for (; t < steady_end; ++t) {
+            const int s0 = t % S, s1 = (t + 1) % S, sl = (t + S - 1) % S;
+            const GF_LDS char* As = a_rows(s0);
+            const GF_LDS char* Bs = b_rows(s0);
+            static_for<KST - 1>([&](auto ks_c) {
+                constexpr int ks = decltype(ks_c)::value;
+                if constexpr (ks == 0)
+                    mfma_step<Cfg, 0, H, Cfg::LPS>(acc, af, bf, As, Bs, frag_off(1), a, ld,
+                                                   stage_ptr(sl), (uint32_t)k0_of(t + S - 1) * 2u,
+                                                   wave);
+                else
+                    mfma_step<Cfg, ks & 1, 0, 0>(acc, af, bf, As, Bs, frag_off(ks + 1), a, ld,
+                                                 nullptr, 0, wave);
+            });
+            wait_vmcnt<Cfg::LPS * (S - 2)>();   // tile t + 1 landed
+            lds_barrier();                       // B(t)
+            mfma_step<Cfg, (KST - 1) & 1, 0, H>(acc, af, bf, a_rows(s1), b_rows(s1), frag_off(0),
+                                                a, ld, stage_ptr(s0), (uint32_t)k0_of(t + S) * 2u,
+                                                wave);
+        }
+        for (; t < nk; ++t) {
+            const int s0 = t % S, s1 = (t + 1) % S, sl = (t + S - 1) % S;
+            const GF_LDS char* As = a_rows(s0);
+            const GF_LDS char* Bs = b_rows(s0);
+            ld.template issue_range<H, Cfg::LPS>(a, stage_ptr(sl), k0_of(t + S - 1), wave);
+            static_for<KST - 1>([&](auto ks_c) {
+                constexpr int ks = decltype(ks_c)::value;
+                mfma_step<Cfg, ks & 1, 0, 0>(acc, af, bf, As, Bs, frag_off(ks + 1), a, ld, nullptr,
+                                             0, wave);
+            });
+            wait_vmcnt<Cfg::LPS * (S - 2)>();
+            lds_barrier();
+            ld.template issue_range<0, H>(a, stage_ptr(s0), k0_of(t + S), wave);
+            // After the last tile these reads fetch stale data that no MFMA uses.
+            mfma_step<Cfg, (KST - 1) & 1, 0, 0>(acc, af, bf, a_rows(s1), b_rows(s1), frag_off(0),
+                                                a, ld, nullptr, 0, wave);
+        }
+        wait_vmcnt<0>();                         // no load may land after the epilogue starts
     } else if constexpr (Cfg::STAGES == 1) {
         for (int kt = 0; kt < nk; ++kt) {
             lds_barrier();                       // everyone is done with the buffer

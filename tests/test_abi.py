@@ -118,8 +118,10 @@ def test_gemv_validation(L):
 
 def test_config_tables(L):
     cfgs = gf.gemm_configs()
-    assert len(cfgs) == 108 + 16 + 6              # 3x3x2x3x2 grid + deep BK=32 + ping-pong
+    # 3x3x2x3x2 grid + deep BK=32 + ping-pong + one wave per SIMD
+    assert len(cfgs) == 108 + 16 + 6 + 8
     assert sum(1 for c, ok in cfgs if ok and c["schedule"] == 1) >= 5
+    assert sum(1 for c, ok in cfgs if ok and c["schedule"] in (2, 3)) == 8
     legal = [c for c, ok in cfgs if ok]
     assert len(legal) >= 90
     for c, ok in cfgs:
@@ -133,6 +135,8 @@ def test_config_tables(L):
     for c, ok in cfgs:
         if c["schedule"] == 1:
             assert c["threads"] == 512
+        if c["schedule"] in (2, 3):
+            assert c["threads"] == 256
     assert d["raster"] in (0, 1)
     dg = gf.gemv_default_config(8192, 8192)
     assert {**dg, "blocks": 0} in gf.gemv_configs() and dg["blocks"] >= 0
