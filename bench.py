@@ -227,6 +227,9 @@ def main():
                     a3, b3, c3, split, mode, ws), 50, 5)
                 sk["%s_s%d" % (name, split)] = round(f3 / t3 / 1e12, 1)
         c16 = torch.empty((sm, sm), dtype=torch.float16, device="cuda")
+        for split in (4, 8, 16):
+            t3 = time_batch(torch, lambda: gf.gemm_f16_nt_splitk_f16(a3, b3, c16, split, ws), 50, 5)
+            sk["twopass_f16out_s%d" % split] = round(f3 / t3 / 1e12, 1)
         t3 = time_batch(torch, lambda: gf.gemm_f16_nt(a3, b3, c16), 50, 5)
         sk["no_split_fp16"] = round(f3 / t3 / 1e12, 1)
         log("splitk 1024x1024x16384 TFLOP/s: %s" % sk)

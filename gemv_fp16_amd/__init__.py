@@ -18,7 +18,7 @@ GF_SPLITK_ATOMIC, GF_SPLITK_TWOPASS = 0, 1
 
 EXPORTS = (
     "gemm_f16_nt", "gemm_f16_nt_splitk", "gemv_f16",
-    "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex",
+    "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex", "gemm_f16_nt_splitk_f16",
     "gemm_f16_nt_cfg", "gemv_f16_cfg",
     "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
     "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_nt_splitk_workspace_bytes.argtypes = [ci, ci, ci]
     L.gemm_f16_nt_splitk_workspace_bytes.restype = sz
     L.gemm_f16_nt_splitk_ex.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
+    L.gemm_f16_nt_splitk_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, sz, vp]
     L.gemm_f16_nt_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.POINTER(GemmCfg), vp]
     L.gemv_f16_cfg.argtypes = [vp, vp, vp, ci, ci, ctypes.POINTER(GemvCfg), vp]
     L.gf_gemm_config_get.argtypes = [ci, ctypes.POINTER(GemmCfg)]
@@ -202,6 +203,27 @@ def gemm_f16_nt_splitk_ex(A, B, C32=None, split_k: int = 4, mode: int = GF_SPLIT
                                        _dev(C32, torch.float32, "C32"), M, N, K, split_k, mode,
                                        ws_ptr, ws_bytes, _stream(stream)), "gemm_f16_nt_splitk_ex")
     return C32
+
+
+def gemm_f16_nt_splitk_f16(A, B, C=None, split_k: int = 4, workspace=None, stream=None):
+    """Split-K with an fp16 output: the fp32 slice partials (workspace, fp32
+    CUDA tensor, allocated if not given) are summed in ascending slice order
+    and rounded once to fp16.  Returns C (M x N fp16)."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be (M, N)")
+    need = gemm_f16_nt_splitk_workspace_bytes(M, N, split_k)
+    if workspace is None:
+        workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=A.device)
+    _check(lib().gemm_f16_nt_splitk_f16(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
+                                        _dev(C, torch.float16, "C"), M, N, K, split_k,
+                                        _dev(workspace, torch.float32, "workspace"),
+                                        workspace.numel() * 4, _stream(stream)),
+           "gemm_f16_nt_splitk_f16")
+    return C
 
 
 def gemv_f16(W, x, y=None, stream=None, cfg: dict | None = None):

@@ -130,6 +130,49 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, float* __rest
     }
 }
 
+// C16[i] = fp16_rne(sum over s = 0 .. slices-1, ascending, of ws[s][i]):
+// the fp32 sum of the two-pass reduce, rounded once.  Eight outputs (two
+// float4 per slice in, one 16-byte store out) per thread.
+__global__ void splitk_reduce_f16x8_kernel(const floatx4* __restrict__ ws, u32x4* __restrict__ c,
+                                           int64_t n8, int slices)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = 2 * n8;
+    for (int64_t t = i; t < n8; t += stride) {
+        floatx4 lo = ws[2 * t], hi = ws[2 * t + 1];
+        for (int k = 1; k < slices; ++k) {
+            lo += ws[(int64_t)k * n4 + 2 * t];
+            hi += ws[(int64_t)k * n4 + 2 * t + 1];
+        }
+        u32x4 o;
+        o.x = f32_to_f16_bits(lo.x) | ((uint32_t)f32_to_f16_bits(lo.y) << 16);
+        o.y = f32_to_f16_bits(lo.z) | ((uint32_t)f32_to_f16_bits(lo.w) << 16);
+        o.z = f32_to_f16_bits(hi.x) | ((uint32_t)f32_to_f16_bits(hi.y) << 16);
+        o.w = f32_to_f16_bits(hi.z) | ((uint32_t)f32_to_f16_bits(hi.w) << 16);
+        c[t] = o;
+    }
+}
+
+__global__ void splitk_reduce_f16_kernel(const float* __restrict__ ws, uint16_t* __restrict__ c,
+                                         int64_t n, int slices)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = i; t < n; t += stride) {
+        float s = ws[t];
+        for (int k = 1; k < slices; ++k) s += ws[(int64_t)k * n + t];
+        c[t] = f32_to_f16_bits(s);
+    }
+}
+
+__global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = i; t < n; t += stride) p[t] = 0;
+}
+
 int grid_for(int64_t n, int block)
 {
     int64_t g = (n + block - 1) / block;
@@ -182,6 +225,42 @@ int splitk_impl(const void* A, const void* B, float* C32, int M, int N, int K, i
     } else {
         hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
                            static_cast<const float*>(ws), C32, mn, slices);
+    }
+    return launch_status(hipGetLastError());
+}
+
+// Split-K with an fp16 output: pass 1 stores each slice's fp32 partial tile
+// into the workspace, pass 2 sums the slices in ascending order and rounds
+// the sum once to fp16.
+int splitk_f16_impl(const void* A, const void* B, void* C, int M, int N, int K, int split_k,
+                    void* ws, size_t ws_bytes, const gf_gemm_cfg& cfg, hipStream_t stream)
+{
+    int rc = validate_gemm(A, B, C, M, N, K, 2);
+    if (rc) return rc;
+    if (split_k < 1 || split_k > 65535) return GF_ERR_INVALID_ARG;
+    const int64_t mn = (int64_t)M * N;
+    if ((uint64_t)ws_bytes < (uint64_t)split_k * (uint64_t)mn * sizeof(float)) return GF_ERR_INVALID_ARG;
+    if (mn > 0 && (!ws || !aligned(ws, 4))) return GF_ERR_INVALID_ARG;
+    if (find_gemm(cfg) < 0) return GF_ERR_UNSUPPORTED;
+    if (mn == 0) return GF_OK;
+
+    const int nkt = ceil_div(K, cfg.block_k);
+    const int kt_per = nkt > 0 ? ceil_div(nkt, split_k) : 0;
+    const int slices = nkt > 0 ? ceil_div(nkt, kt_per) : 0;
+    if (slices == 0) {                           // K == 0: the empty sum
+        hipLaunchKernelGGL(zero_u16_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
+                           static_cast<uint16_t*>(C), mn);
+        return launch_status(hipGetLastError());
+    }
+    rc = run_gemm(A, B, ws, M, N, K, cfg, EPI_F32_STORE, slices, kt_per, true, stream);
+    if (rc) return rc;
+    if (aligned(ws, 16) && aligned(C, 16) && mn % 8 == 0) {
+        hipLaunchKernelGGL(splitk_reduce_f16x8_kernel, dim3(grid_for(mn / 8, 256)), dim3(256), 0,
+                           stream, reinterpret_cast<const floatx4*>(ws), static_cast<u32x4*>(C),
+                           mn / 8, slices);
+    } else {
+        hipLaunchKernelGGL(splitk_reduce_f16_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
+                           static_cast<const float*>(ws), static_cast<uint16_t*>(C), mn, slices);
     }
     return launch_status(hipGetLastError());
 }
@@ -263,6 +342,13 @@ int gemm_f16_nt_splitk(const void* A, const void* B, float* C32, int M, int N, i
 {
     return splitk_impl(A, B, C32, M, N, K, split_k, GF_SPLITK_ATOMIC, nullptr, 0,
                        default_splitk_cfg(M, N, K), static_cast<hipStream_t>(stream));
+}
+
+int gemm_f16_nt_splitk_f16(const void* A, const void* B, void* C, int M, int N, int K,
+                           int split_k, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return splitk_f16_impl(A, B, C, M, N, K, split_k, workspace, workspace_bytes,
+                           default_splitk_cfg(M, N, K), static_cast<hipStream_t>(stream));
 }
 
 size_t gemm_f16_nt_splitk_workspace_bytes(int M, int N, int split_k)

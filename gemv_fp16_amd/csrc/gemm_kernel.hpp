@@ -80,7 +80,8 @@ struct GemmCfg {
     static constexpr bool kValid =
         (NWAVES == 4 || NWAVES == 8) && WTM % MT == 0 && WTN % MT == 0 && WTM >= 16 &&
         WTN >= 16 && BK % KS == 0 && (CH == 4 || CH == 8) && ((BM + BN) * CH) % NT == 0 &&
-        (BM * CH) % kWave == 0 && STAGES >= 1 && STAGES <= 4 && LDS_BYTES <= 160 * 1024 &&
+        (BM * CH) % kWave == 0 && STAGES >= 1 && STAGES <= (SCHED >= 2 ? 5 : 4) &&
+        LDS_BYTES <= 160 * 1024 &&
         LPS * (STAGES > 2 ? STAGES - 2 : 0) < 64 && (WTM * (WTN / 8)) % kWave == 0 &&
         (SCHED == 0 ||
          (SCHED == 1 && NWAVES == 8 && WM == 2 && STAGES >= 2 && LPS * (STAGES - 1) < 64) ||
@@ -754,7 +755,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
             const int grow = wrow0 + r, gcol = wcol0 + cc * 8;
             if (grow >= a.M) continue;
             if (vec_ok && gcol + 8 <= a.N) {
-                *(u32x4*)(C + (size_t)grow * a.N + gcol) = v;
+                // C is written once and not read back here: a streaming
+                // store keeps it from displacing operand lines in L2.
+                __builtin_nontemporal_store(v, (u32x4*)(C + (size_t)grow * a.N + gcol));
             } else {
                 const uint32_t parts[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -6,7 +6,7 @@
 Ops (inputs are the seeded uniform[-1,1] fp16 workloads):
   gemm    C = A . B^T at M = N = K = 8192 (default tile config)
   gemv    y = W . x at N = K = 8192, rotating 5 W copies (640 MiB)
-  splitk  C32 at M = N = 1024, K = 16384, split 8, atomic and two-pass
+  splitk  M = N = 1024, K = 16384, split 8: fp32 atomic, fp32 two-pass, fp16 two-pass
   copy    torch copy of a 512 MiB buffer: a plain copy kernel of known size,
           the calibration for the HBM byte counters
 """
@@ -61,10 +61,12 @@ def main(argv=None):
         A = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, 0)).cuda()
         B = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, 1)).cuda()
         C = torch.empty((1024, 1024), dtype=torch.float32, device="cuda")
+        C16 = torch.empty((1024, 1024), dtype=torch.float16, device="cuda")
         ws = torch.empty(8 * 1024 * 1024, dtype=torch.float32, device="cuda")
         for _ in range(a.iters):
             gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_ATOMIC, ws)
             gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_TWOPASS, ws)
+            gf.gemm_f16_nt_splitk_f16(A, B, C16, 8, ws)
     else:
         src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")   # 512 MiB
         dst = torch.empty_like(src)

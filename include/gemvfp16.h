@@ -99,6 +99,26 @@ int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N
                           int split_k, int mode, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * Split-K with an fp16 output: C = A . B^T, A M x K fp16, B N x K fp16,
+ * C M x N fp16.  Pass 1 stores slice s's fp32 partial tile into
+ * workspace[s][M][N]; pass 2 sums the slices in ascending s in fp32 and
+ * rounds each sum once to fp16 (round-to-nearest-even).  The result is
+ * therefore exactly the GF_SPLITK_TWOPASS fp32 result rounded to fp16, and
+ * bitwise reproducible from run to run.  workspace: caller-owned device
+ * memory of at least gemm_f16_nt_splitk_workspace_bytes(M, N, split_k)
+ * bytes, at least 4-byte aligned (16-byte alignment of workspace and C with
+ * M*N % 8 == 0 selects the vector reduce).  K == 0 writes +0 everywhere.
+ * Returns GF_ERR_INVALID_ARG for split_k < 1 or a NULL / short workspace.
+ * Defined by the "basic GEMM to SplitK" page, SplitK section: the split-K
+ * kernel takes its output type as a parameter (there float32); this is the
+ * same kernel with the fp16 output type, the fp32 slice sums rounded at the
+ * end as in the TileLang FP16 matmul page's fp32-accumulate / fp16-store
+ * GEMM (section 1).
+ */
+int gemm_f16_nt_splitk_f16(const void* A, const void* B, void* C, int M, int N, int K,
+                           int split_k, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Tile configuration of the GEMM kernel (used by the offline sweep).
  * block_m x block_n x block_k tile, `stages` LDS buffers (1..4), `threads`
  * per workgroup (256 or 512).  raster: 0 = plain row-major tile order;

@@ -100,6 +100,19 @@ def test_splitk_validation(L):
     assert L.gemm_f16_nt_splitk_workspace_bytes(4, 4, 0) == 0
 
 
+def test_splitk_f16_validation(L):
+    s = NULL
+    f16 = L.gemm_f16_nt_splitk_f16
+    need = L.gemm_f16_nt_splitk_workspace_bytes(4, 4, 2)
+    assert f16(FAKE, FAKE, FAKE, 4, 4, 4, 0, FAKE, need, s) == gf.GF_ERR_INVALID_ARG     # split_k < 1
+    assert f16(FAKE, FAKE, FAKE, -1, 4, 4, 2, FAKE, need, s) == gf.GF_ERR_INVALID_ARG
+    assert f16(FAKE, FAKE, FAKE, 4, 4, 4, 2, NULL, need, s) == gf.GF_ERR_INVALID_ARG     # no workspace
+    assert f16(FAKE, FAKE, FAKE, 4, 4, 4, 2, FAKE, need - 1, s) == gf.GF_ERR_INVALID_ARG
+    assert f16(FAKE, FAKE, FAKE, 4, 4, 4, 2, ctypes.c_void_p(0x10002), need, s) == gf.GF_ERR_INVALID_ARG
+    assert f16(FAKE, FAKE, ODD, 4, 4, 4, 2, FAKE, need, s) == gf.GF_ERR_INVALID_ARG      # C not 2-aligned
+    assert f16(FAKE, FAKE, NULL, 0, 4, 4, 2, NULL, 0, s) == gf.GF_OK                    # empty output
+
+
 def test_gemv_validation(L):
     s = NULL
     assert L.gemv_f16(FAKE, FAKE, FAKE, -1, 4, s) == gf.GF_ERR_INVALID_ARG
@@ -119,15 +132,17 @@ def test_gemv_validation(L):
 def test_config_tables(L):
     cfgs = gf.gemm_configs()
     # 3x3x2x3x2 grid + deep BK=32 + ping-pong + one wave per SIMD
-    assert len(cfgs) == 108 + 16 + 6 + 8
+    assert len(cfgs) == 108 + 16 + 6 + 9
     assert sum(1 for c, ok in cfgs if ok and c["schedule"] == 1) >= 5
-    assert sum(1 for c, ok in cfgs if ok and c["schedule"] in (2, 3)) == 8
+    assert sum(1 for c, ok in cfgs if ok and c["schedule"] in (2, 3)) == 9
     legal = [c for c, ok in cfgs if ok]
     assert len(legal) >= 90
     for c, ok in cfgs:
         lds = c["stages"] * (c["block_m"] + c["block_n"]) * c["block_k"] * 2
         if lds > 160 * 1024:
             assert not ok, c
+        if c["stages"] > 4 and c["schedule"] != 2:
+            assert not ok, c                      # only schedule 2 runs a 5-stage ring
     assert len(gf.gemv_configs()) >= 30
     d = gf.gemm_default_config(8192, 8192, 8192)
     assert (d["block_m"], d["block_n"]) == (256, 256)

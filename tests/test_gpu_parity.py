@@ -221,6 +221,59 @@ def test_splitk_twopass_bitwise_deterministic():
 
 
 # ---------------------------------------------------------------------------
+# split-K, fp16 out (slice partials summed in fp32, rounded once)
+# ---------------------------------------------------------------------------
+
+def run_splitk_f16(A, B, split_k):
+    C = gf.gemm_f16_nt_splitk_f16(dev(A), dev(B), split_k=split_k)
+    torch.cuda.synchronize()
+    return host_u16(C)
+
+
+@pytest.mark.parametrize("split_k", [4, 8, 16])
+def test_splitk_f16_1024_16384(split_k):
+    """fp16 output at the split-K workload: sampled entries against the
+    oracle's fp16 result; integer inputs bit-exact."""
+    M = N = 1024
+    K = 16384
+    A, B = operands("uniform", M, N, K)
+    _say("splitk f16 1024x1024x16384 s=%d" % split_k)
+    got = run_splitk_f16(A, B, split_k)
+    ij = sample_ij(M, N, 4000, seed=100 + split_k)
+    ref16, _ = oracle.gemm_nt_entries(A, B, ij)
+    check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "splitk f16 s=%d" % split_k)
+    Ai, Bi = operands("integer", M, N, K)
+    got_i = run_splitk_f16(Ai, Bi, split_k)
+    ref_i, _ = oracle.gemm_nt_entries(Ai, Bi, ij)
+    assert np.array_equal(got_i[ij[:, 0], ij[:, 1]], ref_i)
+
+
+@pytest.mark.parametrize("M,N,K,split_k", [
+    (256, 256, 4096, 4), (100, 70, 1000, 3), (100, 72, 1000, 7), (65, 33, 64, 16),
+    (17, 9, 1001, 5), (128, 128, 8, 1), (1, 1, 1, 1), (40, 24, 0, 4),
+])
+def test_splitk_f16_full_small(M, N, K, split_k):
+    A, B = operands("uniform", M, N, K, seed=M * N + K + 1)
+    check_f16_tolerance(run_splitk_f16(A, B, split_k), oracle.gemm_nt_f16(A, B),
+                        "splitk f16 %dx%dx%d s=%d" % (M, N, K, split_k))
+    Ai = inputs.integer_f16((M, K), 2, 0)
+    Bi = inputs.integer_f16((N, K), 2, 1)
+    assert np.array_equal(run_splitk_f16(Ai, Bi, split_k), oracle.gemm_nt_f16(Ai, Bi))
+
+
+@pytest.mark.parametrize("M,N,K,split_k", [(512, 512, 8192, 16), (100, 72, 1000, 7), (33, 17, 300, 3)])
+def test_splitk_f16_is_twopass_rounded(M, N, K, split_k):
+    """The fp16 output is the deterministic fp32 two-pass result rounded
+    once to fp16 (numpy's float32 -> float16 cast is round-to-nearest-even),
+    and it is the same from run to run."""
+    A, B = operands("uniform", M, N, K, seed=3)
+    f32 = run_splitk(A, B, split_k, "twopass")
+    got = run_splitk_f16(A, B, split_k)
+    assert np.array_equal(got, f32.astype(np.float16).view(np.uint16))
+    assert np.array_equal(got, run_splitk_f16(A, B, split_k))
+
+
+# ---------------------------------------------------------------------------
 # GEMV
 # ---------------------------------------------------------------------------
 
