@@ -177,6 +177,16 @@ def main():
         sweep[str(K)] = round(achieved, 1)
         extra["gemm_k_sweep_tflops"] = sweep
 
+        # other operand layouts at 8192^3: B stored K x N (and A K x M)
+        lay = {}
+        Bt = B.t().contiguous()
+        lay["nn"] = round(flops / time_batch(torch, lambda: gf.gemm_f16(A, Bt, C, False, True), 10, 3) / 1e12, 1)
+        At = A.t().contiguous()
+        lay["tn"] = round(flops / time_batch(torch, lambda: gf.gemm_f16(At, Bt, C, True, True), 10, 3) / 1e12, 1)
+        del At, Bt
+        log("gemm 8192^3 other layouts TFLOP/s: %s" % lay)
+        extra["gemm_layouts_8192_tflops"] = lay
+
         # ---- GEMV ----
         gemv = {}
         for nk in (8192, 1024):

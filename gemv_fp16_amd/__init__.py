@@ -19,7 +19,7 @@ GF_SPLITK_ATOMIC, GF_SPLITK_TWOPASS = 0, 1
 EXPORTS = (
     "gemm_f16_nt", "gemm_f16_nt_splitk", "gemv_f16",
     "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex", "gemm_f16_nt_splitk_f16",
-    "gemm_f16_nt_cfg", "gemv_f16_cfg",
+    "gemm_f16_nt_cfg", "gemv_f16_cfg", "gemm_f16", "gemm_f16_nn", "gemm_f16_tn", "gemm_f16_cfg",
     "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
     "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
 )
@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_nt_splitk_workspace_bytes.restype = sz
     L.gemm_f16_nt_splitk_ex.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
     L.gemm_f16_nt_splitk_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, sz, vp]
+    L.gemm_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    L.gemm_f16_nn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+    L.gemm_f16_tn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+    L.gemm_f16_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ctypes.POINTER(GemmCfg), vp]
     L.gemm_f16_nt_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.POINTER(GemmCfg), vp]
     L.gemv_f16_cfg.argtypes = [vp, vp, vp, ci, ci, ctypes.POINTER(GemvCfg), vp]
     L.gf_gemm_config_get.argtypes = [ci, ctypes.POINTER(GemmCfg)]
@@ -162,6 +166,41 @@ def gemm_f16_nt(A, B, C=None, stream=None, cfg: dict | None = None):
         c = GemmCfg(**cfg)
         _check(lib().gemm_f16_nt_cfg(*args, ctypes.byref(c), _stream(stream)), "gemm_f16_nt_cfg")
     return C
+
+
+def gemm_f16(A, B, C=None, a_kmajor: bool = False, b_kmajor: bool = False, stream=None,
+             cfg: dict | None = None):
+    """C = op(A) . op(B) with fp32 accumulation, fp16 out.  A is (M, K), or
+    (K, M) when a_kmajor; B is (N, K), or (K, N) when b_kmajor.  Returns C."""
+    import torch
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    K, M = (A.shape[0], A.shape[1]) if a_kmajor else (A.shape[1], A.shape[0])
+    Kb, N = (B.shape[0], B.shape[1]) if b_kmajor else (B.shape[1], B.shape[0])
+    if K != Kb:
+        raise ValueError("A and B disagree on K (%d vs %d)" % (K, Kb))
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be (M, N)")
+    args = (_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"), _dev(C, torch.float16, "C"),
+            M, N, K, int(bool(a_kmajor)), int(bool(b_kmajor)))
+    if cfg is None:
+        _check(lib().gemm_f16(*args, _stream(stream)), "gemm_f16")
+    else:
+        c = GemmCfg(**cfg)
+        _check(lib().gemm_f16_cfg(*args, ctypes.byref(c), _stream(stream)), "gemm_f16_cfg")
+    return C
+
+
+def gemm_f16_nn(A, B, C=None, stream=None):
+    """C = A . B with A (M, K) and B (K, N), both row-major."""
+    return gemm_f16(A, B, C, False, True, stream)
+
+
+def gemm_f16_tn(A, B, C=None, stream=None):
+    """C = A^T . B with A (K, M) and B (K, N), both row-major."""
+    return gemm_f16(A, B, C, True, True, stream)
 
 
 def gemm_f16_nt_splitk_workspace_bytes(M: int, N: int, split_k: int) -> int:

@@ -10,6 +10,7 @@
 namespace gf {
 
 GemmLaunchFn g_gemm_table[kNumGemm][6] = {};
+GemmLaunchFn g_gemm_layout_table[kNumGemm][4][2] = {};
 
 namespace {
 
@@ -52,14 +53,15 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched
 
 // The tile config for a shape: the largest tile that still gives every CU
 // at least one workgroup.  For the large case the offline sweep at
-// M = N = K = 8192 ranks 256 x 256 x 64 / 2 stages first, with 256 and 512
-// threads within run-to-run noise of each other and plain tile order ahead
-// of the grouped order.
+// M = N = K = 8192 ranks 256 x 256 x 64 / 2 stages first; in side-by-side
+// runs on one GPU the one-wave-per-SIMD schedule (4 waves) matched or beat
+// the 8-wave interleaved schedule by up to 4 %, and plain tile order beat
+// the grouped order.
 gf_gemm_cfg default_gemm_cfg(int M, int N, int /*K*/)
 {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 512, 0);
+    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 256, 0, 2);
     if (t128 >= 128) return make_cfg(128, 128, 64, 2, 256, 0);
     return make_cfg(64, 64, 64, 2, 256, 0);
 }
@@ -335,6 +337,54 @@ int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void
 {
     const gf_gemm_cfg cfg = default_gemm_cfg(M, N, K);
     return gemm_f16_nt_cfg(A, B, C, M, N, K, &cfg, stream);
+}
+
+int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int a_kmajor,
+                 int b_kmajor, const gf_gemm_cfg* cfg, void* stream)
+{
+    if (!cfg || (a_kmajor != 0 && a_kmajor != 1) || (b_kmajor != 0 && b_kmajor != 1))
+        return GF_ERR_INVALID_ARG;
+    if (a_kmajor == 0 && b_kmajor == 0) return gemm_f16_nt_cfg(A, B, C, M, N, K, cfg, stream);
+    int rc = validate_gemm(A, B, C, M, N, K, 2);
+    if (rc) return rc;
+    const int idx = find_gemm(*cfg);
+    if (idx < 0 || !has_layouts(kGemmConfigs[idx])) return GF_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GF_OK;
+    // Fast path: 16-byte aligned operands whose contiguous extent (K for a
+    // K-contiguous operand, M or N for a K-major one) is a multiple of 8.
+    const bool al = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) &&
+                    (a_kmajor ? M % 8 == 0 : K % 8 == 0) && (b_kmajor ? N % 8 == 0 : K % 8 == 0);
+    GemmLaunchFn fn = g_gemm_layout_table[idx][a_kmajor * 2 + b_kmajor][al ? 1 : 0];
+    if (!fn) return GF_ERR_UNSUPPORTED;
+    GemmArgs a;
+    a.A = static_cast<const uint16_t*>(A);
+    a.B = static_cast<const uint16_t*>(B);
+    a.C = C;
+    a.M = M; a.N = N; a.K = K;
+    a.kt_per_slice = ceil_div(K, cfg->block_k);
+    a.raster = panel_of(cfg->raster);
+    return launch_status(fn(a, 1, static_cast<hipStream_t>(stream)));
+}
+
+int gemm_f16(const void* A, const void* B, void* C, int M, int N, int K, int a_kmajor, int b_kmajor,
+             void* stream)
+{
+    gf_gemm_cfg cfg = default_gemm_cfg(M, N, K);
+    if (a_kmajor || b_kmajor) {
+        const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+        cfg = t256 >= 256 ? make_cfg(256, 256, 64, 2, 256, 0, 2) : make_cfg(128, 128, 64, 2, 256, 0, 2);
+    }
+    return gemm_f16_cfg(A, B, C, M, N, K, a_kmajor, b_kmajor, &cfg, stream);
+}
+
+int gemm_f16_nn(const void* A, const void* B, void* C, int M, int N, int K, void* stream)
+{
+    return gemm_f16(A, B, C, M, N, K, 0, 1, stream);
+}
+
+int gemm_f16_tn(const void* A, const void* B, void* C, int M, int N, int K, void* stream)
+{
+    return gemm_f16(A, B, C, M, N, K, 1, 1, stream);
 }
 
 int gemm_f16_nt_splitk(const void* A, const void* B, float* C32, int M, int N, int K, int split_k,

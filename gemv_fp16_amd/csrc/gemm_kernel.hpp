@@ -53,9 +53,12 @@ static __device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0
 // the tile barrier placed before the last MFMA step of each K tile, so that
 // the next tile's first fragments and the loads into the freed stage are
 // issued under that step's MFMAs.  SCHED 3: SCHED 2 with 16x16x32 MFMAs.
-template <int BM_, int BN_, int BK_, int STAGES_, int NT_, int SCHED_ = 0>
+// LA_ / LB_: operand layouts (0: A is M x K / B is N x K, K contiguous;
+// 1: A is K x M / B is K x N, K the slow index).
+template <int BM_, int BN_, int BK_, int STAGES_, int NT_, int SCHED_ = 0, int LA_ = 0, int LB_ = 0>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, NT = NT_, SCHED = SCHED_;
+    static constexpr int LA = LA_, LB = LB_;
     static constexpr int NWAVES = NT / kWave;
     // Square-ish wave grid; the longer tile side gets more waves.
     static constexpr int WM = (NWAVES == 4) ? 2 : (NWAVES == 8 ? (BM > BN ? 4 : 2) : 1);
@@ -76,7 +79,8 @@ struct GemmCfg {
     static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
 
     // A config is legal when it maps onto wave64 MFMA tiles, splits evenly
-    // over the loader, and fits one CU's 160 KiB of LDS.
+    // over the loader, and fits one CU's 160 KiB of LDS.  A K-major operand
+    // needs at least 16 chunks per k-row for its swizzle.
     static constexpr bool kValid =
         (NWAVES == 4 || NWAVES == 8) && WTM % MT == 0 && WTN % MT == 0 && WTM >= 16 &&
         WTN >= 16 && BK % KS == 0 && (CH == 4 || CH == 8) && ((BM + BN) * CH) % NT == 0 &&
@@ -86,12 +90,51 @@ struct GemmCfg {
         (SCHED == 0 ||
          (SCHED == 1 && NWAVES == 8 && WM == 2 && STAGES >= 2 && LPS * (STAGES - 1) < 64) ||
          ((SCHED == 2 || SCHED == 3) && NWAVES == 4 && STAGES >= 2 && (BK / KS) % 2 == 0 &&
-          LPS % 2 == 0 && LPS * STAGES < 64));
+          LPS % 2 == 0 && LPS * STAGES < 64)) &&
+        (LA == 0 || BM % 128 == 0) && (LB == 0 || BN % 128 == 0);
+};
+
+// ---------------------------------------------------------------------------
+// Operand layouts
+// ---------------------------------------------------------------------------
+//
+// Layout 0 (A: M x K, B: N x K; K contiguous): the LDS tile is [rows][BK];
+// chunk c of row r (16 bytes = 8 fp16 along K) sits at slot c ^ swz(r) of
+// its row.
+// Layout 1 (A: K x M, B: K x N; M or N contiguous): the LDS tile is
+// [BK][rows]; chunk c of k-row k (8 fp16 along M or N) sits at slot
+// c ^ (4 * (k % 4)) of that k-row.  A fragment (8 consecutive k for one
+// row) is gathered by two transposing reads, each of which hands every lane
+// 4 values from 4 consecutive k-rows (see FragReader).
+
+template <class Cfg, bool IS_A>
+struct OperandGeom {
+    static constexpr int L = IS_A ? Cfg::LA : Cfg::LB;
+    static constexpr int ROWS = IS_A ? Cfg::BM : Cfg::BN;      // tile extent along M or N
+    static constexpr int CR = ROWS / 8;                        // layout 1: chunks per k-row
 };
 
 __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
 {
     return (row / rows_per_key) % ch;
+}
+
+// Where the 16-byte LDS slot s of an operand tile (0 <= s < rows * BK / 8)
+// comes from: tile row (M/N index) and K offset of its 8 elements for
+// layout 0, or k-row and M/N offset for layout 1.
+template <class Cfg, int L, int ROWS>
+__device__ __forceinline__ void slot_source(int s, int& k_in_tile, int& row_in_tile)
+{
+    if constexpr (L == 0) {
+        const int row = s / Cfg::CH;
+        row_in_tile = row;
+        k_in_tile = ((s % Cfg::CH) ^ swz_key(row, Cfg::ROWS_PER_SWZ, Cfg::CH)) * 8;
+    } else {
+        constexpr int CR = ROWS / 8;
+        const int k = s / CR;
+        k_in_tile = k;
+        row_in_tile = ((s % CR) ^ (4 * (k % 4))) * 8;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -101,36 +144,48 @@ __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
 // Direct-to-LDS loader of one thread.  Load r (0 <= r < LPS) of a K tile
 // fills LDS slot r * NT + tid; a wave instruction fills 64 consecutive slots,
 // so the LDS address is wave-uniform and the swizzle is applied on the global
-// side.  Because NT / CH rows and the A/B boundary are multiples of the
-// 16-row swizzle period, the K chunk c a thread fetches is the same for all
-// r; only the row changes.  The row offsets are computed once per tile
-// position.
+// side.  The A/B boundary is a multiple of 64 slots, so each wave
+// instruction stays within one operand.  Each load's byte offset at k = 0 is
+// computed once per tile position; the K tile's offset (k0 times the byte
+// stride of one k step: 2 for layout 0, 2 * M or 2 * N for layout 1) is added
+// per issue.
 #ifndef GF_DMA_BUFFER
 #define GF_DMA_BUFFER 1
 #endif
 
 template <class Cfg>
 struct DmaLoader {
-    uint32_t voff[Cfg::LPS];   // byte offset of load r's chunk at k = 0 (row clamped)
-    int c8;                    // this thread's K offset inside a tile: c * 8
+    uint32_t voff[Cfg::LPS];   // byte offset of load r's chunk at k = 0 (rows / columns clamped)
+    int tid;
+    uint32_t ska, skb;         // bytes per k step in A and in B
 #if GF_DMA_BUFFER
     // Buffer descriptors of A and B (raw, byte-addressed): the tile's K
     // offset travels in the scalar offset, the row/chunk offset in voff.
     __amdgpu_buffer_rsrc_t ra, rb;
 #endif
 
-    __device__ __forceinline__ void init(const GemmArgs& a, int m0, int n0, int tid)
+    __device__ __forceinline__ void init(const GemmArgs& a, int m0, int n0, int tid_)
     {
-        const int row0 = tid / Cfg::CH;
-        c8 = ((tid % Cfg::CH) ^ swz_key(row0, Cfg::ROWS_PER_SWZ, Cfg::CH)) * 8;
+        tid = tid_;
+        ska = Cfg::LA ? (uint32_t)a.M * 2u : 2u;
+        skb = Cfg::LB ? (uint32_t)a.N * 2u : 2u;
 #pragma unroll
         for (int r = 0; r < Cfg::LPS; ++r) {
             const int slot = r * Cfg::NT + tid;
             const bool is_a = slot < Cfg::BM * Cfg::CH;
             const int s = is_a ? slot : slot - Cfg::BM * Cfg::CH;
-            const int row = s / Cfg::CH;
-            const int grow = is_a ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
-            voff[r] = (uint32_t)(grow * a.K + c8) * 2u;
+            int kk, rr;
+            uint32_t off;
+            if (is_a) {
+                slot_source<Cfg, Cfg::LA, Cfg::BM>(s, kk, rr);
+                off = Cfg::LA == 0 ? (uint32_t)(min(m0 + rr, a.M - 1) * a.K + kk)
+                                   : (uint32_t)(kk * a.M + min(m0 + rr, a.M - 8));
+            } else {
+                slot_source<Cfg, Cfg::LB, Cfg::BN>(s, kk, rr);
+                off = Cfg::LB == 0 ? (uint32_t)(min(n0 + rr, a.N - 1) * a.K + kk)
+                                   : (uint32_t)(kk * a.N + min(n0 + rr, a.N - 8));
+            }
+            voff[r] = off * 2u;
         }
 #if GF_DMA_BUFFER
         constexpr int kRawBufferWord3 = 0x00020000;
@@ -141,29 +196,77 @@ struct DmaLoader {
 #endif
     }
 
-    // Load r of the K tile whose first byte column is k0b = 2 * k0; every
-    // chunk must lie inside K.  Uniform base + 32-bit offset (saddr form).
-    __device__ __forceinline__ void issue(const GemmArgs& a, GF_LDS char* stage, uint32_t k0b, int r,
+    // Whether load r of the K tile at k0 lies inside K (its chunk for
+    // layout 0, its k-row for layout 1).
+    __device__ __forceinline__ bool in_k(const GemmArgs& a, int k0, int r) const
+    {
+        const int slot = r * Cfg::NT + tid;
+        const bool is_a = slot < Cfg::BM * Cfg::CH;
+        const int s = is_a ? slot : slot - Cfg::BM * Cfg::CH;
+        int kk, rr;
+        if (is_a) slot_source<Cfg, Cfg::LA, Cfg::BM>(s, kk, rr);
+        else slot_source<Cfg, Cfg::LB, Cfg::BN>(s, kk, rr);
+        return k0 + kk < a.K;
+    }
+
+    // Kernels with a K-major operand read it with transposing LDS reads,
+    // which the compiler cannot tell apart from the LDS bytes that a
+    // pending direct-to-LDS load may still write: it would drain every load
+    // in flight before each of them.  There the loads are issued as inline
+    // assembly, invisible to that analysis; visibility is ordered by the
+    // kernel's own vmcnt waits and barriers, as for every load here.  (M0
+    // holds the wave's LDS destination; one wait state before its use.)
+    static constexpr bool kAsmDma = Cfg::LA != 0 || Cfg::LB != 0;
+
+    // Load r of the K tile whose first K index is k0; every chunk must lie
+    // inside K.  Uniform base + 32-bit offset.
+    __device__ __forceinline__ void issue(const GemmArgs& a, GF_LDS char* stage, int k0, int r,
                                           int wave) const
     {
         const int wslot = r * Cfg::NT + wave * kWave;    // wave-uniform
         const bool is_a = wslot < Cfg::BM * Cfg::CH;     // wave-uniform
+        const uint32_t koff = (uint32_t)k0 * (is_a ? ska : skb);
 #if GF_DMA_BUFFER
         (void)a;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (GF_LDS void*)(stage + wslot * 16), 16,
-                                                 voff[r], k0b, 0, 0);
+        if constexpr (kAsmDma) {
+            const uint32_t lds = (uint32_t)(uintptr_t)(stage + wslot * 16);
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                         :: "s"(lds), "v"(voff[r]), "s"(is_a ? ra : rb), "s"(koff) : "m0");
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (GF_LDS void*)(stage + wslot * 16),
+                                                     16, voff[r], koff, 0, 0);
+        }
 #else
         const char* base = (const char*)(is_a ? a.A : a.B);
-        __builtin_amdgcn_global_load_lds(base + (voff[r] + k0b), (GF_LDS void*)(stage + wslot * 16),
+        __builtin_amdgcn_global_load_lds(base + (voff[r] + koff), (GF_LDS void*)(stage + wslot * 16),
                                          16, 0, 0);
 #endif
+    }
+
+    // The same where the tile may run past K: chunks at k >= K read 16 zero bytes.
+    __device__ __forceinline__ void issue_masked(const GemmArgs& a, GF_LDS char* stage, int k0, int r,
+                                                 int wave) const
+    {
+        const int wslot = r * Cfg::NT + wave * kWave;
+        const bool is_a = wslot < Cfg::BM * Cfg::CH;
+        const char* base = (const char*)(is_a ? a.A : a.B);
+        const void* src = in_k(a, k0, r)
+                              ? (const void*)(base + voff[r] + (size_t)k0 * (is_a ? ska : skb))
+                              : (const void*)g_zero16;
+        if constexpr (kAsmDma) {
+            const uint32_t lds = (uint32_t)(uintptr_t)(stage + wslot * 16);
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                         :: "s"(lds), "v"(src) : "m0");
+        } else {
+            __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)(stage + wslot * 16), 16, 0, 0);
+        }
     }
 
     __device__ __forceinline__ void issue_all(const GemmArgs& a, GF_LDS char* stage, int k0,
                                               int wave) const
     {
 #pragma unroll
-        for (int r = 0; r < Cfg::LPS; ++r) issue(a, stage, (uint32_t)k0 * 2u, r, wave);
+        for (int r = 0; r < Cfg::LPS; ++r) issue(a, stage, k0, r, wave);
     }
 
     // Loads R0 .. R1-1 of the K tile at k0; where the tile runs past K,
@@ -174,44 +277,24 @@ struct DmaLoader {
                                                 int wave) const
     {
         if (k0 + Cfg::BK <= a.K) {
-            static_for<R1 - R0>([&](auto j) {
-                issue(a, stage, (uint32_t)k0 * 2u, R0 + decltype(j)::value, wave);
-            });
+            static_for<R1 - R0>([&](auto j) { issue(a, stage, k0, R0 + decltype(j)::value, wave); });
         } else {
-            const bool valid = k0 + c8 < a.K;
-            static_for<R1 - R0>([&](auto j) {
-                constexpr int r = R0 + decltype(j)::value;
-                const int wslot = r * Cfg::NT + wave * kWave;
-                const bool is_a = wslot < Cfg::BM * Cfg::CH;
-                const char* base = (const char*)(is_a ? a.A : a.B);
-                const void* src = valid ? (const void*)(base + voff[r] + (size_t)k0 * 2)
-                                        : (const void*)g_zero16;
-                __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)(stage + wslot * 16), 16, 0,
-                                                 0);
-            });
+            static_for<R1 - R0>([&](auto j) { issue_masked(a, stage, k0, R0 + decltype(j)::value, wave); });
         }
     }
 
-    // The same tile where it runs past K: chunks at k >= K read 16 zero bytes.
     __device__ __forceinline__ void issue_all_masked(const GemmArgs& a, GF_LDS char* stage, int k0,
                                                      int wave) const
     {
-        const bool valid = k0 + c8 < a.K;
 #pragma unroll
-        for (int r = 0; r < Cfg::LPS; ++r) {
-            const int wslot = r * Cfg::NT + wave * kWave;
-            const bool is_a = wslot < Cfg::BM * Cfg::CH;
-            const char* base = (const char*)(is_a ? a.A : a.B);
-            const void* src = valid ? (const void*)(base + voff[r] + (size_t)k0 * 2)
-                                    : (const void*)g_zero16;
-            __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)(stage + wslot * 16), 16, 0, 0);
-        }
+        for (int r = 0; r < Cfg::LPS; ++r) issue_masked(a, stage, k0, r, wave);
     }
 };
 
 // Masked staging through registers for operands that are not 16-byte
-// aligned or whose K is not a multiple of 8: element loads with bounds
-// checks, zero fill, then one 16-byte LDS write per chunk.
+// aligned or whose K (layout 0) or M/N (layout 1) is not a multiple of 8:
+// element loads with bounds checks, zero fill, then one 16-byte LDS write
+// per chunk.
 template <class Cfg>
 __device__ __forceinline__ void load_tile_masked(const GemmArgs& a, GF_LDS char* stage, int m0,
                                                  int n0, int k0, int tid)
@@ -221,16 +304,28 @@ __device__ __forceinline__ void load_tile_masked(const GemmArgs& a, GF_LDS char*
         const int slot = r * Cfg::NT + tid;
         const bool is_a = slot < Cfg::BM * Cfg::CH;
         const int s = is_a ? slot : slot - Cfg::BM * Cfg::CH;
-        const int row = s / Cfg::CH;
-        const int c = (s % Cfg::CH) ^ swz_key(row, Cfg::ROWS_PER_SWZ, Cfg::CH);
-        const int grow = is_a ? m0 + row : n0 + row;
+        const int L = is_a ? Cfg::LA : Cfg::LB;
+        int kk, rr;
+        if (is_a) slot_source<Cfg, Cfg::LA, Cfg::BM>(s, kk, rr);
+        else slot_source<Cfg, Cfg::LB, Cfg::BN>(s, kk, rr);
         const int rows = is_a ? a.M : a.N;
+        const int row0 = (is_a ? m0 : n0) + rr;   // layout 0: the row; layout 1: first of 8 rows
         const uint16_t* base = is_a ? a.A : a.B;
         uint16_t v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int kk = k0 + c * 8 + e;
-            v[e] = (grow < rows && kk < a.K) ? base[(size_t)grow * a.K + kk] : (uint16_t)0;
+            bool ok;
+            size_t idx;
+            if (L == 0) {
+                const int kx = k0 + kk + e;
+                ok = row0 < rows && kx < a.K;
+                idx = (size_t)row0 * a.K + kx;
+            } else {
+                const int kx = k0 + kk;
+                ok = kx < a.K && row0 + e < rows;
+                idx = (size_t)kx * rows + row0 + e;
+            }
+            v[e] = ok ? base[idx] : (uint16_t)0;
         }
         u32x4 w;
         w.x = v[0] | ((uint32_t)v[1] << 16);
@@ -275,17 +370,84 @@ struct Mfma<16> {
     static __device__ __forceinline__ int row(int i, int lane) { return 4 * (lane / 16) + i; }
 };
 
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// Fragment reads of one operand.  An MFMA operand gives lane l the 8
+// consecutive k values kb .. kb + 7 (kb = 8 * (l / MT) within the step) of
+// tile row l % MT.
+//  * Layout 0: those 8 values are one swizzled 16-byte chunk: one
+//    ds_read_b128.
+//  * Layout 1: they lie in 8 k-rows.  ds_read_b64_tr_b16 treats each group
+//    of 16 lanes as a 16 x 4 block (lane r names 4 consecutive fp16 at its
+//    address) and hands lane j the values at (4 i + j / 4, j % 4), i = 0..3.
+//    Lane r therefore addresses k-row kb + 4 h + r / 4 at row offset
+//    16 * ((l % MT) / 16) + 4 * (r % 4), for h = 0 and 1: lane j receives 4
+//    consecutive k of row 16 * ((l % MT) / 16) + j.  The four k-rows that a
+//    16-lane group reads together have distinct k % 4, so the chunk swizzle
+//    spreads the 32 lanes of one LDS cycle over all 64 banks.
+template <class Cfg, bool IS_A>
+struct FragReader {
+    typedef OperandGeom<Cfg, IS_A> G;
+    static constexpr int MT = Cfg::MT, L = G::L, ROWS = G::ROWS;
+    static constexpr int WT = IS_A ? Cfg::WTM : Cfg::WTN;
+    static constexpr int NDS = L == 0 ? 1 : 2;   // LDS instructions per fragment
+    int o;       // lane part of the byte offset within the operand tile
+    int q;       // layout 0: lane's K chunk group; layout 1: lane's 16-byte column chunk
+    int key;     // swizzle key of the lane's reads
+
+    __device__ __forceinline__ void init(int w, int lane)
+    {
+        if constexpr (L == 0) {
+            const int lrow = lane % MT;
+            q = lane / MT;
+            key = swz_key(lrow, Cfg::ROWS_PER_SWZ, Cfg::CH);
+            o = (w * WT + lrow) * (Cfg::BK * 2);
+        } else {
+            const int r16 = lane % 16;
+            o = (8 * (lane / MT) + r16 / 4) * (ROWS * 2) + (r16 & 1) * 8;
+            q = (w * WT + 16 * ((lane % MT) / 16)) / 8 + (r16 % 4) / 2;
+            key = 4 * (r16 / 4);
+        }
+    }
+
+    // Fragment F (tile rows F * MT ..) of MFMA step KSTEP from operand tile T.
+    template <int F, int KSTEP>
+    __device__ __forceinline__ half8 read(const GF_LDS char* T) const
+    {
+        if constexpr (L == 0) {
+            return *(const GF_LDS half8*)(T + o + F * MT * (Cfg::BK * 2) +
+                                          (((KSTEP * (Cfg::KS / 8) + q) ^ key) * 16));
+        } else {
+            const GF_LDS char* p = T + o + (((q + F * MT / 8) ^ key) << 4);
+            constexpr int k0b = KSTEP * Cfg::KS * (ROWS * 2);
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (GF_LDS short4v*)(p + k0b));
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (GF_LDS short4v*)(p + k0b + 4 * ROWS * 2));
+            return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+};
+
 template <class Cfg>
-__device__ __forceinline__ void load_frags(const GF_LDS char* As, const GF_LDS char* Bs, int off,
-                                           half8 (&af)[Cfg::FM], half8 (&bf)[Cfg::FN])
-{
-#pragma unroll
-    for (int fm = 0; fm < Cfg::FM; ++fm)
-        af[fm] = *(const GF_LDS half8*)(As + fm * Cfg::MT * (Cfg::BK * 2) + off);
-#pragma unroll
-    for (int fn = 0; fn < Cfg::FN; ++fn)
-        bf[fn] = *(const GF_LDS half8*)(Bs + fn * Cfg::MT * (Cfg::BK * 2) + off);
-}
+struct Frags {
+    FragReader<Cfg, true> ra;
+    FragReader<Cfg, false> rb;
+    __device__ __forceinline__ void init(int wm, int wn, int lane)
+    {
+        ra.init(wm, lane);
+        rb.init(wn, lane);
+    }
+    template <int KSTEP>
+    __device__ __forceinline__ void load_all(const GF_LDS char* stage, half8 (&af)[Cfg::FM],
+                                             half8 (&bf)[Cfg::FN]) const
+    {
+        static_for<Cfg::FM>([&](auto f) { af[f] = ra.template read<decltype(f)::value, KSTEP>(stage); });
+        static_for<Cfg::FN>([&](auto f) {
+            bf[f] = rb.template read<decltype(f)::value, KSTEP>(stage + Cfg::A_BYTES);
+        });
+    }
+};
 
 // sched_group_barrier instruction classes
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
@@ -299,10 +461,10 @@ constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 //    backs up the address path and stalls the issuing wave, and with it the
 //    wave's matrix core.
 template <class Cfg, bool LOAD>
-__device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, int wn, int lane,
+__device__ __forceinline__ void compute_tile(const GF_LDS char* stage, const Frags<Cfg>& fr,
                                              typename Mfma<Cfg::MT>::acc_t (&acc)[Cfg::FM][Cfg::FN],
                                              const GemmArgs& a, const DmaLoader<Cfg>& ld,
-                                             GF_LDS char* lstage, uint32_t k0b, int wave)
+                                             GF_LDS char* lstage, int lk0, int wave)
 {
     constexpr int MT = Cfg::MT;
     constexpr int KSTEPS = Cfg::BK / Cfg::KS;
@@ -311,17 +473,23 @@ __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, i
     constexpr int LSTEPS = KSTEPS >= 2 ? KSTEPS / 2 : 1;   // steps that carry tile loads
     constexpr int NV = (Cfg::LPS + LSTEPS - 1) / LSTEPS;   // tile loads per such step
     constexpr int SP = NM / NV > 0 ? NM / NV : 1;          // MFMAs between two tile loads
-    const int lrow = lane % MT;      // operand row (A) / column (B) this lane feeds
-    const int lk = lane / MT;        // which 8-element K group of the MFMA step
-    const int key = swz_key(lrow, Cfg::ROWS_PER_SWZ, Cfg::CH);
-    const GF_LDS char* As = stage + (wm * Cfg::WTM + lrow) * (Cfg::BK * 2);
-    const GF_LDS char* Bs = stage + Cfg::A_BYTES + (wn * Cfg::WTN + lrow) * (Cfg::BK * 2);
+    const GF_LDS char* Bt = stage + Cfg::A_BYTES;
     half8 af[2][Cfg::FM], bf[2][Cfg::FN];
-    load_frags<Cfg>(As, Bs, ((lk ^ key) * 16), af[0], bf[0]);
+    fr.template load_all<0>(stage, af[0], bf[0]);
     static_for<KSTEPS>([&](auto ks_c) {
         constexpr int ks = decltype(ks_c)::value;
         constexpr int cur = ks & 1;
-        const int noff = (((ks + 1) * (Cfg::KS / 8) + lk) ^ key) * 16;
+        constexpr int nks = ks + 1 < KSTEPS ? ks + 1 : ks;
+        auto read = [&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            if constexpr (i < Cfg::FM)
+                af[cur ^ 1][i] = fr.ra.template read<i, nks>(stage);
+            else
+                bf[cur ^ 1][i - Cfg::FM] = fr.rb.template read<i - Cfg::FM, nks>(Bt);
+        };
+        auto nds = [](int i) constexpr {
+            return i < Cfg::FM ? FragReader<Cfg, true>::NDS : FragReader<Cfg, false>::NDS;
+        };
         // Which tile load (if any) follows MFMA i of this step.
         auto load_at = [](int i) constexpr {
             return (LOAD && ks < LSTEPS && i % SP == 0 && i / SP < NV &&
@@ -331,32 +499,20 @@ __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, i
             constexpr int i = decltype(i_c)::value;
             constexpr int fm = i / Cfg::FN, fn = i % Cfg::FN;
             acc[fm][fn] = Mfma<MT>::run(af[cur][fm], bf[cur][fn], acc[fm][fn]);
-            if constexpr (ks + 1 < KSTEPS && i < ND) {
-                if constexpr (i < Cfg::FM)
-                    af[cur ^ 1][i] = *(const GF_LDS half8*)(As + i * MT * (Cfg::BK * 2) + noff);
-                else
-                    bf[cur ^ 1][i - Cfg::FM] =
-                        *(const GF_LDS half8*)(Bs + (i - Cfg::FM) * MT * (Cfg::BK * 2) + noff);
-            }
+            if constexpr (ks + 1 < KSTEPS && i < ND) read(i_c);
             if constexpr (load_at(i) >= 0)
-                ld.issue(a, lstage, k0b, load_at(i), wave);
+                ld.issue(a, lstage, lk0, load_at(i), wave);
         });
         // Fragment reads that found no MFMA to follow (FM * FN < FM + FN).
         static_for<ND>([&](auto i_c) {
             constexpr int i = decltype(i_c)::value;
-            if constexpr (ks + 1 < KSTEPS && i >= NM) {
-                if constexpr (i < Cfg::FM)
-                    af[cur ^ 1][i] = *(const GF_LDS half8*)(As + i * MT * (Cfg::BK * 2) + noff);
-                else
-                    bf[cur ^ 1][i - Cfg::FM] =
-                        *(const GF_LDS half8*)(Bs + (i - Cfg::FM) * MT * (Cfg::BK * 2) + noff);
-            }
+            if constexpr (ks + 1 < KSTEPS && i >= NM) read(i_c);
         });
         static_for<NM>([&](auto i_c) {
             constexpr int i = decltype(i_c)::value;
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             if constexpr (ks + 1 < KSTEPS && i < ND)
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nds(i), 0);
             if constexpr (load_at(i) >= 0)
                 __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
         });
@@ -370,25 +526,25 @@ __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, int wm, i
             static_for<NV>([&](auto j_c) {
                 constexpr int j = decltype(j_c)::value;
                 if constexpr (j >= (NM + SP - 1) / SP && ks * NV + j < Cfg::LPS)
-                    ld.issue(a, lstage, k0b, ks * NV + j, wave);
+                    ld.issue(a, lstage, lk0, ks * NV + j, wave);
             });
         });
     }
 }
 
-// One MFMA step of SCHED 2/3: the FM x FN MFMAs on fragment buffer CUR,
-// with the reads of the following step's fragments (rows As / Bs, byte
-// offset noff, possibly in another stage) into buffer CUR ^ 1 and the
-// direct-to-LDS loads R0 .. R1-1 of the tile at k0b woven into the stream.
 #ifndef GF_RPM
 #define GF_RPM 1
 #endif
-template <class Cfg, int CUR, int R0, int R1, int RPM = GF_RPM>
+// One MFMA step of SCHED 2/3: the FM x FN MFMAs on fragment buffer CUR,
+// with the reads of step RKS's fragments from stage RS (possibly the next
+// tile's) into buffer CUR ^ 1 and the direct-to-LDS loads R0 .. R1-1 of the
+// tile at lk0 woven into the stream.
+template <class Cfg, int CUR, int RKS, int R0, int R1, int RPM = GF_RPM>
 __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[Cfg::FM][Cfg::FN],
                                           half8 (&af)[2][Cfg::FM], half8 (&bf)[2][Cfg::FN],
-                                          const GF_LDS char* As, const GF_LDS char* Bs, int noff,
+                                          const Frags<Cfg>& fr, const GF_LDS char* RS,
                                           const GemmArgs& a, const DmaLoader<Cfg>& ld,
-                                          GF_LDS char* lstage, uint32_t k0b, int wave)
+                                          GF_LDS char* lstage, int lk0, int wave)
 {
     constexpr int MT = Cfg::MT;
     constexpr int NM = Cfg::FM * Cfg::FN, ND = Cfg::FM + Cfg::FN, NL = R1 - R0;
@@ -401,14 +557,26 @@ __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[C
     // run row by row (A[fm] x B[0..FN-1]), so B0 and A0 first, then the
     // rest of B, then A1 .. A[FM-1].  Each MFMA then waits only for its own
     // operands instead of for the whole batch.
+    // LDS instructions behind read j, and behind the reads that follow MFMA i.
+    auto nds = [](int j) constexpr {
+        return ((j == 0) || (j >= 2 && j <= Cfg::FN)) ? FragReader<Cfg, false>::NDS
+                                                      : FragReader<Cfg, true>::NDS;
+    };
+    auto nds_after = [=](int i) constexpr {
+        int n = 0;
+        for (int q = 0; q < RPM; ++q)
+            if (i * RPM + q < ND) n += nds(i * RPM + q);
+        return n;
+    };
+    const GF_LDS char* RBt = RS + Cfg::A_BYTES;
     auto read = [&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
-        constexpr bool is_b = (j == 0) || (j >= 2 && j <= Cfg::FN);
-        constexpr int f = (j == 0 || j == 1) ? 0 : (is_b ? j - 1 : j - Cfg::FN);
-        if constexpr (is_b)
-            bf[CUR ^ 1][f] = *(const GF_LDS half8*)(Bs + f * MT * (Cfg::BK * 2) + noff);
+        constexpr bool b = (j == 0) || (j >= 2 && j <= Cfg::FN);
+        constexpr int f = (j == 0 || j == 1) ? 0 : (b ? j - 1 : j - Cfg::FN);
+        if constexpr (b)
+            bf[CUR ^ 1][f] = fr.rb.template read<f, RKS>(RBt);
         else
-            af[CUR ^ 1][f] = *(const GF_LDS half8*)(As + f * MT * (Cfg::BK * 2) + noff);
+            af[CUR ^ 1][f] = fr.ra.template read<f, RKS>(RS);
     };
     static_for<NM>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
@@ -418,18 +586,18 @@ __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[C
             constexpr int j = i * RPM + decltype(q_c)::value;
             if constexpr (j < ND) read(std::integral_constant<int, j>{});
         });
-        if constexpr (load_at(i) >= 0) ld.issue(a, lstage, k0b, load_at(i), wave);
+        if constexpr (load_at(i) >= 0) ld.issue(a, lstage, lk0, load_at(i), wave);
     });
     static_for<ND>([&](auto j_c) {
         if constexpr (decltype(j_c)::value >= NM * RPM) read(j_c);
     });
     static_for<NL>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
-        if constexpr (j >= NLS) ld.issue(a, lstage, k0b, R0 + j, wave);
+        if constexpr (j >= NLS) ld.issue(a, lstage, lk0, R0 + j, wave);
     });
     static_for<NM>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
-        constexpr int nr = (i + 1) * RPM <= ND ? RPM : (i * RPM < ND ? ND - i * RPM : 0);
+        constexpr int nr = nds_after(i);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nr, 0);
         if constexpr (load_at(i) >= 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
@@ -444,18 +612,13 @@ __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[C
 // Memory phase, part 1: every fragment this wave needs for one K tile, read
 // from LDS into registers (FM + FN reads per MFMA step).
 template <class Cfg>
-__device__ __forceinline__ void read_tile_frags(const GF_LDS char* stage, int wm, int wn, int lane,
+__device__ __forceinline__ void read_tile_frags(const GF_LDS char* stage, const Frags<Cfg>& fr,
                                                 half8 (&af)[Cfg::BK / Cfg::KS][Cfg::FM],
                                                 half8 (&bf)[Cfg::BK / Cfg::KS][Cfg::FN])
 {
-    constexpr int MT = Cfg::MT;
-    const int lrow = lane % MT, lk = lane / MT;
-    const int key = swz_key(lrow, Cfg::ROWS_PER_SWZ, Cfg::CH);
-    const GF_LDS char* As = stage + (wm * Cfg::WTM + lrow) * (Cfg::BK * 2);
-    const GF_LDS char* Bs = stage + Cfg::A_BYTES + (wn * Cfg::WTN + lrow) * (Cfg::BK * 2);
     static_for<Cfg::BK / Cfg::KS>([&](auto ks_c) {
         constexpr int ks = decltype(ks_c)::value;
-        load_frags<Cfg>(As, Bs, (((ks * (Cfg::KS / 8) + lk) ^ key) * 16), af[ks], bf[ks]);
+        fr.template load_all<ks>(stage, af[ks], bf[ks]);
     });
 }
 
@@ -523,6 +686,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
     auto k0_of = [&](int kt) { return (kt_begin + kt) * Cfg::BK; };
     DmaLoader<Cfg> ld;
     if constexpr (ALIGNED) ld.init(a, m0, n0, tid);
+    Frags<Cfg> fr;
+    fr.init(wm, wn, lane);
     // Whole-tile load, used where nothing can overlap it (pipeline prologue,
     // single-stage configs, and the masked unaligned path).
     auto burst = [&](int s, int kt) {
@@ -576,7 +741,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         const int steady_end = max(0, nfull - D);
         int t = 0;
         for (; t < steady_end; ++t) {
-            read_tile_frags<Cfg>(stage_ptr(t % Cfg::STAGES), wm, wn, lane, af, bf);
+            read_tile_frags<Cfg>(stage_ptr(t % Cfg::STAGES), fr, af, bf);
             ld.issue_all(a, stage_ptr((t + D) % Cfg::STAGES), k0_of(t + D), wave);
             wait_vmcnt<Cfg::LPS * (D - 1)>();
             lds_barrier();
@@ -587,7 +752,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
             lds_barrier();
         }
         for (; t < nk; ++t) {
-            read_tile_frags<Cfg>(stage_ptr(t % Cfg::STAGES), wm, wn, lane, af, bf);
+            read_tile_frags<Cfg>(stage_ptr(t % Cfg::STAGES), fr, af, bf);
             if (t + D < nk) issue_tile(t + D);
             wait_vmcnt<0>();
             lds_barrier();
@@ -614,18 +779,20 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         // iteration; no wait sits under a branch.
         constexpr int S = Cfg::STAGES;
         constexpr int KST = Cfg::BK / Cfg::KS;
-        constexpr int H = Cfg::LPS / 2;            // loads issued under the last step
-        constexpr int MT = Cfg::MT;
-        const int lrow = lane % MT, lk = lane / MT;
-        const int key = swz_key(lrow, Cfg::ROWS_PER_SWZ, Cfg::CH);
-        auto a_rows = [&](int s) {
-            return (const GF_LDS char*)stage_ptr(s) + (wm * Cfg::WTM + lrow) * (Cfg::BK * 2);
+#ifndef GF_S2_HEAD
+#define GF_S2_HEAD 2
+#endif
+#ifndef GF_S2_SPREAD
+#define GF_S2_SPREAD 1
+#endif
+        // Loads of tile t + S: LPS / GF_S2_HEAD under the last step of tile
+        // t, the rest spread evenly over the first GF_S2_SPREAD steps of
+        // tile t + 1.
+        constexpr int H = Cfg::LPS / GF_S2_HEAD;
+        constexpr int NSP = GF_S2_SPREAD < KST - 1 ? GF_S2_SPREAD : KST - 1;
+        auto rest_lo = [](int ks) constexpr {
+            return ks >= NSP ? Cfg::LPS : H + (Cfg::LPS - H) * ks / NSP;
         };
-        auto b_rows = [&](int s) {
-            return (const GF_LDS char*)stage_ptr(s) + Cfg::A_BYTES +
-                   (wn * Cfg::WTN + lrow) * (Cfg::BK * 2);
-        };
-        auto frag_off = [&](int ks) { return ((ks * (Cfg::KS / 8) + lk) ^ key) * 16; };
         half8 af[2][Cfg::FM], bf[2][Cfg::FN];
         if (nk > 0) {
 #pragma unroll
@@ -635,7 +802,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         wait_vmcnt<Cfg::LPS * (S - 2)>();       // tile 0 landed
         lds_barrier();
         if (nk > 0) ld.template issue_range<0, H>(a, stage_ptr(S - 1), k0_of(S - 1), wave);
-        load_frags<Cfg>(a_rows(0), b_rows(0), frag_off(0), af[0], bf[0]);
+        fr.template load_all<0>(stage_ptr(0), af[0], bf[0]);
         // Steady state: tiles t + S - 1 and t + S lie wholly inside K, so
         // their loads go into the MFMA stream unmasked.
         const int nfull = (nk > 0 && k0_of(nk - 1) + Cfg::BK > a.K) ? nk - 1 : nk;
@@ -643,40 +810,30 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         int t = 0;
         for (; t < steady_end; ++t) {
             const int s0 = t % S, s1 = (t + 1) % S, sl = (t + S - 1) % S;
-            const GF_LDS char* As = a_rows(s0);
-            const GF_LDS char* Bs = b_rows(s0);
             static_for<KST - 1>([&](auto ks_c) {
                 constexpr int ks = decltype(ks_c)::value;
-                if constexpr (ks == 0)
-                    mfma_step<Cfg, 0, H, Cfg::LPS>(acc, af, bf, As, Bs, frag_off(1), a, ld,
-                                                   stage_ptr(sl), (uint32_t)k0_of(t + S - 1) * 2u,
-                                                   wave);
-                else
-                    mfma_step<Cfg, ks & 1, 0, 0>(acc, af, bf, As, Bs, frag_off(ks + 1), a, ld,
-                                                 nullptr, 0, wave);
+                mfma_step<Cfg, ks & 1, ks + 1, rest_lo(ks), rest_lo(ks + 1)>(
+                    acc, af, bf, fr, stage_ptr(s0), a, ld, stage_ptr(sl), k0_of(t + S - 1), wave);
             });
             wait_vmcnt<Cfg::LPS * (S - 2)>();   // tile t + 1 landed
             lds_barrier();                       // B(t)
-            mfma_step<Cfg, (KST - 1) & 1, 0, H>(acc, af, bf, a_rows(s1), b_rows(s1), frag_off(0),
-                                                a, ld, stage_ptr(s0), (uint32_t)k0_of(t + S) * 2u,
-                                                wave);
+            mfma_step<Cfg, (KST - 1) & 1, 0, 0, H>(acc, af, bf, fr, stage_ptr(s1), a, ld,
+                                                   stage_ptr(s0), k0_of(t + S), wave);
         }
         for (; t < nk; ++t) {
             const int s0 = t % S, s1 = (t + 1) % S, sl = (t + S - 1) % S;
-            const GF_LDS char* As = a_rows(s0);
-            const GF_LDS char* Bs = b_rows(s0);
             ld.template issue_range<H, Cfg::LPS>(a, stage_ptr(sl), k0_of(t + S - 1), wave);
             static_for<KST - 1>([&](auto ks_c) {
                 constexpr int ks = decltype(ks_c)::value;
-                mfma_step<Cfg, ks & 1, 0, 0>(acc, af, bf, As, Bs, frag_off(ks + 1), a, ld, nullptr,
-                                             0, wave);
+                mfma_step<Cfg, ks & 1, ks + 1, 0, 0>(acc, af, bf, fr, stage_ptr(s0), a, ld, nullptr,
+                                                     0, wave);
             });
             wait_vmcnt<Cfg::LPS * (S - 2)>();
             lds_barrier();
             ld.template issue_range<0, H>(a, stage_ptr(s0), k0_of(t + S), wave);
             // After the last tile these reads fetch stale data that no MFMA uses.
-            mfma_step<Cfg, (KST - 1) & 1, 0, 0>(acc, af, bf, a_rows(s1), b_rows(s1), frag_off(0),
-                                                a, ld, nullptr, 0, wave);
+            mfma_step<Cfg, (KST - 1) & 1, 0, 0, 0>(acc, af, bf, fr, stage_ptr(s1), a, ld, nullptr, 0,
+                                                   wave);
         }
         wait_vmcnt<0>();                         // no load may land after the epilogue starts
     } else if constexpr (Cfg::STAGES == 1) {
@@ -685,7 +842,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
             burst(0, kt);
             wait_vmcnt<0>();
             lds_barrier();
-            compute_tile<Cfg, false>(stage_ptr(0), wm, wn, lane, acc, a, ld, nullptr, 0, wave);
+            compute_tile<Cfg, false>(stage_ptr(0), fr, acc, a, ld, nullptr, 0, wave);
         }
     } else {
 #pragma unroll
@@ -706,8 +863,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
             wait_vmcnt<Cfg::LPS * (Cfg::STAGES - 2)>();    // tile kt landed
             lds_barrier();                       // tile kt visible; tile kt-1 consumed
             const int kn = kt + Cfg::STAGES - 1;
-            compute_tile<Cfg, ALIGNED>(stage_ptr(kt % Cfg::STAGES), wm, wn, lane, acc, a, ld,
-                                       stage_ptr(kn % Cfg::STAGES), (uint32_t)k0_of(kn) * 2u, wave);
+            compute_tile<Cfg, ALIGNED>(stage_ptr(kt % Cfg::STAGES), fr, acc, a, ld,
+                                       stage_ptr(kn % Cfg::STAGES), k0_of(kn), wave);
         }
         for (; kt < nk; ++kt) {
             // Tile kt has landed once at most STAGES-2 younger tiles are pending.
@@ -718,8 +875,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
             lds_barrier();
             const int kn = kt + Cfg::STAGES - 1;
             if (kn < nk) burst(kn % Cfg::STAGES, kn);
-            compute_tile<Cfg, false>(stage_ptr(kt % Cfg::STAGES), wm, wn, lane, acc, a, ld, nullptr,
-                                     0, wave);
+            compute_tile<Cfg, false>(stage_ptr(kt % Cfg::STAGES), fr, acc, a, ld, nullptr, 0,
+                                     wave);
         }
     }
 

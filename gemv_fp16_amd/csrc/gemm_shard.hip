@@ -10,6 +10,18 @@
 namespace gf {
 namespace {
 
+// fp16 GEMM of config I with operand layouts LAY = a_kmajor * 2 + b_kmajor.
+template <int I, int LAY>
+void register_layout()
+{
+    constexpr GemmDesc d = kGemmConfigs[I];
+    typedef GemmCfg<d.bm, d.bn, d.bk, d.stages, d.threads, d.sched, LAY / 2, LAY % 2> CL;
+    if constexpr (CL::kValid) {
+        g_gemm_layout_table[I][LAY][1] = &launch_gemm<CL, EPI_F16, true>;
+        g_gemm_layout_table[I][LAY][0] = &launch_gemm<CL, EPI_F16, false>;
+    }
+}
+
 template <int I>
 void register_from()
 {
@@ -26,6 +38,11 @@ void register_from()
                     g_gemm_table[I][EPI_F32_STORE * 2 + 1] = &launch_gemm<C, EPI_F32_STORE, true>;
                     g_gemm_table[I][EPI_F32_STORE * 2 + 0] = &launch_gemm<C, EPI_F32_STORE, false>;
                 }
+            }
+            if constexpr (has_layouts(d)) {
+                register_layout<I, 1>();
+                register_layout<I, 2>();
+                register_layout<I, 3>();
             }
         }
         register_from<I + 1>();

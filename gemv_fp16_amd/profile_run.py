@@ -4,7 +4,8 @@
     rocprofv3 --pmc FETCH_SIZE -- python3 -m gemv_fp16_amd.profile_run gemv
 
 Ops (inputs are the seeded uniform[-1,1] fp16 workloads):
-  gemm    C = A . B^T at M = N = K = 8192 (default tile config)
+  gemm    C = A . B^T at M = N = K = 8192 (default tile config); --layout nn / tn
+          stores B as K x N (and A as K x M) and runs gemm_f16 on them
   gemv    y = W . x at N = K = 8192, rotating 5 W copies (640 MiB)
   splitk  M = N = 1024, K = 16384, split 8: fp32 atomic, fp32 two-pass, fp16 two-pass
   copy    torch copy of a 512 MiB buffer: a plain copy kernel of known size,
@@ -28,6 +29,7 @@ def main(argv=None):
     ap.add_argument("--m", type=int, default=8192)
     ap.add_argument("--n", type=int, default=8192)
     ap.add_argument("--k", type=int, default=8192)
+    ap.add_argument("--layout", choices=["nt", "nn", "tn"], default="nt")
     ap.add_argument("--cfg", default="",
                     help="gemm tile config block_m,block_n,block_k,stages,threads,raster[,schedule] "
                          "(default: the library's choice)")
@@ -47,7 +49,15 @@ def main(argv=None):
             v = [int(t) for t in a.cfg.split(",")]
             cfg = dict(zip(("block_m", "block_n", "block_k", "stages", "threads", "raster",
                             "schedule"), v + [0] * (7 - len(v))))
-        call = gf.prepare_gemm_f16_nt(A, B, C, cfg=cfg)
+        if a.layout == "nt":
+            call = gf.prepare_gemm_f16_nt(A, B, C, cfg=cfg)
+        else:
+            a_km = a.layout == "tn"
+            As = A.t().contiguous() if a_km else A
+            Bs = B.t().contiguous()
+            del A, B
+            def call():
+                gf.gemm_f16(As, Bs, C, a_km, True, cfg=cfg)
         for _ in range(a.iters):
             call()
     elif a.op == "gemv":

@@ -79,6 +79,27 @@ int gemv_f16(const void* W, const void* x, void* y, int N, int K, void* stream);
 
 /* ---- extensions ------------------------------------------------------ */
 
+/*
+ * fp16 GEMM with other operand layouts: C = op(A) . op(B) with C M x N fp16,
+ * fp32 accumulation and one rounding to fp16 (round-to-nearest-even), as
+ * for gemm_f16_nt.
+ *   a_kmajor = 0: A is M x K (K contiguous);  1: A is K x M (M contiguous).
+ *   b_kmajor = 0: B is N x K (K contiguous);  1: B is K x N (N contiguous).
+ * (0, 0) is gemm_f16_nt.  gemm_f16_nn = (0, 1): C = A . B with B K x N, the
+ * plain row-major product.  gemm_f16_tn = (1, 1): C = A^T . B.  The fast path
+ * needs 16-byte aligned A, B, C and a multiple of 8 for each operand's
+ * contiguous extent; anything else runs a masked path with the same result.
+ * Returns GF_ERR_INVALID_ARG for a flag other than 0 or 1.
+ * Defined by the "basic GEMM to SplitK" page, basic GEMM section (the
+ * row-major product of an M x K and a K x N matrix, C[i][j] the sum over k
+ * of A[i][k] B[k][j]); the TileLang FP16 matmul page, section 2, names the
+ * B^T operand form of gemm_f16_nt.
+ */
+int gemm_f16(const void* A, const void* B, void* C, int M, int N, int K, int a_kmajor, int b_kmajor,
+             void* stream);
+int gemm_f16_nn(const void* A, const void* B, void* C, int M, int N, int K, void* stream);
+int gemm_f16_tn(const void* A, const void* B, void* C, int M, int N, int K, void* stream);
+
 /* Bytes of workspace gemm_f16_nt_splitk_ex needs in GF_SPLITK_TWOPASS mode:
  * split_k * M * N * sizeof(float) (0 for invalid arguments). */
 size_t gemm_f16_nt_splitk_workspace_bytes(int M, int N, int split_k);
@@ -148,6 +169,12 @@ typedef struct gf_gemv_cfg {
  * library holds no kernel for it.  Same semantics as gemm_f16_nt. */
 int gemm_f16_nt_cfg(const void* A, const void* B, void* C, int M, int N, int K,
                     const gf_gemm_cfg* cfg, void* stream);
+
+/* gemm_f16 with an explicit tile config.  Layouts other than (0, 0) exist
+ * for the configs with schedule 2, block_k 64 and block_m, block_n multiples
+ * of 128; GF_ERR_UNSUPPORTED otherwise. */
+int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int a_kmajor,
+                 int b_kmajor, const gf_gemm_cfg* cfg, void* stream);
 
 /* gemv_f16 with an explicit launch shape; GF_ERR_UNSUPPORTED when the
  * library holds no kernel for it.  Same semantics as gemv_f16. */

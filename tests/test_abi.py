@@ -100,6 +100,18 @@ def test_splitk_validation(L):
     assert L.gemm_f16_nt_splitk_workspace_bytes(4, 4, 0) == 0
 
 
+def test_layout_validation(L):
+    s = NULL
+    assert L.gemm_f16(FAKE, FAKE, FAKE, 4, 4, 4, 2, 0, s) == gf.GF_ERR_INVALID_ARG     # bad flag
+    assert L.gemm_f16(FAKE, FAKE, FAKE, 4, 4, 4, 0, -1, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nn(FAKE, FAKE, FAKE, -1, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_tn(FAKE, NULL, FAKE, 4, 4, 4, s) == gf.GF_ERR_INVALID_ARG
+    assert L.gemm_f16_nn(FAKE, FAKE, FAKE, 0, 4, 4, s) == gf.GF_OK                  # empty C
+    cfg = gf.GemmCfg(128, 128, 64, 2, 256, 0, 0)          # schedule 0: no layout variants
+    assert L.gemm_f16_cfg(FAKE, FAKE, FAKE, 4, 4, 4, 0, 1, ctypes.byref(cfg), s) == gf.GF_ERR_UNSUPPORTED
+    assert L.gemm_f16_cfg(FAKE, FAKE, FAKE, 4, 4, 4, 0, 1, None, s) == gf.GF_ERR_INVALID_ARG
+
+
 def test_splitk_f16_validation(L):
     s = NULL
     f16 = L.gemm_f16_nt_splitk_f16

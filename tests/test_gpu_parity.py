@@ -167,6 +167,72 @@ def test_gemm_8192_integer_sampled():
 
 
 # ---------------------------------------------------------------------------
+# other operand layouts: A (M, K) or (K, M), B (N, K) or (K, N)
+# ---------------------------------------------------------------------------
+
+LAYOUTS = [(0, 1), (1, 1), (1, 0)]      # (a_kmajor, b_kmajor): NN, TN, and A^T . B^T
+
+
+def stored(A, B, a_kmajor, b_kmajor):
+    """The operands as the layout stores them (host arrays), from the (M, K)
+    and (N, K) forms the oracle takes."""
+    return (np.ascontiguousarray(A.T) if a_kmajor else A,
+            np.ascontiguousarray(B.T) if b_kmajor else B)
+
+
+def run_layout(A, B, a_kmajor, b_kmajor, cfg=None):
+    As, Bs = stored(A, B, a_kmajor, b_kmajor)
+    C = gf.gemm_f16(dev(As), dev(Bs), a_kmajor=a_kmajor, b_kmajor=b_kmajor, cfg=cfg)
+    torch.cuda.synchronize()
+    return host_u16(C)
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [
+    (256, 256, 256), (512, 384, 640), (640, 128, 1024),      # fast path, several tiles
+    (100, 70, 1000), (130, 136, 72), (24, 40, 7),            # masked path (ragged extents)
+    (8, 8, 8), (1, 1, 1), (16, 24, 0),
+])
+def test_gemm_layouts(M, N, K, lay):
+    a_km, b_km = lay
+    A, B = operands("integer", M, N, K, seed=7)
+    assert np.array_equal(run_layout(A, B, a_km, b_km), oracle.gemm_nt_f16(A, B)), \
+        "layout %s %dx%dx%d: integer inputs not bit-exact" % (lay, M, N, K)
+    A, B = operands("uniform", M, N, K, seed=7)
+    check_f16_tolerance(run_layout(A, B, a_km, b_km), oracle.gemm_nt_f16(A, B),
+                        "layout %s %dx%dx%d" % (lay, M, N, K))
+
+
+def test_gemm_layouts_every_config():
+    """Every config that carries layout variants, each layout, two rasters."""
+    M, N, K = 384, 512, 320
+    A, B = operands("integer", M, N, K, seed=8)
+    ref = oracle.gemm_nt_f16(A, B)
+    n = 0
+    for cfg, ok in gf.gemm_configs():
+        if not ok or cfg["schedule"] != 2 or cfg["block_k"] != 64 or cfg["block_m"] % 128 or cfg["block_n"] % 128:
+            continue
+        for lay in LAYOUTS:
+            for raster in (0, 1):
+                c = dict(cfg, raster=raster)
+                _say("layout %s cfg %s" % (lay, c))
+                assert np.array_equal(run_layout(A, B, *lay, cfg=c), ref), (lay, c)
+                n += 1
+    assert n >= 24
+
+
+def test_gemm_nn_8192_sampled():
+    """The plain row-major product at 8192^3 (default config), sampled."""
+    M = N = K = 8192
+    A, B = operands("uniform", M, N, K)
+    _say("gemm nn 8192^3")
+    got = run_layout(A, B, 0, 1)
+    ij = sample_ij(M, N, 3000, seed=11)
+    ref16, _ = oracle.gemm_nt_entries(A, B, ij)
+    check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "gemm nn 8192^3 sampled")
+
+
+# ---------------------------------------------------------------------------
 # split-K, fp32 out
 # ---------------------------------------------------------------------------
 
