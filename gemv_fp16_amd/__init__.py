@@ -20,9 +20,14 @@ EXPORTS = (
     "gemm_f16_nt", "gemm_f16_nt_splitk", "gemv_f16",
     "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex", "gemm_f16_nt_splitk_f16",
     "gemm_f16_nt_cfg", "gemv_f16_cfg", "gemm_f16", "gemm_f16_nn", "gemm_f16_tn", "gemm_f16_cfg",
+    "gemm_f16_nt_skinny", "gf_skinny_config_count", "gf_skinny_config_get",
     "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
     "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
 )
+
+
+class SkinnyCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("blocks", "unroll", "waves")]
 
 
 class GemmCfg(ctypes.Structure):
@@ -60,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_nt_splitk_ex.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
     L.gemm_f16_nt_splitk_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, sz, vp]
     L.gemm_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    L.gemm_f16_nt_skinny.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.POINTER(SkinnyCfg), vp]
+    L.gf_skinny_config_get.argtypes = [ci, ctypes.POINTER(SkinnyCfg)]
     L.gemm_f16_nn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
     L.gemm_f16_tn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
     L.gemm_f16_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ctypes.POINTER(GemmCfg), vp]
@@ -191,6 +198,31 @@ def gemm_f16(A, B, C=None, a_kmajor: bool = False, b_kmajor: bool = False, strea
         c = GemmCfg(**cfg)
         _check(lib().gemm_f16_cfg(*args, ctypes.byref(c), _stream(stream)), "gemm_f16_cfg")
     return C
+
+
+def gemm_f16_nt_skinny(A, B, C=None, stream=None, cfg: dict | None = None):
+    """C = A . B^T for 1 <= M <= 16 rows of A through the skinny kernel."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be (M, N)")
+    c = ctypes.byref(SkinnyCfg(**cfg)) if cfg is not None else None
+    _check(lib().gemm_f16_nt_skinny(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
+                                    _dev(C, torch.float16, "C"), M, N, K, c, _stream(stream)),
+           "gemm_f16_nt_skinny")
+    return C
+
+
+def skinny_configs() -> list:
+    L = lib()
+    out = []
+    for i in range(L.gf_skinny_config_count()):
+        c = SkinnyCfg()
+        _check(L.gf_skinny_config_get(i, ctypes.byref(c)), "gf_skinny_config_get")
+        out.append({"blocks": c.blocks, "unroll": c.unroll, "waves": c.waves})
+    return out
 
 
 def gemm_f16_nn(A, B, C=None, stream=None):

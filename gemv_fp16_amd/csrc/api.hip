@@ -6,6 +6,7 @@
 
 #include "../../include/gemvfp16.h"
 #include "configs.hpp"
+#include "skinny_kernel.hpp"
 
 namespace gf {
 
@@ -267,6 +268,42 @@ int splitk_f16_impl(const void* A, const void* B, void* C, int M, int N, int K, 
     return launch_status(hipGetLastError());
 }
 
+int find_skinny(const gf_skinny_cfg& c)
+{
+    for (int i = 0; i < kNumSkinny; ++i)
+        if (kSkinnyConfigs[i].blocks == c.blocks && kSkinnyConfigs[i].unroll == c.unroll &&
+            kSkinnyConfigs[i].waves == c.waves)
+            return i;
+    return -1;
+}
+
+// Launch shape of the skinny GEMM, from the offline sweep at N = K = 8192:
+// for up to 4 rows one 16-row block of B per workgroup with 4-step batches,
+// above that two blocks (the A fragments serve both) with 2-step batches.
+gf_skinny_cfg default_skinny_cfg(int M, int /*N*/, int /*K*/)
+{
+    gf_skinny_cfg c;
+    c.blocks = M <= 4 ? 1 : 2;
+    c.unroll = M <= 4 ? 4 : 2;
+    c.waves = 8;
+    return c;
+}
+
+bool skinny_fits(const void* A, const void* B, int M, int K)
+{
+    return M >= 1 && M <= kSkinnyMaxM && K % 8 == 0 && aligned(A, 16) && aligned(B, 16);
+}
+
+int skinny_impl(const void* A, const void* B, void* C, int M, int N, int K, const gf_skinny_cfg& cfg,
+                hipStream_t stream)
+{
+    const int idx = find_skinny(cfg);
+    if (idx < 0) return GF_ERR_UNSUPPORTED;
+    return launch_status(g_skinny_table[idx](static_cast<const uint16_t*>(A),
+                                             static_cast<const uint16_t*>(B),
+                                             static_cast<uint16_t*>(C), M, N, K, stream));
+}
+
 int find_gemv(const gf_gemv_cfg& c)
 {
     for (int i = 0; i < kNumGemv; ++i) {
@@ -335,8 +372,37 @@ int gemm_f16_nt_cfg(const void* A, const void* B, void* C, int M, int N, int K,
 
 int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void* stream)
 {
+    // A handful of rows of A: the skinny kernel streams B once.
+    if (M > 0 && N > 0 && skinny_fits(A, B, M, K)) {
+        const int rc = validate_gemm(A, B, C, M, N, K, 2);
+        if (rc) return rc;
+        return skinny_impl(A, B, C, M, N, K, default_skinny_cfg(M, N, K),
+                           static_cast<hipStream_t>(stream));
+    }
     const gf_gemm_cfg cfg = default_gemm_cfg(M, N, K);
     return gemm_f16_nt_cfg(A, B, C, M, N, K, &cfg, stream);
+}
+
+int gemm_f16_nt_skinny(const void* A, const void* B, void* C, int M, int N, int K,
+                       const gf_skinny_cfg* cfg, void* stream)
+{
+    int rc = validate_gemm(A, B, C, M, N, K, 2);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return GF_OK;
+    if (!skinny_fits(A, B, M, K)) return GF_ERR_UNSUPPORTED;
+    const gf_skinny_cfg c = cfg ? *cfg : default_skinny_cfg(M, N, K);
+    return skinny_impl(A, B, C, M, N, K, c, static_cast<hipStream_t>(stream));
+}
+
+int gf_skinny_config_count(void) { return kNumSkinny; }
+
+int gf_skinny_config_get(int i, gf_skinny_cfg* out)
+{
+    if (!out || i < 0 || i >= kNumSkinny) return GF_ERR_INVALID_ARG;
+    out->blocks = kSkinnyConfigs[i].blocks;
+    out->unroll = kSkinnyConfigs[i].unroll;
+    out->waves = kSkinnyConfigs[i].waves;
+    return GF_OK;
 }
 
 int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int a_kmajor,

@@ -28,7 +28,21 @@ constexpr GemvDesc kGemvConfigs[] = {
 };
 constexpr int kNumGemv = sizeof(kGemvConfigs) / sizeof(kGemvConfigs[0]);
 
+// Skinny GEMM launch shapes: 16-row blocks of B per workgroup, k-steps per
+// register batch (two batches in flight per wave), waves per workgroup.
+struct SkinnyDesc {
+    int blocks, unroll, waves;
+};
+
+constexpr SkinnyDesc kSkinnyConfigs[] = {
+    {1, 1, 8},  {1, 2, 8},  {1, 4, 8},  {2, 1, 8},  {2, 2, 8},  {2, 4, 8},
+    {1, 1, 16}, {1, 2, 16}, {1, 4, 16}, {2, 1, 16}, {2, 2, 16}, {4, 1, 8},
+};
+constexpr int kNumSkinny = sizeof(kSkinnyConfigs) / sizeof(kSkinnyConfigs[0]);
+
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs&, int slices, hipStream_t);
+typedef hipError_t (*SkinnyLaunchFn)(const uint16_t*, const uint16_t*, uint16_t*, int, int, int,
+                                     hipStream_t);
 typedef hipError_t (*GemvLaunchFn)(const uint16_t*, const uint16_t*, uint16_t*, int, int, int,
                                    hipStream_t);
 
@@ -47,6 +61,8 @@ constexpr bool has_layouts(const GemmDesc& d)
 }
 // [config][aligned]
 extern GemvLaunchFn g_gemv_table[kNumGemv][2];
+// [config]; fast path only (K % 8 == 0, 16-byte aligned A and B)
+extern SkinnyLaunchFn g_skinny_table[kNumSkinny];
 
 // Instantiation shards (one object file each, compiled in parallel).
 constexpr int kGemmShards = 8;

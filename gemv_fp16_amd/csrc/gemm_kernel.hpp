@@ -214,9 +214,13 @@ struct DmaLoader {
     // pending direct-to-LDS load may still write: it would drain every load
     // in flight before each of them.  There the loads are issued as inline
     // assembly, invisible to that analysis; visibility is ordered by the
-    // kernel's own vmcnt waits and barriers, as for every load here.  (M0
-    // holds the wave's LDS destination; one wait state before its use.)
-    static constexpr bool kAsmDma = Cfg::LA != 0 || Cfg::LB != 0;
+    // kernel's own vmcnt waits and barriers, as for every load here.  The
+    // wave's LDS destination goes in through M0 (the compiler writes it);
+    // an s_nop gives the one wait state an M0 write needs before an LDS DMA.
+#ifndef GF_ASM_DMA_ALL
+#define GF_ASM_DMA_ALL 0
+#endif
+    static constexpr bool kAsmDma = GF_ASM_DMA_ALL || Cfg::LA != 0 || Cfg::LB != 0;
 
     // Load r of the K tile whose first K index is k0; every chunk must lie
     // inside K.  Uniform base + 32-bit offset.
@@ -230,8 +234,8 @@ struct DmaLoader {
         (void)a;
         if constexpr (kAsmDma) {
             const uint32_t lds = (uint32_t)(uintptr_t)(stage + wslot * 16);
-            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                         :: "s"(lds), "v"(voff[r]), "s"(is_a ? ra : rb), "s"(koff) : "m0");
+            asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                         :: "{m0}"(lds), "v"(voff[r]), "s"(is_a ? ra : rb), "s"(koff));
         } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (GF_LDS void*)(stage + wslot * 16),
                                                      16, voff[r], koff, 0, 0);
@@ -255,8 +259,7 @@ struct DmaLoader {
                               : (const void*)g_zero16;
         if constexpr (kAsmDma) {
             const uint32_t lds = (uint32_t)(uintptr_t)(stage + wslot * 16);
-            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                         :: "s"(lds), "v"(src) : "m0");
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "{m0}"(lds), "v"(src));
         } else {
             __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)(stage + wslot * 16), 16, 0, 0);
         }

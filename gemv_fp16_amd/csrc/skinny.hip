@@ -1,0 +1,25 @@
+// Skinny GEMM instantiations (every launch shape), registered at library
+// load into gf::g_skinny_table.
+#include "configs.hpp"
+#include "skinny_kernel.hpp"
+
+namespace gf {
+
+SkinnyLaunchFn g_skinny_table[kNumSkinny] = {};
+
+namespace {
+
+template <int I>
+void register_from()
+{
+    if constexpr (I < kNumSkinny) {
+        constexpr SkinnyDesc d = kSkinnyConfigs[I];
+        g_skinny_table[I] = &launch_skinny<d.blocks, d.unroll, d.waves>;
+        register_from<I + 1>();
+    }
+}
+
+const int registered = (register_from<0>(), 0);
+
+}  // namespace
+}  // namespace gf

@@ -176,6 +176,29 @@ int gemm_f16_nt_cfg(const void* A, const void* B, void* C, int M, int N, int K,
 int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int a_kmajor,
                  int b_kmajor, const gf_gemm_cfg* cfg, void* stream);
 
+/*
+ * Skinny fp16 NT GEMM: gemm_f16_nt for 1 <= M <= 16 rows of A (a decode
+ * batch against one large B): every byte of B is streamed once and the rows
+ * of A ride along in the MFMA operand.  Same result contract as
+ * gemm_f16_nt (fp32 accumulation, one fp16 rounding).  gemm_f16_nt takes
+ * this path by itself when M <= 16, K % 8 == 0 and A and B are 16-byte
+ * aligned; this entry point runs it explicitly and returns
+ * GF_ERR_UNSUPPORTED outside those conditions.  cfg: launch shape (blocks =
+ * 16-row blocks of B per workgroup, unroll = k-steps per register batch, two
+ * batches in flight per wave, waves = waves per workgroup splitting K), NULL =
+ * the library's choice.
+ * Defined by the TileLang GEMV page: GEMV as the degenerate GEMM with a
+ * single row of A, here with up to 16 rows (C = A B^T of the TileLang FP16
+ * matmul page, section 1).
+ */
+typedef struct gf_skinny_cfg {
+    int blocks, unroll, waves;
+} gf_skinny_cfg;
+int gemm_f16_nt_skinny(const void* A, const void* B, void* C, int M, int N, int K,
+                       const gf_skinny_cfg* cfg, void* stream);
+int gf_skinny_config_count(void);
+int gf_skinny_config_get(int i, gf_skinny_cfg* out);
+
 /* gemv_f16 with an explicit launch shape; GF_ERR_UNSUPPORTED when the
  * library holds no kernel for it.  Same semantics as gemv_f16. */
 int gemv_f16_cfg(const void* W, const void* x, void* y, int N, int K,

@@ -112,6 +112,21 @@ def test_layout_validation(L):
     assert L.gemm_f16_cfg(FAKE, FAKE, FAKE, 4, 4, 4, 0, 1, None, s) == gf.GF_ERR_INVALID_ARG
 
 
+def test_skinny_validation(L):
+    s = NULL
+    sk = L.gemm_f16_nt_skinny
+    assert sk(FAKE, FAKE, FAKE, 17, 64, 64, None, s) == gf.GF_ERR_UNSUPPORTED      # M > 16
+    assert sk(FAKE, FAKE, FAKE, 4, 64, 60, None, s) == gf.GF_ERR_UNSUPPORTED       # K % 8 != 0
+    assert sk(ctypes.c_void_p(0x10002), FAKE, FAKE, 4, 64, 64, None, s) == gf.GF_ERR_UNSUPPORTED
+    bad = gf.SkinnyCfg(3, 3, 8)
+    assert sk(FAKE, FAKE, FAKE, 4, 64, 64, ctypes.byref(bad), s) == gf.GF_ERR_UNSUPPORTED
+    assert sk(FAKE, FAKE, FAKE, -1, 64, 64, None, s) == gf.GF_ERR_INVALID_ARG
+    assert sk(FAKE, FAKE, NULL, 4, 0, 64, None, s) == gf.GF_OK                      # empty C
+    assert len(gf.skinny_configs()) >= 4
+    out = gf.SkinnyCfg()
+    assert L.gf_skinny_config_get(-1, ctypes.byref(out)) == gf.GF_ERR_INVALID_ARG
+
+
 def test_splitk_f16_validation(L):
     s = NULL
     f16 = L.gemm_f16_nt_splitk_f16

@@ -233,6 +233,55 @@ def test_gemm_nn_8192_sampled():
 
 
 # ---------------------------------------------------------------------------
+# skinny GEMM (1 <= M <= 16 rows of A)
+# ---------------------------------------------------------------------------
+
+def run_skinny(A, B, cfg=None):
+    C = gf.gemm_f16_nt_skinny(dev(A), dev(B), cfg=cfg)
+    torch.cuda.synchronize()
+    return host_u16(C)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 15, 16])
+@pytest.mark.parametrize("N,K", [(256, 512), (1000, 1032), (17, 8), (40, 24), (33, 0)])
+def test_skinny(M, N, K):
+    A, B = operands("integer", M, N, K, seed=5)
+    assert np.array_equal(run_skinny(A, B), oracle.gemm_nt_f16(A, B)), \
+        "skinny %dx%dx%d: integer inputs not bit-exact" % (M, N, K)
+    A, B = operands("uniform", M, N, K, seed=5)
+    check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny %dx%dx%d" % (M, N, K))
+
+
+def test_skinny_every_config():
+    M, N, K = 16, 520, 1000
+    A, B = operands("integer", M, N, K, seed=6)
+    ref = oracle.gemm_nt_f16(A, B)
+    for cfg in gf.skinny_configs():
+        _say("skinny cfg %s" % cfg)
+        assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
+
+
+def test_skinny_is_gemm_nt_for_small_m():
+    """gemm_f16_nt takes the skinny kernel for M <= 16 (same bits), and
+    agrees bit-exactly with the tiled kernel on integer inputs."""
+    A, B = operands("integer", 6, 700, 2048, seed=9)
+    got = run_gemm(A, B)
+    assert np.array_equal(got, run_skinny(A, B))
+    tiled = run_gemm(A, B, cfg=dict(block_m=64, block_n=64, block_k=64, stages=2, threads=256,
+                                    raster=0, schedule=0))
+    assert np.array_equal(got, tiled)
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_skinny_decode_8192(M):
+    """The decode-size case: M rows against an 8192 x 8192 B, all outputs."""
+    N = K = 8192
+    A, B = operands("uniform", M, N, K)
+    _say("skinny decode M=%d 8192^2" % M)
+    check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny M=%d 8192^2" % M)
+
+
+# ---------------------------------------------------------------------------
 # split-K, fp32 out
 # ---------------------------------------------------------------------------
 
