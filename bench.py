@@ -223,6 +223,25 @@ def main():
                             "traffic": measured_traffic("gemv_kernel", "8192^2")}
         extra["gemv"] = gemv
 
+        # ---- skinny GEMM: M = 2..16 rows against an 8192 x 8192 B (decode batches) ----
+        Bsk = [torch.from_numpy(inputs.uniform_f16((8192, 8192), i, 1)).cuda() for i in range(5)]
+        sk_res = {}
+        for mm in (2, 4, 8, 16):
+            Ask = torch.from_numpy(inputs.uniform_f16((mm, 8192), 0, 0)).cuda()
+            Csk = torch.empty((mm, 8192), dtype=torch.float16, device="cuda")
+            state = [0]
+
+            def skinny(Ask=Ask, Csk=Csk, state=state):
+                gf.gemm_f16_nt(Ask, Bsk[state[0] % len(Bsk)], Csk)
+                state[0] += 1
+
+            t = time_batch(torch, skinny, 100, 10)
+            byt = 2.0 * 8192 * 8192 + 2.0 * mm * 8192 * 2
+            sk_res["M%d" % mm] = {"us": round(t * 1e6, 2), "GB/s": round(byt / t / 1e9, 1)}
+        del Bsk
+        log("skinny M x 8192 x 8192 (B from HBM): %s" % sk_res)
+        extra["skinny_8192"] = sk_res
+
         # ---- split-K ----
         sm, sk_k = 1024, 16384
         a3 = torch.from_numpy(inputs.uniform_f16((sm, sk_k), 0, 0)).cuda()

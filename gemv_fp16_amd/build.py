@@ -56,13 +56,16 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)
-    # Diagnostic: the HBM streaming-read ceiling probe (not linked into the library).
-    probe = os.path.join(PKG, "readbw")
-    cmd = [HIPCC] + [f for f in FLAGS if f != "-fPIC"] + [os.path.join(CSRC, "readbw.hip"), "-o", probe + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed for readbw.hip:\n%s" % r.stderr)
-    os.replace(probe + ".tmp", probe)
+    # Diagnostics (not linked into the library): the HBM streaming-read and
+    # the MFMA throughput ceiling probes.
+    for name in ("readbw", "mfmapeak"):
+        probe = os.path.join(PKG, name)
+        cmd = [HIPCC] + [f for f in FLAGS if f != "-fPIC"] + [os.path.join(CSRC, name + ".hip"), "-o",
+                                                            probe + ".tmp"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s.hip:\n%s" % (name, r.stderr))
+        os.replace(probe + ".tmp", probe)
     if verbose:
         print("built", LIB)
     return LIB
