@@ -33,6 +33,10 @@ def check_f16_tolerance(got_bits, ref_bits, what=""):
     assert np.array_equal(got[~fin], ref[~fin]), what + ": non-finite mismatch"
     err = np.abs(got[fin] - ref[fin])
     bound = f16_ulp(ref_bits[fin]) + 1e-3
+    if err.size:
+        # Reported with `pytest -s`: the worst error seen, in fp16 ulps of the oracle value.
+        print("[maxerr] %s: %.3g abs, %.3g ulp, %d of %d entries differ" % (
+            what, err.max(), (err / f16_ulp(ref_bits[fin])).max(), np.count_nonzero(err), err.size))
     bad = np.flatnonzero(err > bound)
     assert bad.size == 0, "%s: %d entries out of tolerance, worst err %.3g (bound %.3g)" % (
         what, bad.size, err.max(), bound[np.argmax(err - bound)])
@@ -44,6 +48,8 @@ def check_f32_splitk_tolerance(got, ref, K, what=""):
     ref = np.asarray(ref, dtype=np.float64)
     bound = 1e-5 * np.sqrt(max(K, 1)) * max(np.abs(ref).max(), 0.0)
     err = np.abs(got - ref).max() if ref.size else 0.0
+    if ref.size:
+        print("[maxerr] %s: %.3g abs, %.3g of max|ref|" % (what, err, err / max(np.abs(ref).max(), 1e-300)))
     assert err <= bound, "%s: max err %.3g > bound %.3g" % (what, err, bound)
 
 
