@@ -14,13 +14,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemvfp16.so")
 
 GF_OK, GF_ERR_INVALID_ARG, GF_ERR_HIP, GF_ERR_UNSUPPORTED = 0, 1, 2, 3
-GF_SPLITK_ATOMIC, GF_SPLITK_TWOPASS = 0, 1
+GF_SPLITK_ATOMIC, GF_SPLITK_TWOPASS, GF_SPLITK_F16 = 0, 1, 2
 
 EXPORTS = (
     "gemm_f16_nt", "gemm_f16_nt_splitk", "gemv_f16",
     "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex", "gemm_f16_nt_splitk_f16",
     "gemm_f16_nt_cfg", "gemv_f16_cfg", "gemm_f16", "gemm_f16_nn", "gemm_f16_tn", "gemm_f16_cfg",
-    "gemm_f16_nt_skinny", "gf_skinny_config_count", "gf_skinny_config_get",
+    "gemm_f16_nt_skinny", "gf_skinny_config_count", "gf_skinny_config_get", "gemm_f16_nt_splitk_cfg",
     "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
     "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
 )
@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_nt_splitk_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, sz, vp]
     L.gemm_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
     L.gemm_f16_nt_skinny.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.POINTER(SkinnyCfg), vp]
+    L.gemm_f16_nt_splitk_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, ctypes.POINTER(GemmCfg), vp]
     L.gf_skinny_config_get.argtypes = [ci, ctypes.POINTER(SkinnyCfg)]
     L.gemm_f16_nn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
     L.gemm_f16_tn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
@@ -274,6 +275,23 @@ def gemm_f16_nt_splitk_ex(A, B, C32=None, split_k: int = 4, mode: int = GF_SPLIT
                                        _dev(C32, torch.float32, "C32"), M, N, K, split_k, mode,
                                        ws_ptr, ws_bytes, _stream(stream)), "gemm_f16_nt_splitk_ex")
     return C32
+
+
+
+
+def gemm_f16_nt_splitk_cfg(A, B, C, split_k: int, mode: int, cfg: dict, workspace, stream=None):
+    """Split-K with an explicit tile config; C is fp32 (atomic / two-pass) or
+    fp16 (GF_SPLITK_F16).  The workspace (fp32 CUDA tensor) is required."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    cdt = torch.float16 if mode == GF_SPLITK_F16 else torch.float32
+    c = GemmCfg(**cfg)
+    _check(lib().gemm_f16_nt_splitk_cfg(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
+                                        _dev(C, cdt, "C"), M, N, K, split_k, mode,
+                                        _dev(workspace, torch.float32, "workspace"),
+                                        workspace.numel() * 4, ctypes.byref(c), _stream(stream)),
+           "gemm_f16_nt_splitk_cfg")
+    return C
 
 
 def gemm_f16_nt_splitk_f16(A, B, C=None, split_k: int = 4, workspace=None, stream=None):

@@ -67,10 +67,26 @@ gf_gemm_cfg default_gemm_cfg(int M, int N, int /*K*/)
     return make_cfg(64, 64, 64, 2, 256, 0);
 }
 
-gf_gemm_cfg default_splitk_cfg(int M, int N, int K)
+// Split-K tile: the largest tile (among the configs compiled with the fp32
+// epilogues) whose tiles x slices still give every CU a workgroup.  The
+// sweep at M = N = 1024, K = 16384 found exactly that: 128 x 128 / 3 stages
+// at split 4, 128 x 256 at split 8, 256 x 256 at split 16, each with
+// 256 workgroups.
+gf_gemm_cfg default_splitk_cfg(int M, int N, int K, int split_k)
 {
-    (void)M; (void)N; (void)K;
-    return make_cfg(128, 128, 64, 2, 256, 1);
+    constexpr int kCus = 256;
+    const gf_gemm_cfg cands[] = {
+        make_cfg(256, 256, 64, 2, 512, 1), make_cfg(128, 256, 64, 2, 256, 1),
+        make_cfg(128, 128, 64, 3, 256, 1), make_cfg(64, 64, 64, 2, 256, 1),
+    };
+    for (const gf_gemm_cfg& c : cands) {
+        const int64_t tiles = (int64_t)ceil_div(M, c.block_m) * ceil_div(N, c.block_n);
+        const int nkt = ceil_div(K, c.block_k);
+        const int per = nkt > 0 ? ceil_div(nkt, max(1, split_k)) : 0;
+        const int slices = per > 0 ? ceil_div(nkt, per) : 1;
+        if (tiles * slices >= kCus) return c;
+    }
+    return cands[3];
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GF_OK : GF_ERR_HIP; }
@@ -457,14 +473,28 @@ int gemm_f16_nt_splitk(const void* A, const void* B, float* C32, int M, int N, i
                        void* stream)
 {
     return splitk_impl(A, B, C32, M, N, K, split_k, GF_SPLITK_ATOMIC, nullptr, 0,
-                       default_splitk_cfg(M, N, K), static_cast<hipStream_t>(stream));
+                       default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));
+}
+
+int gemm_f16_nt_splitk_cfg(const void* A, const void* B, void* C, int M, int N, int K, int split_k,
+                           int mode, void* workspace, size_t workspace_bytes, const gf_gemm_cfg* cfg,
+                           void* stream)
+{
+    if (!cfg) return GF_ERR_INVALID_ARG;
+    const int idx = find_gemm(*cfg);
+    if (idx >= 0 && !kGemmConfigs[idx].core) return GF_ERR_UNSUPPORTED;   // no fp32 epilogues compiled
+    if (mode == GF_SPLITK_F16)
+        return splitk_f16_impl(A, B, C, M, N, K, split_k, workspace, workspace_bytes, *cfg,
+                               static_cast<hipStream_t>(stream));
+    return splitk_impl(A, B, static_cast<float*>(C), M, N, K, split_k, mode, workspace,
+                       workspace_bytes, *cfg, static_cast<hipStream_t>(stream));
 }
 
 int gemm_f16_nt_splitk_f16(const void* A, const void* B, void* C, int M, int N, int K,
                            int split_k, void* workspace, size_t workspace_bytes, void* stream)
 {
     return splitk_f16_impl(A, B, C, M, N, K, split_k, workspace, workspace_bytes,
-                           default_splitk_cfg(M, N, K), static_cast<hipStream_t>(stream));
+                           default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));
 }
 
 size_t gemm_f16_nt_splitk_workspace_bytes(int M, int N, int split_k)
@@ -477,7 +507,7 @@ int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N
                           int mode, void* workspace, size_t workspace_bytes, void* stream)
 {
     return splitk_impl(A, B, C32, M, N, K, split_k, mode, workspace, workspace_bytes,
-                       default_splitk_cfg(M, N, K), static_cast<hipStream_t>(stream));
+                       default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));
 }
 
 int gemv_f16_cfg(const void* W, const void* x, void* y, int N, int K, const gf_gemv_cfg* cfg,

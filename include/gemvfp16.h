@@ -40,7 +40,7 @@ enum {
     GF_ERR_UNSUPPORTED = 3    /* no compiled kernel for the requested config */
 };
 
-enum { GF_SPLITK_ATOMIC = 0, GF_SPLITK_TWOPASS = 1 };
+enum { GF_SPLITK_ATOMIC = 0, GF_SPLITK_TWOPASS = 1, GF_SPLITK_F16 = 2 };
 
 /*
  * C = A . B^T.  A is M x K fp16, B is N x K fp16, C is M x N fp16.
@@ -169,6 +169,15 @@ typedef struct gf_gemv_cfg {
  * library holds no kernel for it.  Same semantics as gemm_f16_nt. */
 int gemm_f16_nt_cfg(const void* A, const void* B, void* C, int M, int N, int K,
                     const gf_gemm_cfg* cfg, void* stream);
+
+/* Split-K with an explicit tile config (used by the offline sweep): mode
+ * GF_SPLITK_ATOMIC or GF_SPLITK_TWOPASS as gemm_f16_nt_splitk_ex (C is then
+ * float*), or GF_SPLITK_F16 as gemm_f16_nt_splitk_f16 (C is fp16).  Only
+ * configs compiled with the fp32 epilogues qualify; GF_ERR_UNSUPPORTED
+ * otherwise. */
+int gemm_f16_nt_splitk_cfg(const void* A, const void* B, void* C, int M, int N, int K, int split_k,
+                           int mode, void* workspace, size_t workspace_bytes, const gf_gemm_cfg* cfg,
+                           void* stream);
 
 /* gemm_f16 with an explicit tile config.  Layouts other than (0, 0) exist
  * for the configs with schedule 2, block_k 64 and block_m, block_n multiples

@@ -328,6 +328,42 @@ def test_splitk_full_small(M, N, K, split_k, mode):
     assert np.array_equal(run_splitk(Ai, Bi, split_k, mode), oracle.gemm_nt_f32(Ai, Bi))
 
 
+def test_splitk_every_config():
+    """gemm_f16_nt_splitk_cfg on every config compiled with the fp32
+    epilogues, all three combines, integer inputs (exact), a ragged shape."""
+    M, N, K, split = 200, 136, 1000, 3
+    Ai = inputs.integer_f16((M, K), 4, 0)
+    Bi = inputs.integer_f16((N, K), 4, 1)
+    ref32 = oracle.gemm_nt_f32(Ai, Bi)
+    ref16 = oracle.gemm_nt_f16(Ai, Bi)
+    dA, dB = dev(Ai), dev(Bi)
+    ws = torch.empty(split * M * N, dtype=torch.float32, device="cuda")
+    n = 0
+    for cfg, ok in gf.gemm_configs():
+        if not ok:
+            continue
+        for raster in (0, 1):
+            c = dict(cfg, raster=raster)
+            C32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            try:
+                gf.gemm_f16_nt_splitk_cfg(dA, dB, C32, split, gf.GF_SPLITK_TWOPASS, c, ws)
+            except RuntimeError as e:
+                assert "unsupported" in str(e).lower(), e
+                continue
+            _say("splitk cfg %s" % c)
+            torch.cuda.synchronize()
+            assert np.array_equal(C32.cpu().numpy(), ref32), c
+            gf.gemm_f16_nt_splitk_cfg(dA, dB, C32, split, gf.GF_SPLITK_ATOMIC, c, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(C32.cpu().numpy(), ref32), c
+            C16 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            gf.gemm_f16_nt_splitk_cfg(dA, dB, C16, split, gf.GF_SPLITK_F16, c, ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_u16(C16), ref16), c
+            n += 1
+    assert n >= 20
+
+
 def test_splitk_twopass_bitwise_deterministic():
     A, B = operands("uniform", 512, 512, 8192, seed=2)
     r1 = run_splitk(A, B, 16, "twopass")
