@@ -27,7 +27,7 @@ EXPORTS = (
 
 
 class SkinnyCfg(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int) for n in ("blocks", "unroll", "waves")]
+    _fields_ = [(n, ctypes.c_int) for n in ("blocks", "unroll", "waves", "stages")]
 
 
 class GemmCfg(ctypes.Structure):
@@ -222,7 +222,7 @@ def skinny_configs() -> list:
     for i in range(L.gf_skinny_config_count()):
         c = SkinnyCfg()
         _check(L.gf_skinny_config_get(i, ctypes.byref(c)), "gf_skinny_config_get")
-        out.append({"blocks": c.blocks, "unroll": c.unroll, "waves": c.waves})
+        out.append({"blocks": c.blocks, "unroll": c.unroll, "waves": c.waves, "stages": c.stages})
     return out
 
 

@@ -288,20 +288,29 @@ int find_skinny(const gf_skinny_cfg& c)
 {
     for (int i = 0; i < kNumSkinny; ++i)
         if (kSkinnyConfigs[i].blocks == c.blocks && kSkinnyConfigs[i].unroll == c.unroll &&
-            kSkinnyConfigs[i].waves == c.waves)
+            kSkinnyConfigs[i].waves == c.waves && kSkinnyConfigs[i].stages == c.stages)
             return i;
     return -1;
 }
 
 // Launch shape of the skinny GEMM, from the offline sweep at N = K = 8192:
-// for up to 4 rows one 16-row block of B per workgroup with 4-step batches,
-// above that two blocks (the A fragments serve both) with 2-step batches.
-gf_skinny_cfg default_skinny_cfg(int M, int /*N*/, int /*K*/)
+// up to 4 rows the direct form (one 16-row block of B per workgroup, 4-step
+// batches) streams fastest; from 5 rows the extra A traffic of the direct
+// form dominates and the LDS-staged form (three blocks of B share each A
+// chunk, two chunks in flight) is ahead, when K is a multiple of its chunk.
+gf_skinny_cfg default_skinny_cfg(int M, int /*N*/, int K)
 {
     gf_skinny_cfg c;
-    c.blocks = M <= 4 ? 1 : 2;
-    c.unroll = M <= 4 ? 4 : 2;
     c.waves = 8;
+    if (M > 4 && K > 0 && K % kSkinnyKc == 0) {
+        c.blocks = 3;
+        c.unroll = 0;
+        c.stages = 2;
+    } else {
+        c.blocks = M <= 4 ? 1 : 2;
+        c.unroll = M <= 4 ? 4 : 2;
+        c.stages = 0;
+    }
     return c;
 }
 
@@ -314,7 +323,8 @@ int skinny_impl(const void* A, const void* B, void* C, int M, int N, int K, cons
                 hipStream_t stream)
 {
     const int idx = find_skinny(cfg);
-    if (idx < 0) return GF_ERR_UNSUPPORTED;
+    if (idx < 0 || !g_skinny_table[idx]) return GF_ERR_UNSUPPORTED;
+    if (kSkinnyConfigs[idx].stages > 0 && (K % kSkinnyKc != 0 || K == 0)) return GF_ERR_UNSUPPORTED;
     return launch_status(g_skinny_table[idx](static_cast<const uint16_t*>(A),
                                              static_cast<const uint16_t*>(B),
                                              static_cast<uint16_t*>(C), M, N, K, stream));
@@ -418,6 +428,7 @@ int gf_skinny_config_get(int i, gf_skinny_cfg* out)
     out->blocks = kSkinnyConfigs[i].blocks;
     out->unroll = kSkinnyConfigs[i].unroll;
     out->waves = kSkinnyConfigs[i].waves;
+    out->stages = kSkinnyConfigs[i].stages;
     return GF_OK;
 }
 

@@ -28,15 +28,19 @@ constexpr GemvDesc kGemvConfigs[] = {
 };
 constexpr int kNumGemv = sizeof(kGemvConfigs) / sizeof(kGemvConfigs[0]);
 
-// Skinny GEMM launch shapes: 16-row blocks of B per workgroup, k-steps per
-// register batch (two batches in flight per wave), waves per workgroup.
+// Skinny GEMM launch shapes: 16-row blocks of B per workgroup, waves per
+// workgroup, and either stages = 0 (direct form: unroll = k-steps per
+// register batch, two batches in flight per wave) or stages >= 2 (LDS-staged
+// form with that many 512-k chunks in the ring; unroll unused, 0).
 struct SkinnyDesc {
-    int blocks, unroll, waves;
+    int blocks, unroll, waves, stages;
 };
 
 constexpr SkinnyDesc kSkinnyConfigs[] = {
-    {1, 1, 8},  {1, 2, 8},  {1, 4, 8},  {2, 1, 8},  {2, 2, 8},  {2, 4, 8},
-    {1, 1, 16}, {1, 2, 16}, {1, 4, 16}, {2, 1, 16}, {2, 2, 16}, {4, 1, 8},
+    {1, 1, 8, 0},  {1, 2, 8, 0},  {1, 4, 8, 0},  {2, 1, 8, 0},  {2, 2, 8, 0},  {2, 4, 8, 0},
+    {1, 1, 16, 0}, {1, 2, 16, 0}, {1, 4, 16, 0}, {2, 1, 16, 0}, {2, 2, 16, 0}, {4, 1, 8, 0},
+    {1, 0, 8, 2},  {1, 0, 8, 3},  {1, 0, 8, 4},  {1, 0, 4, 4},  {1, 0, 16, 4}, {2, 0, 8, 2},
+    {2, 0, 8, 3},  {2, 0, 4, 3},  {3, 0, 8, 2},  {1, 0, 4, 3},
 };
 constexpr int kNumSkinny = sizeof(kSkinnyConfigs) / sizeof(kSkinnyConfigs[0]);
 
@@ -61,7 +65,8 @@ constexpr bool has_layouts(const GemmDesc& d)
 }
 // [config][aligned]
 extern GemvLaunchFn g_gemv_table[kNumGemv][2];
-// [config]; fast path only (K % 8 == 0, 16-byte aligned A and B)
+// [config]; fast path only (K % 8 == 0, or K % 512 == 0 for the LDS-staged
+// form, and 16-byte aligned A and B)
 extern SkinnyLaunchFn g_skinny_table[kNumSkinny];
 
 // Instantiation shards (one object file each, compiled in parallel).

@@ -14,7 +14,10 @@ void register_from()
 {
     if constexpr (I < kNumSkinny) {
         constexpr SkinnyDesc d = kSkinnyConfigs[I];
-        g_skinny_table[I] = &launch_skinny<d.blocks, d.unroll, d.waves>;
+        if constexpr (d.stages == 0)
+            g_skinny_table[I] = &launch_skinny<d.blocks, d.unroll, d.waves>;
+        else if constexpr (SkinnyLdsCfg<d.blocks, d.stages, d.waves>::kValid)
+            g_skinny_table[I] = &launch_skinny_lds<d.blocks, d.stages, d.waves>;
         register_from<I + 1>();
     }
 }

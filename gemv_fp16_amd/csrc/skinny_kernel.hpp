@@ -120,4 +120,134 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// LDS-staged form (K % 512 == 0): row-long loads
+// ---------------------------------------------------------------------------
+//
+// The direct form above reads 16 rows x 64 bytes per load instruction.  Here
+// every load instruction moves 1 KiB of ONE row (512 consecutive k) straight
+// into LDS, the pattern the GEMV streams at: per 512-k chunk a workgroup
+// loads its 16 * NB rows of B and the 16 rows of A (rows past M clamped to a
+// valid row: an MFMA row of A only reaches the same row of the result, and
+// those rows are not stored).  Chunk c of a row sits at 16-byte slot
+// c ^ (row % 16), so the 16 lanes that read one fragment (16 rows, same k)
+// hit 16 different bank groups.  S chunks ring through LDS; every wave
+// issues the same number of loads per chunk, so each wait is a constant.
+// The 16 k-steps of a chunk are dealt to the W waves; their partial tiles
+// are summed at the end as in the direct form.
+constexpr int kSkinnyKc = 512;                  // k per chunk (1 KiB per row)
+
+template <int NB, int S, int W>
+struct SkinnyLdsCfg {
+    static constexpr int ROWS = 16 * (NB + 1);          // B rows, then 16 A rows
+    static constexpr int CHUNK_BYTES = ROWS * kSkinnyKc * 2;
+    static constexpr int LW = ROWS / W;                 // loads per wave per chunk
+    static constexpr int LDS_BYTES = S * CHUNK_BYTES;
+    static constexpr bool kValid =
+        W <= 16 && ROWS % W == 0 && LDS_BYTES <= 160 * 1024 && S >= 2 && LW * S < 64;
+};
+
+template <int NB, int S, int W>
+__global__ __launch_bounds__(W * kWave) void skinny_lds_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int M,
+    int N, int K)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef SkinnyLdsCfg<NB, S, W> Cf;
+    extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+    GF_LDS char* smem = (GF_LDS char*)smem_raw;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n0 = blockIdx.x * NB * 16;
+    const int nchunks = K / kSkinnyKc;
+    __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)A, 0, (int)((uint32_t)M * (uint32_t)K * 2u), 0x00020000);
+    __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)B, 0, (int)((uint32_t)N * (uint32_t)K * 2u), 0x00020000);
+    // Load q of this wave covers tile row i = q * W + wave: B rows first,
+    // then A.  Byte offset of the row's chunk 0 (scalar) and of the lane's
+    // swizzled 16 bytes inside the chunk (vector).
+    auto row_of = [&](int q) { return q * W + wave; };
+    auto issue_chunk = [&](int chunk, int slot) {
+#pragma unroll
+        for (int q = 0; q < Cf::LW; ++q) {
+            const int i = row_of(q);
+            const bool is_b = i < 16 * NB;
+            const int grow = is_b ? min(n0 + i, N - 1) : min(i - 16 * NB, M - 1);
+            const uint32_t soff = ((uint32_t)grow * (uint32_t)K + (uint32_t)chunk * kSkinnyKc) * 2u;
+            const uint32_t voff = (uint32_t)((lane ^ (i % 16)) * 16);
+            GF_LDS char* dst = smem + slot * Cf::CHUNK_BYTES + i * (kSkinnyKc * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_b ? rb : ra, (GF_LDS void*)dst, 16, voff, soff, 0, 0);
+        }
+    };
+    // Fragment of tile row block `blk` (16 rows) at k-step ks of a chunk:
+    // lane l reads row 16 * blk + l % 16, 16-byte chunk 4 * ks + l / 16.
+    const int r16 = lane % 16, kq = lane / 16;
+    auto frag = [&](int slot, int blk, int ks) {
+        const int row = 16 * blk + r16;
+        const int c = (4 * ks + kq) ^ r16;
+        return *(const GF_LDS half8*)(smem + slot * Cf::CHUNK_BYTES + row * (kSkinnyKc * 2) + c * 16);
+    };
+    floatx4 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    // Prologue: chunks 0 .. S-2 (chunk indices past the end load a valid
+    // chunk 0 again, keeping the count of loads in flight fixed).
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) issue_chunk(t < nchunks ? t : 0, t);
+    for (int t = 0; t < nchunks; ++t) {
+        wait_vmcnt<Cf::LW * (S - 2)>();          // this wave's loads of chunk t landed
+        lds_barrier();                           // everyone's; chunk t - 1's slot is free
+        const int tn = t + S - 1;
+        issue_chunk(tn < nchunks ? tn : 0, tn % S);
+        const int slot = t % S;
+#pragma unroll
+        for (int ks = 0; ks < kSkinnyKc / 32; ++ks) {
+            if (ks % W != wave % W) continue;    // wave-uniform
+            const half8 a = frag(slot, NB, ks);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, frag(slot, j, ks), acc[j], 0, 0, 0);
+        }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();                               // stage memory is free: reuse it for the partials
+    floatx4* part = (floatx4*)smem_raw;         // [W][NB][64]
+#pragma unroll
+    for (int j = 0; j < NB; ++j) part[(wave * NB + j) * kWave + lane] = acc[j];
+    __syncthreads();
+    if (threadIdx.x < NB * kWave) {
+        const int j = threadIdx.x / kWave, l = threadIdx.x % kWave;
+        floatx4 sum = part[j * kWave + l];
+#pragma unroll
+        for (int w = 1; w < W; ++w) sum += part[(w * NB + j) * kWave + l];
+        const int n = n0 + j * 16 + l % 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * (l / 16) + i;
+            if (m < M && n < N) C[(size_t)m * N + n] = f32_to_f16_bits(sum[i]);
+        }
+    }
+#endif
+}
+
+template <int NB, int S, int W>
+hipError_t launch_skinny_lds(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                             hipStream_t stream)
+{
+    typedef SkinnyLdsCfg<NB, S, W> Cf;
+    static_assert(Cf::kValid, "skinny LDS config");
+    auto kern = skinny_lds_kernel<NB, S, W>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, Cf::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int grid = ceil_div(N, NB * 16);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(W * kWave), Cf::LDS_BYTES, stream, A, B, C, M, N, K);
+    return hipGetLastError();
+}
+
 }  // namespace gf

@@ -193,15 +193,18 @@ int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int
  * this path by itself when M <= 16, K % 8 == 0 and A and B are 16-byte
  * aligned; this entry point runs it explicitly and returns
  * GF_ERR_UNSUPPORTED outside those conditions.  cfg: launch shape (blocks =
- * 16-row blocks of B per workgroup, unroll = k-steps per register batch, two
- * batches in flight per wave, waves = waves per workgroup splitting K), NULL =
- * the library's choice.
+ * 16-row blocks of B per workgroup, waves = waves per workgroup splitting K,
+ * and stages = 0 for the direct form, whose loads go straight to registers
+ * (unroll = k-steps per register batch, two batches in flight per wave), or
+ * stages >= 2 for the LDS-staged form, which loads 1 KiB of one row per
+ * instruction through a ring of that many 512-k chunks (needs K % 512 == 0;
+ * unroll 0)), NULL = the library's choice.
  * Defined by the TileLang GEMV page: GEMV as the degenerate GEMM with a
  * single row of A, here with up to 16 rows (C = A B^T of the TileLang FP16
  * matmul page, section 1).
  */
 typedef struct gf_skinny_cfg {
-    int blocks, unroll, waves;
+    int blocks, unroll, waves, stages;
 } gf_skinny_cfg;
 int gemm_f16_nt_skinny(const void* A, const void* B, void* C, int M, int N, int K,
                        const gf_skinny_cfg* cfg, void* stream);

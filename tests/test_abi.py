@@ -118,7 +118,7 @@ def test_skinny_validation(L):
     assert sk(FAKE, FAKE, FAKE, 17, 64, 64, None, s) == gf.GF_ERR_UNSUPPORTED      # M > 16
     assert sk(FAKE, FAKE, FAKE, 4, 64, 60, None, s) == gf.GF_ERR_UNSUPPORTED       # K % 8 != 0
     assert sk(ctypes.c_void_p(0x10002), FAKE, FAKE, 4, 64, 64, None, s) == gf.GF_ERR_UNSUPPORTED
-    bad = gf.SkinnyCfg(3, 3, 8)
+    bad = gf.SkinnyCfg(3, 3, 8, 0)
     assert sk(FAKE, FAKE, FAKE, 4, 64, 64, ctypes.byref(bad), s) == gf.GF_ERR_UNSUPPORTED
     assert sk(FAKE, FAKE, FAKE, -1, 64, 64, None, s) == gf.GF_ERR_INVALID_ARG
     assert sk(FAKE, FAKE, NULL, 4, 0, 64, None, s) == gf.GF_OK                      # empty C

@@ -252,13 +252,29 @@ def test_skinny(M, N, K):
     check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny %dx%dx%d" % (M, N, K))
 
 
-def test_skinny_every_config():
-    M, N, K = 16, 520, 1000
+@pytest.mark.parametrize("M,N,K", [(16, 520, 1536), (3, 1000, 512), (9, 77, 2048)])
+def test_skinny_every_config(M, N, K):
+    """Every launch shape, direct and LDS-staged (K a multiple of 512)."""
     A, B = operands("integer", M, N, K, seed=6)
     ref = oracle.gemm_nt_f16(A, B)
     for cfg in gf.skinny_configs():
-        _say("skinny cfg %s" % cfg)
+        _say("skinny cfg %s %dx%dx%d" % (cfg, M, N, K))
         assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
+    A, B = operands("uniform", M, N, K, seed=6)
+    ref = oracle.gemm_nt_f16(A, B)
+    for cfg in gf.skinny_configs():
+        check_f16_tolerance(run_skinny(A, B, cfg), ref, "skinny %s %dx%dx%d" % (cfg, M, N, K))
+
+
+def test_skinny_lds_form_needs_k_multiple_of_512():
+    A, B = operands("integer", 4, 64, 1000, seed=6)
+    ref = oracle.gemm_nt_f16(A, B)
+    for cfg in gf.skinny_configs():
+        if cfg["stages"] == 0:
+            assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
+        else:
+            with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+                run_skinny(A, B, cfg)
 
 
 def test_skinny_is_gemm_nt_for_small_m():
