@@ -149,20 +149,14 @@ __device__ __forceinline__ void slot_source(int s, int& k_in_tile, int& row_in_t
 // computed once per tile position; the K tile's offset (k0 times the byte
 // stride of one k step: 2 for layout 0, 2 * M or 2 * N for layout 1) is added
 // per issue.
-#ifndef GF_DMA_BUFFER
-#define GF_DMA_BUFFER 1
-#endif
-
 template <class Cfg>
 struct DmaLoader {
     uint32_t voff[Cfg::LPS];   // byte offset of load r's chunk at k = 0 (rows / columns clamped)
     int tid;
     uint32_t ska, skb;         // bytes per k step in A and in B
-#if GF_DMA_BUFFER
     // Buffer descriptors of A and B (raw, byte-addressed): the tile's K
     // offset travels in the scalar offset, the row/chunk offset in voff.
     __amdgpu_buffer_rsrc_t ra, rb;
-#endif
 
     __device__ __forceinline__ void init(const GemmArgs& a, int m0, int n0, int tid_)
     {
@@ -187,13 +181,11 @@ struct DmaLoader {
             }
             voff[r] = off * 2u;
         }
-#if GF_DMA_BUFFER
         constexpr int kRawBufferWord3 = 0x00020000;
         ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, (int)((uint32_t)a.M * (uint32_t)a.K * 2u),
                                                kRawBufferWord3);
         rb = __builtin_amdgcn_make_buffer_rsrc((void*)a.B, 0, (int)((uint32_t)a.N * (uint32_t)a.K * 2u),
                                                kRawBufferWord3);
-#endif
     }
 
     // Whether load r of the K tile at k0 lies inside K (its chunk for
@@ -217,10 +209,7 @@ struct DmaLoader {
     // kernel's own vmcnt waits and barriers, as for every load here.  The
     // wave's LDS destination goes in through M0 (the compiler writes it);
     // an s_nop gives the one wait state an M0 write needs before an LDS DMA.
-#ifndef GF_ASM_DMA_ALL
-#define GF_ASM_DMA_ALL 0
-#endif
-    static constexpr bool kAsmDma = GF_ASM_DMA_ALL || Cfg::LA != 0 || Cfg::LB != 0;
+    static constexpr bool kAsmDma = Cfg::LA != 0 || Cfg::LB != 0;
 
     // Load r of the K tile whose first K index is k0; every chunk must lie
     // inside K.  Uniform base + 32-bit offset.
@@ -230,7 +219,6 @@ struct DmaLoader {
         const int wslot = r * Cfg::NT + wave * kWave;    // wave-uniform
         const bool is_a = wslot < Cfg::BM * Cfg::CH;     // wave-uniform
         const uint32_t koff = (uint32_t)k0 * (is_a ? ska : skb);
-#if GF_DMA_BUFFER
         (void)a;
         if constexpr (kAsmDma) {
             const uint32_t lds = (uint32_t)(uintptr_t)(stage + wslot * 16);
@@ -240,11 +228,6 @@ struct DmaLoader {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb, (GF_LDS void*)(stage + wslot * 16),
                                                      16, voff[r], koff, 0, 0);
         }
-#else
-        const char* base = (const char*)(is_a ? a.A : a.B);
-        __builtin_amdgcn_global_load_lds(base + (voff[r] + koff), (GF_LDS void*)(stage + wslot * 16),
-                                         16, 0, 0);
-#endif
     }
 
     // The same where the tile may run past K: chunks at k >= K read 16 zero bytes.
@@ -535,14 +518,11 @@ __device__ __forceinline__ void compute_tile(const GF_LDS char* stage, const Fra
     }
 }
 
-#ifndef GF_RPM
-#define GF_RPM 1
-#endif
 // One MFMA step of SCHED 2/3: the FM x FN MFMAs on fragment buffer CUR,
 // with the reads of step RKS's fragments from stage RS (possibly the next
 // tile's) into buffer CUR ^ 1 and the direct-to-LDS loads R0 .. R1-1 of the
 // tile at lk0 woven into the stream.
-template <class Cfg, int CUR, int RKS, int R0, int R1, int RPM = GF_RPM>
+template <class Cfg, int CUR, int RKS, int R0, int R1>
 __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[Cfg::FM][Cfg::FN],
                                           half8 (&af)[2][Cfg::FM], half8 (&bf)[2][Cfg::FN],
                                           const Frags<Cfg>& fr, const GF_LDS char* RS,
@@ -560,16 +540,10 @@ __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[C
     // run row by row (A[fm] x B[0..FN-1]), so B0 and A0 first, then the
     // rest of B, then A1 .. A[FM-1].  Each MFMA then waits only for its own
     // operands instead of for the whole batch.
-    // LDS instructions behind read j, and behind the reads that follow MFMA i.
+    // LDS instructions behind read j (the read that follows MFMA j).
     auto nds = [](int j) constexpr {
         return ((j == 0) || (j >= 2 && j <= Cfg::FN)) ? FragReader<Cfg, false>::NDS
                                                       : FragReader<Cfg, true>::NDS;
-    };
-    auto nds_after = [=](int i) constexpr {
-        int n = 0;
-        for (int q = 0; q < RPM; ++q)
-            if (i * RPM + q < ND) n += nds(i * RPM + q);
-        return n;
     };
     const GF_LDS char* RBt = RS + Cfg::A_BYTES;
     auto read = [&](auto j_c) {
@@ -585,14 +559,11 @@ __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[C
         constexpr int i = decltype(i_c)::value;
         constexpr int fm = i / Cfg::FN, fn = i % Cfg::FN;
         acc[fm][fn] = Mfma<MT>::run(af[CUR][fm], bf[CUR][fn], acc[fm][fn]);
-        static_for<RPM>([&](auto q_c) {
-            constexpr int j = i * RPM + decltype(q_c)::value;
-            if constexpr (j < ND) read(std::integral_constant<int, j>{});
-        });
+        if constexpr (i < ND) read(i_c);
         if constexpr (load_at(i) >= 0) ld.issue(a, lstage, lk0, load_at(i), wave);
     });
     static_for<ND>([&](auto j_c) {
-        if constexpr (decltype(j_c)::value >= NM * RPM) read(j_c);
+        if constexpr (decltype(j_c)::value >= NM) read(j_c);
     });
     static_for<NL>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
@@ -600,7 +571,7 @@ __device__ __forceinline__ void mfma_step(typename Mfma<Cfg::MT>::acc_t (&acc)[C
     });
     static_for<NM>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
-        constexpr int nr = nds_after(i);
+        constexpr int nr = i < ND ? nds(i) : 0;
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nr, 0);
         if constexpr (load_at(i) >= 0) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
@@ -782,20 +753,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         // iteration; no wait sits under a branch.
         constexpr int S = Cfg::STAGES;
         constexpr int KST = Cfg::BK / Cfg::KS;
-#ifndef GF_S2_HEAD
-#define GF_S2_HEAD 2
-#endif
-#ifndef GF_S2_SPREAD
-#define GF_S2_SPREAD 1
-#endif
-        // Loads of tile t + S: LPS / GF_S2_HEAD under the last step of tile
-        // t, the rest spread evenly over the first GF_S2_SPREAD steps of
-        // tile t + 1.
-        constexpr int H = Cfg::LPS / GF_S2_HEAD;
-        constexpr int NSP = GF_S2_SPREAD < KST - 1 ? GF_S2_SPREAD : KST - 1;
-        auto rest_lo = [](int ks) constexpr {
-            return ks >= NSP ? Cfg::LPS : H + (Cfg::LPS - H) * ks / NSP;
-        };
+        // Loads of tile t + S: half under the last step of tile t, half in
+        // the first step of tile t + 1 (measured best among splits over one
+        // to three steps).
+        constexpr int H = Cfg::LPS / 2;
+        auto rest_lo = [](int ks) constexpr { return ks >= 1 ? Cfg::LPS : H; };
         half8 af[2][Cfg::FM], bf[2][Cfg::FN];
         if (nk > 0) {
 #pragma unroll
