@@ -17,7 +17,13 @@ output of a SplitMix64 generator seeded with 0.  From z:
     uniform value  = fp16(2u - 1)               round-to-nearest-even, [-1, 1]
     integer value  = floor(5u) - 2              in {-2, -1, 0, 1, 2}
 
-Stream ids: 0 for A (GEMM) or W (GEMV), 1 for B (GEMM) or x (GEMV).
+Stream ids: 0 for A (GEMM) or W (GEMV), 1 for B (GEMM) or x (GEMV), 2 for
+the 2:4 sparsity pattern of A.
+
+2:4-sparse A (``sparse24``): values as above; along the last axis every group
+of 4 consecutive entries keeps one of its 6 index pairs, pair floor(6u) in the
+order (0,1) (0,2) (0,3) (1,2) (1,3) (2,3), u drawn from stream 2 (one draw per
+group), and its other two entries are set to +0.
 """
 from __future__ import annotations
 
@@ -29,6 +35,9 @@ _M2 = np.uint64(0x94D049BB133111EB)
 
 STREAM_A = 0
 STREAM_B = 1
+STREAM_MASK = 2
+
+_PAIRS = np.array([(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)])
 
 
 _CHUNK = 1 << 20
@@ -117,3 +126,21 @@ def make(kind: str, shape, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarr
     if kind == "integer":
         return integer_f16(shape, seed, stream_id)
     raise ValueError("kind must be 'uniform' or 'integer'")
+
+
+def sparse24(kind: str, shape, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarray:
+    """A ``make(kind, ...)`` array with at most 2 nonzeros in each group of 4
+    along the last axis (whose length must be a multiple of 4)."""
+    a = make(kind, shape, seed, stream_id)
+    if shape[-1] % 4:
+        raise ValueError("the last axis must be a multiple of 4")
+    groups = a.size // 4
+    pick = np.minimum((uniform01(seed, STREAM_MASK, groups) * 6.0).astype(np.int64), 5)
+    keep = np.zeros((groups, 4), dtype=bool)
+    rows = np.arange(groups)
+    keep[rows, _PAIRS[pick, 0]] = True
+    keep[rows, _PAIRS[pick, 1]] = True
+    g = a.reshape(groups, 4)
+    g[~keep] = np.float16(0.0)
+    return a
+

@@ -21,6 +21,14 @@ Functions and the passages they follow:
   statement and kernel signatures A(K,), B(N,K), C(N,) with x = A, W = B.
 * ``gemm_nt_entries``    -- single entries of the above, for sampled checks of
   full-size outputs.
+* ``sp24_compress(A)`` / ``sp24_decompress(A_sparse, E)`` -- 2:4 structured
+  sparsity: each group of 4 consecutive k keeps its two largest-magnitude
+  entries (ties to the lower index); A_sparse is (M, K/2), E is (M, K/16)
+  16-bit words of 4-bit fields i0 | i1 << 2.  TileLang FP16 matmul autotune
+  benchmark page, section 6 (A_sparse (M, K/2), metadata E (M, K/e_factor));
+  the selection rule and the bit layout are readings (see ``oracle.c``).
+* ``gemm_sp_nt_f16(A_sparse, E, B)`` -- round_f16(decompress(A_sparse, E) .
+  B^T), the GEMM above with the A that the compressed form describes.
 * ``f16_from_double`` / ``f16_to_double`` -- IEEE binary16 round-to-nearest-
   even encode and exact decode.
 """
@@ -73,8 +81,11 @@ def _load():
     lib.oracle_f16_encode_array.restype = None
     lib.oracle_f16_decode_array.argtypes = [u16p, f64p, ctypes.c_int64]
     lib.oracle_f16_decode_array.restype = None
+    lib.oracle_sp24_compress.argtypes = [u16p, u16p, u16p, c_int, c_int]
+    lib.oracle_sp24_decompress.argtypes = [u16p, u16p, u16p, c_int, c_int]
     for name in ("oracle_gemm_nt_f16_rows", "oracle_gemm_nt_f16", "oracle_gemm_nt_f32",
-                 "oracle_gemm_nt_entries", "oracle_gemv_f16", "oracle_threads"):
+                 "oracle_gemm_nt_entries", "oracle_gemv_f16", "oracle_threads",
+                 "oracle_sp24_compress", "oracle_sp24_decompress"):
         getattr(lib, name).restype = c_int
     _lib = lib
     return lib
@@ -184,3 +195,46 @@ def f16_bits_to_double(h) -> np.ndarray:
     out = np.zeros(h.shape[0], dtype=np.float64)
     _load().oracle_f16_decode_array(_p(h, ctypes.c_uint16), _p(out, ctypes.c_double), h.shape[0])
     return out
+
+
+def sp24_compress(A) -> tuple[np.ndarray, np.ndarray]:
+    """2:4 compression of A (M, K), K a multiple of 16: returns A_sparse
+    (M, K/2) uint16 fp16 bits and E (M, K/16) uint16 metadata words."""
+    A = _u16(A)
+    M, K = A.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    Asp = np.zeros((M, K // 2), dtype=np.uint16)
+    E = np.zeros((M, K // 16), dtype=np.uint16)
+    rc = _load().oracle_sp24_compress(_p(A, ctypes.c_uint16), _p(Asp, ctypes.c_uint16),
+                                      _p(E, ctypes.c_uint16), M, K)
+    if rc:
+        raise RuntimeError("oracle_sp24_compress failed (%d)" % rc)
+    return Asp, E
+
+
+def sp24_decompress(Asp, E) -> np.ndarray:
+    """The dense (M, K) uint16 A that A_sparse (M, K/2) and E (M, K/16) describe."""
+    Asp = _u16(Asp)
+    E = np.ascontiguousarray(E, dtype=np.uint16)
+    M, K2 = Asp.shape
+    K = 2 * K2
+    if E.shape != (M, K // 16) or K % 16:
+        raise ValueError("A_sparse must be (M, K/2) and E (M, K/16) with K a multiple of 16")
+    A = np.zeros((M, K), dtype=np.uint16)
+    rc = _load().oracle_sp24_decompress(_p(Asp, ctypes.c_uint16), _p(E, ctypes.c_uint16),
+                                        _p(A, ctypes.c_uint16), M, K)
+    if rc:
+        raise RuntimeError("oracle_sp24_decompress failed (%d)" % rc)
+    return A
+
+
+def gemm_sp_nt_f16(Asp, E, B, rows: tuple[int, int] | None = None) -> np.ndarray:
+    """C = round_f16(decompress(A_sparse, E) . B^T); returns (M, N) uint16."""
+    return gemm_nt_f16(sp24_decompress(Asp, E), B, rows)
+
+
+def gemm_sp_nt_entries(Asp, E, B, ij) -> np.ndarray:
+    """Entries C[i, j] (fp16 bits) of the sparse product for each row of ``ij``."""
+    return gemm_nt_entries(sp24_decompress(Asp, E), B, ij)[0]
+

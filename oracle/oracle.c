@@ -24,6 +24,30 @@
  *          GEMV optimisation" page, problem statement (GEMV is the (1,k)x(k,n)
  *          degenerate GEMM) and its kernels' signature A(K,), B(N,K), C(N,),
  *          accumulated in float; here x = A, W = B, y = C.
+ *   2:4    Structured sparsity of A.  Source: the "TileLang FP16 matmul
+ *          autotune benchmark" page, section 6 (further reading): A is
+ *          compressed 2:4-style into A_sparse of shape (M, K/2) plus mask
+ *          metadata E of shape (M, K/e_factor), and the sparse product is
+ *          the GEMM above taken with the A that these two describe.  The page
+ *          fixes neither the choice of the two kept entries nor the bit
+ *          layout of E; the readings taken here:
+ *            - K is cut into groups of 4 consecutive entries; a group keeps
+ *              the two entries of largest magnitude, ties going to the lower
+ *              index (so a group with at most two nonzeros loses nothing).
+ *              Magnitude is compared on the fp16 bit pattern without its
+ *              sign, which orders every non-NaN value by |x| and puts NaN
+ *              above infinity.
+ *            - A_sparse holds the two kept values of group g at positions
+ *              2g, 2g+1, lower index first.
+ *            - E holds 4 bits per group, i0 | i1 << 2 (i0 < i1 the kept
+ *              indices within the group), packed from the least significant
+ *              bit up in group order into 16-bit words: group g sits at bits
+ *              4 (g % 4) of word g / 4, so E is (M, K/16) for e_dtype int16
+ *              (e_factor 16); read as bytes (int8) or 32-bit words (int32) on
+ *              a little-endian machine the same memory is the e_factor 8 and
+ *              32 forms.
+ *          K must be a multiple of 16 (whole metadata words).
+ *          SPARSE GEMM C = round_f16( decompress(A_sparse, E) . B^T ).
  *
  * Arithmetic: every input is decoded exactly to double, every sum runs over
  * ascending k starting from +0.0, and the result is rounded once.  A product
@@ -238,3 +262,75 @@ void oracle_f16_decode_array(const uint16_t* h, double* out, int64_t n)
     for (int64_t t = 0; t < n; ++t)
         out[t] = oracle_f16_to_double(h[t]);
 }
+
+/* ---- 2:4 structured sparsity ------------------------------------------ */
+
+/* Sign-free bit pattern: orders fp16 values by magnitude (NaN above inf). */
+static unsigned magnitude_key(uint16_t h) { return h & 0x7fffu; }
+
+/* A (M x K) -> A_sparse (M x K/2) and E (M x K/16 16-bit words). */
+int oracle_sp24_compress(const uint16_t* A, uint16_t* Asp, uint16_t* E, int M, int K)
+{
+    if (M < 0 || K < 0 || K % 16 != 0)
+        return 1;
+    const int groups = K / 4;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < M; ++i) {
+        const uint16_t* a = A + (int64_t)i * K;
+        uint16_t* v = Asp + (int64_t)i * (K / 2);
+        uint16_t* e = E + (int64_t)i * (K / 16);
+        for (int w = 0; w < K / 16; ++w)
+            e[w] = 0;
+        for (int g = 0; g < groups; ++g) {
+            const uint16_t* x = a + 4 * g;
+            /* largest magnitude, first occurrence */
+            int first = 0;
+            for (int t = 1; t < 4; ++t)
+                if (magnitude_key(x[t]) > magnitude_key(x[first]))
+                    first = t;
+            /* largest of the other three, first occurrence */
+            int second = -1;
+            for (int t = 0; t < 4; ++t) {
+                if (t == first)
+                    continue;
+                if (second < 0 || magnitude_key(x[t]) > magnitude_key(x[second]))
+                    second = t;
+            }
+            const int i0 = first < second ? first : second;
+            const int i1 = first < second ? second : first;
+            v[2 * g] = x[i0];
+            v[2 * g + 1] = x[i1];
+            e[g / 4] |= (uint16_t)((i0 | (i1 << 2)) << (4 * (g % 4)));
+        }
+    }
+    return 0;
+}
+
+/* A_sparse and E -> the dense A they describe (zeros elsewhere).  Returns 3
+ * if a group's field does not name two indices in increasing order. */
+int oracle_sp24_decompress(const uint16_t* Asp, const uint16_t* E, uint16_t* A, int M, int K)
+{
+    if (M < 0 || K < 0 || K % 16 != 0)
+        return 1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int i = 0; i < M; ++i) {
+        const uint16_t* v = Asp + (int64_t)i * (K / 2);
+        const uint16_t* e = E + (int64_t)i * (K / 16);
+        uint16_t* a = A + (int64_t)i * K;
+        for (int k = 0; k < K; ++k)
+            a[k] = 0;
+        for (int g = 0; g < K / 4; ++g) {
+            const int field = (e[g / 4] >> (4 * (g % 4))) & 0xf;
+            const int i0 = field & 3, i1 = field >> 2;
+            if (i0 >= i1) {
+                bad = 1;
+                continue;
+            }
+            a[4 * g + i0] = v[2 * g];
+            a[4 * g + i1] = v[2 * g + 1];
+        }
+    }
+    return bad ? 3 : 0;
+}
+
