@@ -23,6 +23,8 @@ EXPORTS = (
     "gemm_f16_nt_skinny", "gf_skinny_config_count", "gf_skinny_config_get", "gemm_f16_nt_splitk_cfg",
     "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
     "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
+    "sp24_compress_f16", "gemm_sp_f16_nt", "gemm_sp_f16_nt_cfg", "gf_sp_config_count",
+    "gf_sp_config_get", "gf_sp_default_config",
 )
 
 
@@ -33,6 +35,13 @@ class SkinnyCfg(ctypes.Structure):
 class GemmCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ("block_m", "block_n", "block_k", "stages", "threads", "raster", "schedule")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class SpCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("block_m", "block_n", "stages", "raster")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -77,6 +86,11 @@ def lib() -> ctypes.CDLL:
     L.gf_gemv_config_get.argtypes = [ci, ctypes.POINTER(GemvCfg)]
     L.gf_gemm_default_config.argtypes = [ci, ci, ci, ctypes.POINTER(GemmCfg)]
     L.gf_gemv_default_config.argtypes = [ci, ci, ctypes.POINTER(GemvCfg)]
+    L.sp24_compress_f16.argtypes = [vp, vp, vp, ci, ci, vp]
+    L.gemm_sp_f16_nt.argtypes = [vp, vp, vp, vp, ci, ci, ci, vp]
+    L.gemm_sp_f16_nt_cfg.argtypes = [vp, vp, vp, vp, ci, ci, ci, ctypes.POINTER(SpCfg), vp]
+    L.gf_sp_config_get.argtypes = [ci, ctypes.POINTER(SpCfg)]
+    L.gf_sp_default_config.argtypes = [ci, ci, ci, ctypes.POINTER(SpCfg)]
     L.gf_status_string.argtypes = [ci]
     L.gf_status_string.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -106,7 +120,7 @@ def _dev(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError("%s must be a CUDA (HIP) tensor" % name)
-    if t.dtype != dtype:
+    if t.dtype != dtype and not (dtype == torch.int16 and t.dtype == getattr(torch, "uint16", None)):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
@@ -396,3 +410,86 @@ def prepare_gemv_f16(W, x, y, stream=None, cfg: dict | None = None):
                 _check(rc, "gemv_f16_cfg")
     call.keep = (W, x, y, args)
     return call
+
+
+# ---------------------------------------------------------------------------
+# 2:4 structured sparsity
+# ---------------------------------------------------------------------------
+
+def sp24_compress_f16(A, A_sparse=None, E=None, stream=None):
+    """Compress A (M, K) fp16, K % 16 == 0, into A_sparse (M, K/2) fp16 and
+    E (M, K/16) int16 metadata words.  Returns (A_sparse, E)."""
+    import torch
+    if A.dim() != 2:
+        raise ValueError("A must be (M, K)")
+    M, K = A.shape
+    if A_sparse is None:
+        A_sparse = torch.empty((M, K // 2), dtype=torch.float16, device=A.device)
+    if E is None:
+        E = torch.empty((M, K // 16), dtype=torch.int16, device=A.device)
+    if tuple(A_sparse.shape) != (M, K // 2) or tuple(E.shape) != (M, K // 16):
+        raise ValueError("A_sparse must be (M, K/2) and E (M, K/16)")
+    _check(lib().sp24_compress_f16(_dev(A, torch.float16, "A"), _dev(A_sparse, torch.float16, "A_sparse"),
+                                   _dev(E, torch.int16, "E"), M, K, _stream(stream)), "sp24_compress_f16")
+    return A_sparse, E
+
+
+def _sp_args(A_sparse, E, B, C):
+    import torch
+    if A_sparse.dim() != 2 or E.dim() != 2 or B.dim() != 2:
+        raise ValueError("A_sparse must be (M, K/2), E (M, K/16), B (N, K)")
+    M, K = A_sparse.shape[0], 2 * A_sparse.shape[1]
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(E.shape) != (M, K // 16):
+        raise ValueError("A_sparse must be (M, K/2), E (M, K/16), B (N, K)")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float16, device=B.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be (M, N)")
+    args = (_dev(A_sparse, torch.float16, "A_sparse"), _dev(E, torch.int16, "E"), _dev(B, torch.float16, "B"),
+            _dev(C, torch.float16, "C"), M, N, K)
+    return C, args
+
+
+def gemm_sp_f16_nt(A_sparse, E, B, C=None, stream=None, cfg: dict | None = None):
+    """C = decompress(A_sparse, E) . B^T (fp16 in, fp32 accumulate, fp16 out)."""
+    C, args = _sp_args(A_sparse, E, B, C)
+    if cfg is None:
+        _check(lib().gemm_sp_f16_nt(*args, _stream(stream)), "gemm_sp_f16_nt")
+    else:
+        c = SpCfg(**cfg)
+        _check(lib().gemm_sp_f16_nt_cfg(*args, ctypes.byref(c), _stream(stream)), "gemm_sp_f16_nt_cfg")
+    return C
+
+
+def prepare_gemm_sp_f16_nt(A_sparse, E, B, C, stream=None, cfg: dict | None = None):
+    """Zero-argument callable that launches the sparse product on `stream`."""
+    C, args = _sp_args(A_sparse, E, B, C)
+    s = _stream(stream)
+    L = lib()
+    c = SpCfg(**cfg) if cfg is not None else None
+    ref = ctypes.byref(c) if c is not None else None
+    fn = L.gemm_sp_f16_nt_cfg
+
+    def call():
+        rc = fn(*args, ref, s)
+        if rc:
+            _check(rc, "gemm_sp_f16_nt_cfg")
+    call.keep = (A_sparse, E, B, C, args, c)
+    return call
+
+
+def sp_configs() -> list[dict]:
+    L, out = lib(), []
+    for i in range(L.gf_sp_config_count()):
+        c = SpCfg()
+        _check(L.gf_sp_config_get(i, ctypes.byref(c)), "gf_sp_config_get")
+        out.append(c.as_dict())
+    return out
+
+
+def sp_default_config(M: int, N: int, K: int) -> dict:
+    c = SpCfg()
+    _check(lib().gf_sp_default_config(M, N, K, ctypes.byref(c)), "gf_sp_default_config")
+    return c.as_dict()
+

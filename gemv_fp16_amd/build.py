@@ -30,7 +30,8 @@ FLAGS = [
 
 def _units():
     units = [("gemm_shard.hip", "gemm_shard_%d.o" % i, ["-DGF_SHARD=%d" % i]) for i in range(N_SHARDS)]
-    units += [("gemv.hip", "gemv.o", []), ("skinny.hip", "skinny.o", []), ("api.hip", "api.o", [])]
+    units += [("gemv.hip", "gemv.o", []), ("skinny.hip", "skinny.o", []),
+              ("sparse.hip", "sparse.o", []), ("api.hip", "api.o", [])]
     return units
 
 

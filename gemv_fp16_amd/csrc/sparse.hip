@@ -1,0 +1,156 @@
+// 2:4 structured-sparse GEMM and compression: kernel instances and C-ABI
+// entry points.  Validation runs on the host before any HIP call.
+#include <stdint.h>
+
+#include "../../include/gemvfp16.h"
+#include "sparse_kernel.hpp"
+
+namespace gf {
+namespace {
+
+constexpr int64_t kSpMaxElems = (int64_t(1) << 31) - 1;
+constexpr int kSpDefaultPanel = 10;
+
+bool sp_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+typedef hipError_t (*SpLaunchFn)(const SpArgs&, hipStream_t);
+
+struct SpDesc {
+    int bm, bn, stages;
+    SpLaunchFn fn;
+};
+
+template <int BM, int BN, int S>
+constexpr SpDesc sp_desc()
+{
+    return SpDesc{BM, BN, S, &launch_sp_gemm<SpCfg<BM, BN, S>, true>};
+}
+
+// Compiled tile configs (the offline sweep times each of them).
+const SpDesc kSpConfigs[] = {
+    sp_desc<256, 256, 2>(), sp_desc<256, 256, 3>(),
+    sp_desc<256, 128, 2>(), sp_desc<256, 128, 3>(), sp_desc<256, 128, 4>(),
+    sp_desc<128, 256, 2>(), sp_desc<128, 256, 3>(),
+    sp_desc<128, 128, 2>(), sp_desc<128, 128, 3>(), sp_desc<128, 128, 4>(),
+};
+constexpr int kNumSp = sizeof(kSpConfigs) / sizeof(kSpConfigs[0]);
+
+static_assert(SpCfg<256, 256, 2>::kValid && SpCfg<256, 256, 3>::kValid && SpCfg<256, 128, 2>::kValid &&
+                  SpCfg<256, 128, 3>::kValid && SpCfg<256, 128, 4>::kValid && SpCfg<128, 256, 2>::kValid &&
+                  SpCfg<128, 256, 3>::kValid && SpCfg<128, 128, 2>::kValid && SpCfg<128, 128, 3>::kValid &&
+                  SpCfg<128, 128, 4>::kValid,
+              "every listed sparse config must be valid");
+
+// Operands without the direct-to-LDS alignment take one register-staged kernel.
+typedef SpCfg<128, 128, 2> SpFallbackCfg;
+
+int find_sp(const gf_sp_cfg& c)
+{
+    for (int i = 0; i < kNumSp; ++i)
+        if (kSpConfigs[i].bm == c.block_m && kSpConfigs[i].bn == c.block_n && kSpConfigs[i].stages == c.stages)
+            return i;
+    return -1;
+}
+
+// The largest tile that still gives every CU a workgroup.
+gf_sp_cfg default_sp_cfg(int M, int N)
+{
+    gf_sp_cfg c;
+    c.raster = 1;
+    const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+    const int64_t t25612 = (int64_t)ceil_div(M, 256) * ceil_div(N, 128);
+    if (t256 >= 256) { c.block_m = 256; c.block_n = 256; c.stages = 3; }
+    else if (t25612 >= 256) { c.block_m = 256; c.block_n = 128; c.stages = 3; }
+    else { c.block_m = 128; c.block_n = 128; c.stages = 3; }
+    return c;
+}
+
+int validate_sp(const void* Asp, const void* E, const void* B, const void* C, int M, int N, int K)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return GF_ERR_INVALID_ARG;
+    if ((int64_t)M * K > kSpMaxElems || (int64_t)N * K > kSpMaxElems || (int64_t)M * N > kSpMaxElems)
+        return GF_ERR_INVALID_ARG;
+    if (M > 0 && K > 0 && (!Asp || !E || !sp_aligned(Asp, 2) || !sp_aligned(E, 2))) return GF_ERR_INVALID_ARG;
+    if (N > 0 && K > 0 && (!B || !sp_aligned(B, 2))) return GF_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && (!C || !sp_aligned(C, 2))) return GF_ERR_INVALID_ARG;
+    return GF_OK;
+}
+
+int sp_impl(const void* Asp, const void* E, const void* B, void* C, int M, int N, int K, const gf_sp_cfg& cfg,
+            hipStream_t stream)
+{
+    const int idx = find_sp(cfg);
+    if (idx < 0) return GF_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return GF_OK;
+    SpArgs a;
+    a.Asp = (const uint16_t*)Asp;
+    a.E = (const uint16_t*)E;
+    a.B = (const uint16_t*)B;
+    a.C = (uint16_t*)C;
+    a.M = M; a.N = N; a.K = K;
+    a.raster = cfg.raster <= 0 ? 0 : (cfg.raster == 1 ? kSpDefaultPanel : cfg.raster);
+    const bool al = K % 32 == 0 && sp_aligned(Asp, 16) && sp_aligned(B, 16) && sp_aligned(E, 4);
+    hipError_t e = al ? kSpConfigs[idx].fn(a, stream) : launch_sp_gemm<SpFallbackCfg, false>(a, stream);
+    return e == hipSuccess ? GF_OK : GF_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace gf
+
+using namespace gf;
+
+extern "C" {
+
+int sp24_compress_f16(const void* A, void* A_sparse, void* E, int M, int K, void* stream)
+{
+    if (M < 0 || K < 0 || K % 16 != 0 || (int64_t)M * K > kSpMaxElems) return GF_ERR_INVALID_ARG;
+    if (M == 0 || K == 0) return GF_OK;
+    if (!A || !A_sparse || !E || !sp_aligned(A, 2) || !sp_aligned(A_sparse, 2) || !sp_aligned(E, 2))
+        return GF_ERR_INVALID_ARG;
+    const size_t words = (size_t)M * (size_t)(K / 16);
+    const int grid = (int)((words + 255) / 256 < 8192 ? (words + 255) / 256 : 8192);
+    hipStream_t s = (hipStream_t)stream;
+    if (sp_aligned(A, 16) && sp_aligned(A_sparse, 16))
+        hipLaunchKernelGGL(sp24_compress_kernel, dim3(grid), dim3(256), 0, s, (const u32x4*)A, (u32x4*)A_sparse,
+                           (uint16_t*)E, words);
+    else
+        hipLaunchKernelGGL(sp24_compress_kernel_u16, dim3(grid), dim3(256), 0, s, (const uint16_t*)A,
+                           (uint16_t*)A_sparse, (uint16_t*)E, words);
+    return hipGetLastError() == hipSuccess ? GF_OK : GF_ERR_HIP;
+}
+
+int gemm_sp_f16_nt_cfg(const void* A_sparse, const void* E, const void* B, void* C, int M, int N, int K,
+                       const gf_sp_cfg* cfg, void* stream)
+{
+    const int v = validate_sp(A_sparse, E, B, C, M, N, K);
+    if (v != GF_OK) return v;
+    const gf_sp_cfg c = cfg ? *cfg : default_sp_cfg(M, N);
+    return sp_impl(A_sparse, E, B, C, M, N, K, c, (hipStream_t)stream);
+}
+
+int gemm_sp_f16_nt(const void* A_sparse, const void* E, const void* B, void* C, int M, int N, int K,
+                   void* stream)
+{
+    return gemm_sp_f16_nt_cfg(A_sparse, E, B, C, M, N, K, nullptr, stream);
+}
+
+int gf_sp_config_count(void) { return kNumSp; }
+
+int gf_sp_config_get(int i, gf_sp_cfg* out)
+{
+    if (i < 0 || i >= kNumSp || !out) return GF_ERR_INVALID_ARG;
+    out->block_m = kSpConfigs[i].bm;
+    out->block_n = kSpConfigs[i].bn;
+    out->stages = kSpConfigs[i].stages;
+    out->raster = 1;
+    return GF_OK;
+}
+
+int gf_sp_default_config(int M, int N, int K, gf_sp_cfg* out)
+{
+    if (!out || M < 0 || N < 0 || K < 0) return GF_ERR_INVALID_ARG;
+    *out = default_sp_cfg(M, N);
+    return GF_OK;
+}
+
+}  // extern "C"

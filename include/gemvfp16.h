@@ -227,6 +227,59 @@ int gf_gemv_config_get(int i, gf_gemv_cfg* out);
 int gf_gemm_default_config(int M, int N, int K, gf_gemm_cfg* out);
 int gf_gemv_default_config(int N, int K, gf_gemv_cfg* out);
 
+/*
+ * 2:4 structured sparsity of A.
+ * Defined by the TileLang FP16 matmul autotune benchmark page, section 6
+ * (the sparse benchmark compresses A 2:4-style into A_sparse of shape
+ * (M, K/2) plus mask metadata E of shape (M, K/e_factor) and multiplies it
+ * with the sparse tensor-core GEMM).  The page fixes neither which two
+ * entries a group keeps nor the metadata bits; this library's format:
+ *  - K must be a multiple of 16; K is cut into groups of 4 consecutive k.
+ *  - A_sparse: M x K/2 fp16, row-major; group g's two kept values at 2g and
+ *    2g+1, lower index first.
+ *  - E: M x K/16 16-bit words, row-major; group g's field i0 | i1 << 2
+ *    (i0 < i1, the kept indices within the group) sits at bits 4 * (g % 4)
+ *    of word g / 4.  This is e_dtype int16 (e_factor 16); the same bytes
+ *    read as int8 or int32 are the e_factor 8 and 32 forms.
+ */
+
+/*
+ * Compress a dense A (M x K fp16) into A_sparse and E: each group keeps
+ * its two entries of largest magnitude (compared on the fp16 bits without
+ * the sign, so NaN ranks above infinity), ties going to the lower index.
+ * Lossless when no group of A has more than two nonzeros.  Bit-exact,
+ * deterministic.  A, A_sparse, E: device pointers, 2-byte aligned (16-byte
+ * aligned A and A_sparse take the vector path).  GF_ERR_INVALID_ARG for
+ * K % 16 != 0, M or K < 0, NULL or misaligned pointers, or M * K >= 2^31.
+ */
+int sp24_compress_f16(const void* A, void* A_sparse, void* E, int M, int K, void* stream);
+
+/*
+ * C = decompress(A_sparse, E) . B^T: the sparse product, A_sparse M x K/2
+ * fp16 and E M x K/16 as above, B N x K fp16 (dense, row-major), C M x N fp16.
+ * Products are accumulated in fp32 and each result is rounded once to fp16,
+ * as for gemm_f16_nt.  The fast path (direct-to-LDS loads) needs A_sparse and
+ * B 16-byte aligned, E 4-byte aligned and K % 32 == 0; otherwise a register-
+ * staged path computes the same result.  A metadata field with i0 >= i1
+ * gives an unspecified result for its row (no fault).  GF_ERR_INVALID_ARG for
+ * K % 16 != 0, negative sizes, NULL or misaligned pointers, or any operand of
+ * 2^31 elements or more.  M == 0 or N == 0 is a no-op; K == 0 writes +0.
+ */
+int gemm_sp_f16_nt(const void* A_sparse, const void* E, const void* B, void* C, int M, int N, int K,
+                   void* stream);
+
+/* Tile config of the sparse GEMM: block_m x block_n output tile (K tiles of
+ * 64), `stages` LDS buffers, raster as in gf_gemm_cfg.  NULL = the
+ * library's choice.  GF_ERR_UNSUPPORTED when no kernel is compiled for it. */
+typedef struct gf_sp_cfg {
+    int block_m, block_n, stages, raster;
+} gf_sp_cfg;
+int gemm_sp_f16_nt_cfg(const void* A_sparse, const void* E, const void* B, void* C, int M, int N, int K,
+                       const gf_sp_cfg* cfg, void* stream);
+int gf_sp_config_count(void);
+int gf_sp_config_get(int i, gf_sp_cfg* out);
+int gf_sp_default_config(int M, int N, int K, gf_sp_cfg* out);
+
 /* Static string naming a status code. */
 const char* gf_status_string(int status);
 

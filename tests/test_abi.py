@@ -185,3 +185,29 @@ def test_config_tables(L):
     bad = gf.GemmCfg()
     assert L.gf_gemm_config_get(-1, ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
     assert L.gf_gemm_config_get(len(cfgs), ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
+
+
+def test_sparse_validation(L):
+    s = NULL
+    c = L.sp24_compress_f16
+    assert c(FAKE, FAKE, FAKE, 4, 24, s) == gf.GF_ERR_INVALID_ARG           # K % 16 != 0
+    assert c(FAKE, FAKE, FAKE, -1, 32, s) == gf.GF_ERR_INVALID_ARG
+    assert c(NULL, FAKE, FAKE, 4, 32, s) == gf.GF_ERR_INVALID_ARG
+    assert c(FAKE, FAKE, ODD, 4, 32, s) == gf.GF_ERR_INVALID_ARG
+    assert c(NULL, NULL, NULL, 0, 32, s) == gf.GF_OK                         # empty
+    assert c(NULL, NULL, NULL, 4, 0, s) == gf.GF_OK
+    g = L.gemm_sp_f16_nt
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 4, 40, s) == gf.GF_ERR_INVALID_ARG   # K % 16 != 0
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 4, 32, s) == gf.GF_ERR_INVALID_ARG
+    assert g(FAKE, NULL, FAKE, FAKE, 4, 4, 32, s) == gf.GF_ERR_INVALID_ARG   # no metadata
+    assert g(FAKE, FAKE, FAKE, ODD, 4, 4, 32, s) == gf.GF_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE, NULL, 0, 4, 32, s) == gf.GF_OK                # empty C
+    assert g(FAKE, FAKE, FAKE, FAKE, 1 << 16, 4, 1 << 15, s) == gf.GF_ERR_INVALID_ARG   # 2^31 elements
+    bad = gf.SpCfg(64, 64, 2, 0)
+    assert L.gemm_sp_f16_nt_cfg(FAKE, FAKE, FAKE, FAKE, 4, 4, 32, ctypes.byref(bad), s) == gf.GF_ERR_UNSUPPORTED
+    cfgs = gf.sp_configs()
+    assert len(cfgs) == L.gf_sp_config_count() >= 4
+    d = gf.sp_default_config(8192, 8192, 8192)
+    assert {**d, "raster": 1} in cfgs
+    out = gf.SpCfg()
+    assert L.gf_sp_config_get(len(cfgs), ctypes.byref(out)) == gf.GF_ERR_INVALID_ARG
