@@ -8,8 +8,9 @@ on the host cores.
 One step is one C = A . B^T call at 8192^3 (fp16 in, fp32 accumulate, fp16
 out) on torch's current stream with A and B already resident in HBM.  The
 headline value is whole-job TFLOP/s over the timed steps (wall clock,
-bracketed by device synchronisation).  The GEMV (N = K = 8192 and 1024) and
-split-K (M = N = 1024, K = 16384) figures are reported in "extra", each
+bracketed by device synchronisation).  The GEMV (N = K = 8192 and 1024),
+split-K (M = N = 1024, K = 16384) and 2:4 sparse GEMM (8192^3, plus the
+compression of its A) figures are reported in "extra", each
 timed with HIP events on the launching stream around batches of
 back-to-back launches; GEMV rotates over enough W
 copies (> 512 MiB) that every call streams W from HBM, not from the 256 MiB
@@ -31,19 +32,30 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+PEAK_F16_SPARSE_TFLOPS = 5000.0   # MI355X fp16 MFMA with 2:4 structured sparsity, published
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# The sources each timed kernel is built from: a traffic record taken on
+# other sources is stale.
+KERNEL_SOURCES = {
+    "gemm_nt_kernel": ("common.hpp", "gemm_kernel.hpp", "gemm_configs.def", "configs.hpp",
+                       "gemm_shard.hip", "api.hip"),
+    "gemv_kernel": ("common.hpp", "gemv_kernel.hpp", "gemv_configs.def", "gemv.hip", "api.hip"),
+    "sp_gemm_kernel": ("common.hpp", "sparse_kernel.hpp", "sparse.hip"),
+    "sp24_compress_kernel": ("common.hpp", "sparse_kernel.hpp", "sparse.hip"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemv_fp16_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hpp", ".hip", ".def")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in sorted(KERNEL_SOURCES[kernel]):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -57,7 +69,7 @@ def measured_traffic(kernel: str, workload: str):
         rec = json.load(open(path)).get(kernel + "|" + workload)
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -264,6 +276,38 @@ def main():
         log("splitk 1024x1024x16384 TFLOP/s: %s" % sk)
         extra["splitk_1024x1024x16384_tflops"] = sk
         del a3, b3, c3, ws
+
+        # ---- 2:4 structured-sparse GEMM at 8192^3: the headline A compressed
+        # (pruned to 2 of every 4 along K) on the GPU, then C = A_sparse . B^T ----
+        Asp, E = gf.sp24_compress_f16(A)
+        t_sp = time_batch(torch, gf.prepare_gemm_sp_f16_nt(Asp, E, B, C), 20, 5)
+        sp_eff = flops / t_sp / 1e12
+        # compression, rotating 3 inputs (384 MiB > the 256 MiB MALL)
+        Acs = [A] + [torch.from_numpy(inputs.uniform_f16((M, K), i, 0)).cuda() for i in (1, 2)]
+        outs = [(torch.empty_like(Asp), torch.empty_like(E)) for _ in range(3)]
+        state = [0]
+
+        def comp(state=state):
+            j = state[0] % 3
+            gf.sp24_compress_f16(Acs[j], *outs[j])
+            state[0] += 1
+
+        t_c = time_batch(torch, comp, 60, 6)
+        c_bytes = 2.0 * M * K + 2.0 * M * K / 2 + 2.0 * M * K / 16
+        extra["sparse24_8192"] = {
+            "gemm_ms": round(t_sp * 1e3, 4),
+            "gemm_tflops_effective": round(sp_eff, 1),
+            "tile": gf.sp_default_config(M, N, K),
+            "roofline": {"bound": "mfma", "achieved": round(sp_eff, 2), "peak": PEAK_F16_SPARSE_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(sp_eff / PEAK_F16_SPARSE_TFLOPS, 4),
+                         "traffic": measured_traffic("sp_gemm_kernel", "8192^3")},
+            "compress_us": round(t_c * 1e6, 2),
+            "compress_GB/s": round(c_bytes / t_c / 1e9, 1),
+            "compress_frac_hbm_peak": round(c_bytes / t_c / 1e9 / PEAK_HBM_GBS, 4),
+        }
+        log("sparse 2:4 8192^3: %.1f effective TFLOP/s (%.3f ms); compress %.1f us, %.1f GB/s" %
+            (sp_eff, t_sp * 1e3, t_c * 1e6, c_bytes / t_c / 1e9))
+        del Asp, E, Acs, outs
 
     if not args.no_cpu:
         import oracle

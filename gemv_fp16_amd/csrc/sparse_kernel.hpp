@@ -29,9 +29,13 @@
 //  * B lane group h then needs, for instruction groups 4h .. 4h+3, the tile's
 //    k ranges [16 s + 8 h, +8) and [32 + 16 s + 8 h, +8): two 16-byte chunks.
 //
-// Staging: A_sparse, B and E of one K tile go global -> LDS with direct-to-LDS
-// loads (16-byte chunks for the operands, 4-byte words for E), one stage per
-// tile in a ring.  The schedule is the dense GEMM's one-wave-per-SIMD form: the
+// Staging: A_sparse and B of one K tile go global -> LDS with direct-to-LDS
+// 16-byte loads, one stage per tile in a ring.  The metadata of two K tiles
+// (16 bytes per row) moves together into a separate three-slot ring with
+// 4-byte direct-to-LDS loads, half a slot per K tile: a load instruction then
+// covers 16 rows instead of 32, which halves the cache lines the address unit
+// has to process for E (the address path, not the MFMAs, sets the pace of
+// this kernel).  The schedule is the dense GEMM's one-wave-per-SIMD form: the
 // tile barrier sits before the last MFMA step, and the next tile's first
 // fragments and half of a later tile's loads go under that step.
 #pragma once
@@ -139,14 +143,19 @@ struct SpCfg {
     static constexpr int KST = BK / 32;                    // sparse MFMA steps per K tile
     static constexpr int CHA = BK / 16, CHB = BK / 8;      // 16-byte chunks per row: A_sparse, B
     static constexpr int EDW = BK / 32;                    // metadata dwords per row per K tile
-    static constexpr int A_BYTES = BM * CHA * 16, B_BYTES = BN * CHB * 16, E_BYTES = BM * EDW * 4;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + E_BYTES;
-    // Loads per thread per K tile: A_sparse chunks, B chunks, E dwords.
+    static constexpr int A_BYTES = BM * CHA * 16, B_BYTES = BN * CHB * 16;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    // Metadata ring: slot j holds K tiles 2j and 2j+1 of every tile row
+    // (16 bytes per row), three slots after the operand stages.
+    static constexpr int E_SLOT = BM * EDW * 4 * 2, E_SLOTS = 3;
+    static constexpr int E_BASE = STAGES * STAGE_BYTES;
+    // Loads per thread per K tile: A_sparse chunks, B chunks, E dwords (half a
+    // metadata slot per K tile).
     static constexpr int LA = BM * CHA / NT, LB = BN * CHB / NT, LE = BM * EDW / NT;
-    static constexpr int LPS = LA + LB + LE;
+    static constexpr int LAB = LA + LB, LPS = LAB + LE;
     static constexpr int EPAD = 8;                         // fp16 pad per epilogue row
     static constexpr int EPI_BYTES = 4 * WTM * (WTN + EPAD) * 2;
-    static constexpr int MAIN_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int MAIN_BYTES = STAGES * STAGE_BYTES + E_SLOTS * E_SLOT;
     static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
     static constexpr bool kValid =
         WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1 && (BM * CHA) % NT == 0 &&
@@ -190,8 +199,9 @@ struct SpLoader {
             row = s / Cfg::CHB;
             kk = ((s % Cfg::CHB) ^ sp_key(row, Cfg::CHB)) * 8;
         } else {
-            row = s / Cfg::EDW;
-            kk = (s % Cfg::EDW) * 32;
+            // dword d = s % 4 of the row's 16 metadata bytes of a two-tile slot
+            row = s / 4;
+            kk = (s % 4) * 32;
         }
     }
 
@@ -206,8 +216,9 @@ struct SpLoader {
                 voff[R] = (uint32_t)min(m0 + row, a.M - 1) * (uint32_t)a.K + (uint32_t)kk;
             else if constexpr (kind<R>() == 1)   // B row: 2K bytes
                 voff[R] = ((uint32_t)min(n0 + row, a.N - 1) * (uint32_t)a.K + (uint32_t)kk) * 2u;
-            else                                 // E row: K/8 bytes
-                voff[R] = (uint32_t)min(m0 + row, a.M - 1) * (uint32_t)(a.K / 8) + (uint32_t)(kk / 8);
+            else                                 // E row: K/8 bytes (rows past M read zeros or
+                                                 // other rows' words; they feed no stored output)
+                voff[R] = (uint32_t)(m0 + row) * (uint32_t)(a.K / 8) + (uint32_t)(kk / 8);
         });
         constexpr int kRawBufferWord3 = 0x00020000;
         ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.Asp, 0, (int)((uint32_t)a.M * (uint32_t)a.K),
@@ -221,14 +232,33 @@ struct SpLoader {
     template <int R>
     __device__ __forceinline__ GF_LDS char* dest(GF_LDS char* stage, int wave) const
     {
-        constexpr int base = kind<R>() == 0 ? 0 : (kind<R>() == 1 ? Cfg::A_BYTES : Cfg::A_BYTES + Cfg::B_BYTES);
-        constexpr int unit = kind<R>() == 2 ? 4 : 16;
-        return stage + base + ((R - first<R>()) * Cfg::NT + wave * kWave) * unit;
+        constexpr int base = kind<R>() == 0 ? 0 : Cfg::A_BYTES;
+        return stage + base + ((R - first<R>()) * Cfg::NT + wave * kWave) * 16;
     }
 
-    // Load R of the K tile at k0, every chunk inside K.
+    // Metadata half h: slot h / 2 (K tiles h - h % 2 and the next) of the
+    // ring, rows [h % 2 * BM / 2, (h % 2 + 1) * BM / 2).  Its LDS base and the
+    // part of the source offset common to all lanes (the slot's 16 bytes of
+    // each row, plus the half's first row).  That part is added to the
+    // per-lane offset, not passed as the scalar offset: the buffer's range
+    // check covers the per-lane offset only, and halves past K (or rows past
+    // M) reach beyond the end of E, where the check turns them into zeros.
+    struct EHalf {
+        GF_LDS char* lds;
+        uint32_t soff;
+    };
+    __device__ __forceinline__ static EHalf e_half(GF_LDS char* smem, int h, int K)
+    {
+        const int j = h >> 1, hp = h & 1;
+        EHalf e;
+        e.lds = smem + Cfg::E_BASE + (j % Cfg::E_SLOTS) * Cfg::E_SLOT + hp * (Cfg::E_SLOT / 2);
+        e.soff = (uint32_t)j * 16u + (uint32_t)(hp * (Cfg::BM / 2)) * (uint32_t)(K / 8);
+        return e;
+    }
+
+    // Load R of the K tile at k0 (every chunk inside K), or of metadata half eh.
     template <int R>
-    __device__ __forceinline__ void issue(GF_LDS char* stage, int k0, int wave) const
+    __device__ __forceinline__ void issue(GF_LDS char* stage, int k0, const EHalf& eh, int wave) const
     {
         if constexpr (kind<R>() == 0)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (GF_LDS void*)dest<R>(stage, wave), 16, voff[R],
@@ -237,19 +267,21 @@ struct SpLoader {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (GF_LDS void*)dest<R>(stage, wave), 16, voff[R],
                                                      (uint32_t)k0 * 2u, 0, 0);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (GF_LDS void*)dest<R>(stage, wave), 4, voff[R],
-                                                     (uint32_t)k0 / 8u, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                re, (GF_LDS void*)(eh.lds + ((R - first<R>()) * Cfg::NT + wave * kWave) * 4), 4,
+                voff[R] + eh.soff, 0, 0, 0);
     }
 
     // The same where the tile may run past K: operand chunks at k >= K read
-    // 16 zero bytes.  Metadata words past K are loaded as they are (the
-    // buffer's range check keeps the last row's reads inside E, and whatever
-    // index they hold selects zeros of both operands).
+    // 16 zero bytes.  Metadata words past K are loaded as they are (words of
+    // the next row, or zeros past the end of E); whatever index they hold
+    // selects zeros of both operands.
     template <int R>
-    __device__ __forceinline__ void issue_masked(const SpArgs& a, GF_LDS char* stage, int k0, int wave) const
+    __device__ __forceinline__ void issue_masked(const SpArgs& a, GF_LDS char* stage, int k0, const EHalf& eh,
+                                                 int wave) const
     {
         if constexpr (kind<R>() == 2) {
-            issue<R>(stage, k0, wave);
+            issue<R>(stage, k0, eh, wave);
         } else {
             int row, kk;
             source<R>(row, kk);
@@ -261,22 +293,31 @@ struct SpLoader {
     }
 
     template <int R0, int R1>
-    __device__ __forceinline__ void issue_range(const SpArgs& a, GF_LDS char* stage, int k0, int wave) const
+    __device__ __forceinline__ void issue_range(const SpArgs& a, GF_LDS char* stage, int k0, const EHalf& eh,
+                                                int wave) const
     {
         if (k0 + Cfg::BK <= a.K) {
-            static_for<R1 - R0>([&](auto j) { issue<R0 + decltype(j)::value>(stage, k0, wave); });
+            static_for<R1 - R0>([&](auto j) { issue<R0 + decltype(j)::value>(stage, k0, eh, wave); });
         } else {
-            static_for<R1 - R0>([&](auto j) { issue_masked<R0 + decltype(j)::value>(a, stage, k0, wave); });
+            static_for<R1 - R0>([&](auto j) { issue_masked<R0 + decltype(j)::value>(a, stage, k0, eh, wave); });
         }
+    }
+
+    // Metadata half h on its own.
+    __device__ __forceinline__ void issue_e(GF_LDS char* smem, int h, int K, int wave) const
+    {
+        const EHalf eh = e_half(smem, h, K);
+        static_for<Cfg::LE>([&](auto j) { issue<Cfg::LAB + decltype(j)::value>(nullptr, 0, eh, wave); });
     }
 };
 
 // Register-staged loads of one K tile for operands without the alignment the
 // direct-to-LDS path needs: element loads with bounds checks, zero fill.
 template <class Cfg>
-__device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char* stage, int m0, int n0,
-                                                    int k0, int tid)
+__device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char* stage, GF_LDS char* smem,
+                                                    int m0, int n0, int t, int tid)
 {
+    const int k0 = t * Cfg::BK;
     // A_sparse chunks: 8 kept values = 16 logical k
     for (int s = tid; s < Cfg::BM * Cfg::CHA; s += Cfg::NT) {
         const int row = s / Cfg::CHA, kk = ((s % Cfg::CHA) ^ sp_key(row, Cfg::CHA)) * 16;
@@ -304,6 +345,7 @@ __device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char
                    v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
         *(GF_LDS u32x4*)(stage + Cfg::A_BYTES + s * 16) = w;
     }
+    GF_LDS char* eslot = smem + Cfg::E_BASE + ((t / 2) % Cfg::E_SLOTS) * Cfg::E_SLOT + (t % 2) * 8;
     for (int s = tid; s < Cfg::BM * Cfg::EDW; s += Cfg::NT) {
         const int row = s / Cfg::EDW, gr = m0 + row;
         const int w0 = (k0 + (s % Cfg::EDW) * 32) / 16;   // first metadata word
@@ -312,7 +354,7 @@ __device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char
             if (w0 < a.K / 16) d = a.E[(size_t)gr * (a.K / 16) + w0];
             if (w0 + 1 < a.K / 16) d |= (uint32_t)a.E[(size_t)gr * (a.K / 16) + w0 + 1] << 16;
         }
-        *(GF_LDS uint32_t*)(stage + Cfg::A_BYTES + Cfg::B_BYTES + s * 4) = d;
+        *(GF_LDS uint32_t*)(eslot + row * 16 + (s % Cfg::EDW) * 4) = d;
     }
 }
 
@@ -322,7 +364,7 @@ __device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char
 
 template <class Cfg>
 struct SpReader {
-    int oa, ob, oe;   // lane byte offsets of fragment 0 in the A, B and E regions
+    int oa, ob, oe;   // lane byte offsets of fragment 0 in the A and B regions and in a metadata slot
     int ka, kb;       // swizzle keys (the same for every fragment of the lane)
     int g;            // lane group
 
@@ -335,7 +377,7 @@ struct SpReader {
         ka = sp_key(ra, Cfg::CHA);
         ob = Cfg::A_BYTES + rb * Cfg::CHB * 16;
         kb = sp_key(rb, Cfg::CHB);
-        oe = Cfg::A_BYTES + Cfg::B_BYTES + ra * Cfg::EDW * 4 + g * 4;
+        oe = ra * 16 + g * 4;
     }
     template <int F, int S>
     __device__ __forceinline__ half8 a(const GF_LDS char* st) const
@@ -350,11 +392,16 @@ struct SpReader {
         const half8 hi = *(const GF_LDS half8*)(p + (((2 * (Cfg::KST + S) + g) ^ kb) * 16));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     }
-    // Metadata words 2g (step 0, low half) and 2g + 1 (step 1, high half).
+    // Metadata words 2g (step 0, low half) and 2g + 1 (step 1, high half) of
+    // K tile u: `et` is the ring address of u's 8 bytes in row 0.
     template <int F>
-    __device__ __forceinline__ uint32_t e(const GF_LDS char* st) const
+    __device__ __forceinline__ uint32_t e(const GF_LDS char* et) const
     {
-        return *(const GF_LDS uint32_t*)(st + oe + F * 32 * Cfg::EDW * 4);
+        return *(const GF_LDS uint32_t*)(et + oe + F * 32 * 16);
+    }
+    __device__ __forceinline__ static const GF_LDS char* e_tile(const GF_LDS char* smem, int u)
+    {
+        return smem + Cfg::E_BASE + ((u / 2) % Cfg::E_SLOTS) * Cfg::E_SLOT + (u % 2) * 8;
     }
 };
 
@@ -401,21 +448,23 @@ struct SpStepPlan {
 
 // One MFMA step: the FM x FN sparse MFMAs on fragments `cur` with index
 // words `idx`, with two streams woven in: the fragment reads of step RS (from
-// stage rst; with that tile's metadata when RS == 0) into `nxt` / `enxt`, and
-// the direct-to-LDS loads R0 .. R1-1 of the tile at lk0 into stage lst.
+// stage rst; with that tile's metadata from ret when RS == 0) into `nxt` /
+// `enxt`, and the direct-to-LDS loads R0 .. R1-1 of the tile at lk0 into stage
+// lst (metadata loads: half eh).
 template <class Cfg, int RS, int R0, int R1>
 __device__ __forceinline__ void sp_step(floatx16 (&acc)[Cfg::FM][Cfg::FN], const SpFrags<Cfg>& cur,
                                         const uint32_t (&idx)[Cfg::FM], SpFrags<Cfg>& nxt,
                                         uint32_t (&enxt)[Cfg::FM], const SpReader<Cfg>& rd,
-                                        const GF_LDS char* rst, const SpLoader<Cfg>& ld,
-                                        GF_LDS char* lst, int lk0, int wave)
+                                        const GF_LDS char* rst, const GF_LDS char* ret,
+                                        const SpLoader<Cfg>& ld, GF_LDS char* lst, int lk0,
+                                        const typename SpLoader<Cfg>::EHalf& eh, int wave)
 {
     typedef SpStepPlan<Cfg, RS, R0, R1> P;
     auto read = [&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
         constexpr int f = P::frag(j);
         if constexpr (j < P::NE)
-            enxt[f] = rd.template e<f>(rst);
+            enxt[f] = rd.template e<f>(ret);
         else if constexpr (P::is_b(j))
             nxt.b[f] = rd.template b<f, RS>(rst);
         else
@@ -429,11 +478,11 @@ __device__ __forceinline__ void sp_step(floatx16 (&acc)[Cfg::FM][Cfg::FN], const
             constexpr int j = i * P::RPM + decltype(r_c)::value;
             if constexpr (j < P::ND) read(std::integral_constant<int, j>{});
         });
-        if constexpr (P::load_at(i) >= 0) ld.template issue<P::load_at(i)>(lst, lk0, wave);
+        if constexpr (P::load_at(i) >= 0) ld.template issue<P::load_at(i)>(lst, lk0, eh, wave);
     });
     static_for<P::NL>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
-        if constexpr (j >= P::NLS) ld.template issue<R0 + j>(lst, lk0, wave);
+        if constexpr (j >= P::NLS) ld.template issue<R0 + j>(lst, lk0, eh, wave);
     });
     static_for<P::NM>([&](auto i_c) {
         constexpr int i = decltype(i_c)::value;
@@ -498,19 +547,39 @@ __global__ __launch_bounds__(256) void sp_gemm_kernel(SpArgs a)
         // the first half of tile t + S's loads into stage t % S; the second
         // half goes under tile t + 1's first step.  Loads are issued for every
         // tile index, also past K (masked ones read zeros), so the count in
-        // flight, and with it every wait, is the same in every iteration.
+        // flight is the same in every iteration.
+        // Metadata moves in halves of a two-tile ring slot: iteration t issues
+        // half t + 4 (with the second half of the tile loads, so it has landed
+        // by B(t + 1)); slot (t + 4) / 2 last held K tiles t - 2 and t - 1 (or
+        // t - 3 and t - 2), whose metadata every wave read before B(t - 1).
+        // The prologue loads halves 0 .. 3.  Every vmcnt wait below counts only
+        // the operand loads of the tiles behind the one it waits for and so
+        // may wait for a little more than needed, never less.
         constexpr int S = Cfg::STAGES, H = Cfg::LPS / 2;
+        static_assert(H <= Cfg::LAB, "metadata loads must fall in the second half of a tile's loads");
+        typedef typename SpLoader<Cfg>::EHalf EHalf;
         SpLoader<Cfg> ld;
         ld.init(a, m0, n0, tid);
+        const EHalf no_e = {nullptr, 0u};
         if (nk > 0) {
+            ld.issue_e(smem, 0, a.K, wave);
+            ld.issue_e(smem, 1, a.K, wave);
 #pragma unroll
-            for (int t = 0; t < S - 1; ++t)
-                ld.template issue_range<0, Cfg::LPS>(a, stage_ptr(t), t * Cfg::BK, wave);
+            for (int t = 0; t < S - 1; ++t) {
+                if (t == S - 2) {
+                    ld.issue_e(smem, 2, a.K, wave);
+                    ld.issue_e(smem, 3, a.K, wave);
+                }
+                ld.template issue_range<0, Cfg::LAB>(a, stage_ptr(t), t * Cfg::BK, no_e, wave);
+            }
         }
-        wait_vmcnt<Cfg::LPS * (S - 2)>();        // tile 0 landed
+        wait_vmcnt<Cfg::LAB * (S - 2)>();        // tile 0 and metadata halves 0, 1 landed
         lds_barrier();
-        if (nk > 0) ld.template issue_range<0, H>(a, stage_ptr(S - 1), (S - 1) * Cfg::BK, wave);
-        static_for<Cfg::FM>([&](auto f) { e[f] = rd.template e<decltype(f)::value>(stage_ptr(0)); });
+        if (nk > 0) ld.template issue_range<0, H>(a, stage_ptr(S - 1), (S - 1) * Cfg::BK, no_e, wave);
+        {
+            const GF_LDS char* et = SpReader<Cfg>::e_tile(smem, 0);
+            static_for<Cfg::FM>([&](auto f) { e[f] = rd.template e<decltype(f)::value>(et); });
+        }
         static_for<Cfg::FM>([&](auto f) { f0.a[f] = rd.template a<decltype(f)::value, 0>(stage_ptr(0)); });
         static_for<Cfg::FN>([&](auto f) { f0.b[f] = rd.template b<decltype(f)::value, 0>(stage_ptr(0)); });
         // Steady state: tiles t + S - 1 and t + S lie wholly inside K.
@@ -519,35 +588,39 @@ __global__ __launch_bounds__(256) void sp_gemm_kernel(SpArgs a)
         int t = 0;
         for (; t < steady_end; ++t) {
             const int s0 = t % S, s1 = (t + 1) % S, sl = (t + S - 1) % S;
+            const EHalf eh = SpLoader<Cfg>::e_half(smem, t + 4, a.K);
 #pragma unroll
             for (int f = 0; f < Cfg::FM; ++f) { lo[f] = e[f] & 0xffffu; hi[f] = e[f] >> 16; }
-            sp_step<Cfg, 1, H, Cfg::LPS>(acc, f0, lo, f1, e, rd, stage_ptr(s0), ld, stage_ptr(sl),
-                                         (t + S - 1) * Cfg::BK, wave);
+            sp_step<Cfg, 1, H, Cfg::LPS>(acc, f0, lo, f1, e, rd, stage_ptr(s0), nullptr, ld, stage_ptr(sl),
+                                         (t + S - 1) * Cfg::BK, eh, wave);
             wait_vmcnt<Cfg::LPS * (S - 2)>();    // tile t + 1 landed
             lds_barrier();                        // B(t)
-            sp_step<Cfg, 0, 0, H>(acc, f1, hi, f0, e, rd, stage_ptr(s1), ld, stage_ptr(s0),
-                                  (t + S) * Cfg::BK, wave);
+            sp_step<Cfg, 0, 0, H>(acc, f1, hi, f0, e, rd, stage_ptr(s1), SpReader<Cfg>::e_tile(smem, t + 1), ld,
+                                  stage_ptr(s0), (t + S) * Cfg::BK, no_e, wave);
         }
         for (; t < nk; ++t) {
             const int s0 = t % S, s1 = (t + 1) % S, sl = (t + S - 1) % S;
-            ld.template issue_range<H, Cfg::LPS>(a, stage_ptr(sl), (t + S - 1) * Cfg::BK, wave);
+            ld.template issue_range<H, Cfg::LPS>(a, stage_ptr(sl), (t + S - 1) * Cfg::BK,
+                                                 SpLoader<Cfg>::e_half(smem, t + 4, a.K), wave);
 #pragma unroll
             for (int f = 0; f < Cfg::FM; ++f) { lo[f] = e[f] & 0xffffu; hi[f] = e[f] >> 16; }
-            sp_step<Cfg, 1, 0, 0>(acc, f0, lo, f1, e, rd, stage_ptr(s0), ld, nullptr, 0, wave);
+            sp_step<Cfg, 1, 0, 0>(acc, f0, lo, f1, e, rd, stage_ptr(s0), nullptr, ld, nullptr, 0, no_e, wave);
             wait_vmcnt<Cfg::LPS * (S - 2)>();
             lds_barrier();
-            ld.template issue_range<0, H>(a, stage_ptr(s0), (t + S) * Cfg::BK, wave);
+            ld.template issue_range<0, H>(a, stage_ptr(s0), (t + S) * Cfg::BK, no_e, wave);
             // After the last tile these reads fetch stale data that no MFMA uses.
-            sp_step<Cfg, 0, 0, 0>(acc, f1, hi, f0, e, rd, stage_ptr(s1), ld, nullptr, 0, wave);
+            sp_step<Cfg, 0, 0, 0>(acc, f1, hi, f0, e, rd, stage_ptr(s1), SpReader<Cfg>::e_tile(smem, t + 1), ld,
+                                  nullptr, 0, no_e, wave);
         }
         wait_vmcnt<0>();                          // no load may land after the epilogue starts
     } else {
         for (int t = 0; t < nk; ++t) {
             lds_barrier();                        // everyone is done with the buffer
-            sp_load_tile_masked<Cfg>(a, stage_ptr(0), m0, n0, t * Cfg::BK, tid);
+            sp_load_tile_masked<Cfg>(a, stage_ptr(0), smem, m0, n0, t, tid);
             lds_barrier();
             const GF_LDS char* st = stage_ptr(0);
-            static_for<Cfg::FM>([&](auto f) { e[f] = rd.template e<decltype(f)::value>(st); });
+            const GF_LDS char* et = SpReader<Cfg>::e_tile(smem, t);
+            static_for<Cfg::FM>([&](auto f) { e[f] = rd.template e<decltype(f)::value>(et); });
             static_for<Cfg::FM>([&](auto f) { f0.a[f] = rd.template a<decltype(f)::value, 0>(st); });
             static_for<Cfg::FN>([&](auto f) { f0.b[f] = rd.template b<decltype(f)::value, 0>(st); });
             static_for<Cfg::FM>([&](auto f) { f1.a[f] = rd.template a<decltype(f)::value, 1>(st); });

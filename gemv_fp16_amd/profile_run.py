@@ -8,6 +8,9 @@ Ops (inputs are the seeded uniform[-1,1] fp16 workloads):
           stores B as K x N (and A as K x M) and runs gemm_f16 on them
   gemv    y = W . x at N = K = 8192, rotating 5 W copies (640 MiB)
   splitk  M = N = 1024, K = 16384, split 8: fp32 atomic, fp32 two-pass, fp16 two-pass
+  sparse  2:4 sparse C = decompress(A_sparse, E) . B^T at M = N = K = 8192 (A compressed
+          once on the GPU from a dense uniform A; default tile config)
+  compress  2:4 compression of an 8192 x 8192 A, rotating 3 copies (384 MiB)
   copy    torch copy of a 512 MiB buffer: a plain copy kernel of known size,
           the calibration for the HBM byte counters
 """
@@ -24,7 +27,7 @@ if ROOT not in sys.path:
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("op", choices=["gemm", "gemv", "splitk", "copy"])
+    ap.add_argument("op", choices=["gemm", "gemv", "splitk", "sparse", "compress", "copy"])
     ap.add_argument("--iters", type=int, default=10)
     ap.add_argument("--m", type=int, default=8192)
     ap.add_argument("--n", type=int, default=8192)
@@ -77,6 +80,21 @@ def main(argv=None):
             gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_ATOMIC, ws)
             gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_TWOPASS, ws)
             gf.gemm_f16_nt_splitk_f16(A, B, C16, 8, ws)
+    elif a.op == "sparse":
+        A = torch.from_numpy(inputs.uniform_f16((a.m, a.k), 0, 0)).cuda()
+        B = torch.from_numpy(inputs.uniform_f16((a.n, a.k), 0, 1)).cuda()
+        Asp, E = gf.sp24_compress_f16(A)
+        del A
+        C = torch.empty((a.m, a.n), dtype=torch.float16, device="cuda")
+        call = gf.prepare_gemm_sp_f16_nt(Asp, E, B, C)
+        for _ in range(a.iters):
+            call()
+    elif a.op == "compress":
+        As = [torch.from_numpy(inputs.uniform_f16((a.m, a.k), i, 0)).cuda() for i in range(3)]
+        outs = [(torch.empty((a.m, a.k // 2), dtype=torch.float16, device="cuda"),
+                 torch.empty((a.m, a.k // 16), dtype=torch.int16, device="cuda")) for _ in range(3)]
+        for i in range(a.iters):
+            gf.sp24_compress_f16(As[i % 3], *outs[i % 3])
     else:
         src = torch.ones(128 << 20, dtype=torch.float32, device="cuda")   # 512 MiB
         dst = torch.empty_like(src)

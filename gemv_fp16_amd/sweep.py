@@ -2,6 +2,7 @@
 
     python -m gemv_fp16_amd.sweep gemm --m 8192 --n 8192 --k 8192 --out sweep.json
     python -m gemv_fp16_amd.sweep gemv --n 8192 --k 8192 --out sweep_gemv.json
+    python -m gemv_fp16_amd.sweep sparse --m 8192 --n 8192 --k 8192 --out sweep_sparse.json
 
 A plain host loop in the spirit of the autotune grid on the TileLang FP16
 matmul benchmark page (section 2.1: block_M, block_N, block_K, pipeline
@@ -142,6 +143,45 @@ def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
             _emit(out, rec)
 
 
+def sweep_sparse(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
+    """The 2:4 sparse product's tile configs: A uniform (dense, pruned by the
+    compression) and 2:4 integer inputs for the bit-exact gate."""
+    import torch
+    import gemv_fp16_amd as gf
+    import inputs
+    A = torch.from_numpy(inputs.uniform_f16((M, K), 0, 0)).cuda()
+    B = torch.from_numpy(inputs.uniform_f16((N, K), 0, 1)).cuda()
+    Ai = torch.from_numpy(inputs.sparse24("integer", (M, K), 0, 0)).cuda()
+    Bi = torch.from_numpy(inputs.integer_f16((N, K), 0, 1)).cuda()
+    Asp, E = gf.sp24_compress_f16(A)
+    Aspi, Ei = gf.sp24_compress_f16(Ai)
+    del A, Ai
+    C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ref_u = _u16(gf.gemm_sp_f16_nt(Asp, E, B))
+    ref_i = _u16(gf.gemm_sp_f16_nt(Aspi, Ei, Bi))
+    default = gf.sp_default_config(M, N, K)
+    seen = _done(out)
+    flops = 2.0 * M * N * K
+    shape = [M, N, K]
+    for cfg in gf.sp_configs():
+        for raster in rasters:
+            c = dict(cfg, raster=raster)
+            key = json.dumps(["sparse", shape, c], sort_keys=True)
+            if key in seen:
+                continue
+            rec = {"op": "sparse", "shape": shape, "config": c}
+            ci = _u16(gf.gemm_sp_f16_nt(Aspi, Ei, Bi, cfg=c))
+            cu = _u16(gf.gemm_sp_f16_nt(Asp, E, B, cfg=c))
+            if not np.array_equal(ci, ref_i) or not _close(cu, ref_u):
+                rec["status"] = "mismatch"
+                _emit(out, rec)
+                continue
+            med, mn = _time_batch(torch, gf.prepare_gemm_sp_f16_nt(Asp, E, B, C, cfg=c), reps, warmup, trials)
+            rec.update(status="ok", median_ms=round(med * 1e3, 5), min_ms=round(mn * 1e3, 5),
+                       tflops_effective=round(flops / med / 1e12, 2), is_default=(c == default))
+            _emit(out, rec)
+
+
 def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,)):
     import torch
     import gemv_fp16_amd as gf
@@ -186,7 +226,7 @@ def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,)):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("op", choices=["gemm", "gemv"])
+    ap.add_argument("op", choices=["gemm", "gemv", "sparse"])
     ap.add_argument("--m", type=int, default=8192)
     ap.add_argument("--n", type=int, default=8192)
     ap.add_argument("--k", type=int, default=8192)
@@ -201,6 +241,8 @@ def main(argv=None):
     t = time.time()
     if a.op == "gemm":
         sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster), a.only)
+    elif a.op == "sparse":
+        sweep_sparse(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster))
     else:
         sweep_gemv(a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.blocks))
     print("sweep done in %.1f s" % (time.time() - t), file=sys.stderr, flush=True)
