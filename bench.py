@@ -99,7 +99,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=3072,
+    ap.add_argument("--cpu-rows", type=int, default=6144,
                     help="rows of the 8192^3 product the CPU oracle computes")
     ap.add_argument("--no-extra", action="store_true", help="headline GEMM only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
