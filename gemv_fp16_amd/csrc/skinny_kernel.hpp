@@ -127,9 +127,10 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
 // The direct form above reads 16 rows x 64 bytes per load instruction.  Here
 // every load instruction moves 1 KiB of ONE row (512 consecutive k) straight
 // into LDS, the pattern the GEMV streams at: per 512-k chunk a workgroup
-// loads its 16 * NB rows of B and the 16 rows of A (rows past M clamped to a
-// valid row: an MFMA row of A only reaches the same row of the result, and
-// those rows are not stored).  Chunk c of a row sits at 16-byte slot
+// loads its 16 * NB rows of B and MA rows of A, MA = 4, 8 or 16, the fewest
+// that cover M (rows past M are clamped to a valid row; an MFMA row of A only
+// reaches the same row of the result, and those rows are not stored, so the
+// fragment reads of the 16 - MA rows that are not staged re-read row MA - 1).  Chunk c of a row sits at 16-byte slot
 // c ^ (row % 16), so the 16 lanes that read one fragment (16 rows, same k)
 // hit 16 different bank groups.  S chunks ring through LDS; every wave
 // issues the same number of loads per chunk, so each wait is a constant.
@@ -137,23 +138,24 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
 // are summed at the end as in the direct form.
 constexpr int kSkinnyKc = 512;                  // k per chunk (1 KiB per row)
 
-template <int NB, int S, int W>
+template <int NB, int S, int W, int MA = 16>
 struct SkinnyLdsCfg {
-    static constexpr int ROWS = 16 * (NB + 1);          // B rows, then 16 A rows
+    static constexpr int ROWS = 16 * NB + MA;           // B rows, then MA A rows
     static constexpr int CHUNK_BYTES = ROWS * kSkinnyKc * 2;
     static constexpr int LW = ROWS / W;                 // loads per wave per chunk
     static constexpr int LDS_BYTES = S * CHUNK_BYTES;
     static constexpr bool kValid =
-        W <= 16 && ROWS % W == 0 && LDS_BYTES <= 160 * 1024 && S >= 2 && LW * S < 64;
+        W <= 16 && ROWS % W == 0 && LDS_BYTES <= 160 * 1024 && S >= 2 && LW * S < 64 &&
+        (MA == 4 || MA == 8 || MA == 16);
 };
 
-template <int NB, int S, int W>
+template <int NB, int S, int W, int MA>
 __global__ __launch_bounds__(W * kWave) void skinny_lds_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int M,
     int N, int K)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    typedef SkinnyLdsCfg<NB, S, W> Cf;
+    typedef SkinnyLdsCfg<NB, S, W, MA> Cf;
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     GF_LDS char* smem = (GF_LDS char*)smem_raw;
     const int lane = threadIdx.x % kWave;
@@ -184,8 +186,9 @@ __global__ __launch_bounds__(W * kWave) void skinny_lds_kernel(
     // lane l reads row 16 * blk + l % 16, 16-byte chunk 4 * ks + l / 16.
     const int r16 = lane % 16, kq = lane / 16;
     auto frag = [&](int slot, int blk, int ks) {
-        const int row = 16 * blk + r16;
-        const int c = (4 * ks + kq) ^ r16;
+        const int rr = blk == NB ? min(r16, MA - 1) : r16;   // row within the 16-row block
+        const int row = 16 * blk + rr;
+        const int c = (4 * ks + kq) ^ rr;
         return *(const GF_LDS half8*)(smem + slot * Cf::CHUNK_BYTES + row * (kSkinnyKc * 2) + c * 16);
     };
     floatx4 acc[NB];
@@ -231,13 +234,13 @@ __global__ __launch_bounds__(W * kWave) void skinny_lds_kernel(
 #endif
 }
 
-template <int NB, int S, int W>
-hipError_t launch_skinny_lds(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
-                             hipStream_t stream)
+template <int NB, int S, int W, int MA>
+hipError_t launch_skinny_lds_ma(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                                hipStream_t stream)
 {
-    typedef SkinnyLdsCfg<NB, S, W> Cf;
+    typedef SkinnyLdsCfg<NB, S, W, MA> Cf;
     static_assert(Cf::kValid, "skinny LDS config");
-    auto kern = skinny_lds_kernel<NB, S, W>;
+    auto kern = skinny_lds_kernel<NB, S, W, MA>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -248,6 +251,20 @@ hipError_t launch_skinny_lds(const uint16_t* A, const uint16_t* B, uint16_t* C, 
     const int grid = ceil_div(N, NB * 16);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(W * kWave), Cf::LDS_BYTES, stream, A, B, C, M, N, K);
     return hipGetLastError();
+}
+
+// The LDS-staged launch for M rows of A: the fewest staged A rows (4, 8 or
+// 16) that cover M and divide evenly over the waves.
+template <int NB, int S, int W>
+hipError_t launch_skinny_lds(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                             hipStream_t stream)
+{
+    static_assert(SkinnyLdsCfg<NB, S, W, 16>::kValid, "skinny LDS config");
+    if constexpr (SkinnyLdsCfg<NB, S, W, 4>::kValid)
+        if (M <= 4) return launch_skinny_lds_ma<NB, S, W, 4>(A, B, C, M, N, K, stream);
+    if constexpr (SkinnyLdsCfg<NB, S, W, 8>::kValid)
+        if (M <= 8) return launch_skinny_lds_ma<NB, S, W, 8>(A, B, C, M, N, K, stream);
+    return launch_skinny_lds_ma<NB, S, W, 16>(A, B, C, M, N, K, stream);
 }
 
 }  // namespace gf

@@ -252,7 +252,7 @@ def test_skinny(M, N, K):
     check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny %dx%dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 520, 1536), (3, 1000, 512), (9, 77, 2048)])
+@pytest.mark.parametrize("M,N,K", [(16, 520, 1536), (3, 1000, 512), (9, 77, 2048), (6, 300, 1024)])
 def test_skinny_every_config(M, N, K):
     """Every launch shape, direct and LDS-staged (K a multiple of 512)."""
     A, B = operands("integer", M, N, K, seed=6)
