@@ -53,16 +53,18 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched
 }
 
 // The tile config for a shape: the largest tile that still gives every CU
-// at least one workgroup.  For the large case the offline sweep at
-// M = N = K = 8192 ranks 256 x 256 x 64 / 2 stages first; in side-by-side
-// runs on one GPU the one-wave-per-SIMD schedule (4 waves) matched or beat
-// the 8-wave interleaved schedule by up to 4 %, and plain tile order beat
-// the grouped order.
-gf_gemm_cfg default_gemm_cfg(int M, int N, int /*K*/)
+// at least one workgroup.  For the large case the offline sweeps at
+// M = N = 8192 rank 256 x 256 x 64 / 2 stages with the one-wave-per-SIMD
+// schedule first at K = 1024, 4096 and 8192 (in side-by-side runs it matched
+// or beat the 8-wave interleaved schedule by up to 4 %).  The grouped,
+// XCD-aware tile order is 5 % ahead at K = 1024, where each tile's short K
+// loop leaves operand re-reads less time to hide, ties at K = 4096, and is
+// within noise of plain order at K = 8192, where plain order is kept.
+gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
 {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 256, 0, 2);
+    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 256, K <= 4096 ? 1 : 0, 2);
     if (t128 >= 128) return make_cfg(128, 128, 64, 2, 256, 0);
     return make_cfg(64, 64, 64, 2, 256, 0);
 }
