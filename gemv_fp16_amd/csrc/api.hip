@@ -296,14 +296,23 @@ int find_skinny(const gf_skinny_cfg& c)
 }
 
 // Launch shape of the skinny GEMM, from the offline sweep at N = K = 8192:
-// up to 4 rows the direct form (one 16-row block of B per workgroup, 4-step
-// batches) streams fastest; from 5 rows the extra A traffic of the direct
-// form dominates and the LDS-staged form (three blocks of B share each A
-// chunk, two chunks in flight) is ahead, when K is a multiple of its chunk.
+// up to 8 rows the vector form (one row of B per wave, the GEMV's access
+// pattern) streams fastest where it fits: 5.8 TB/s at M = 2 (8 chunks per
+// row in flight), 5.4 at M = 4 and 4.8 at M = 8 (4 chunks), against 4.8,
+// 4.6 and 4.6 for the best MFMA form.  Elsewhere, up to 4 rows the direct
+// form (one 16-row block of B per workgroup, 4-step batches); from 5 rows
+// the LDS-staged form (three blocks of B share each A chunk, two chunks in
+// flight), when K is a multiple of its chunk.
 gf_skinny_cfg default_skinny_cfg(int M, int /*N*/, int K)
 {
     gf_skinny_cfg c;
     c.waves = 8;
+    if (M <= kSkinnyVecMaxM && skinny_vec_fits(M, K, M <= 2 ? 8 : 4)) {
+        c.blocks = 1;
+        c.unroll = M <= 2 ? 8 : 4;
+        c.stages = 1;
+        return c;
+    }
     if (M > 4 && K > 0 && K % kSkinnyKc == 0) {
         c.blocks = 3;
         c.unroll = 0;
@@ -326,7 +335,9 @@ int skinny_impl(const void* A, const void* B, void* C, int M, int N, int K, cons
 {
     const int idx = find_skinny(cfg);
     if (idx < 0 || !g_skinny_table[idx]) return GF_ERR_UNSUPPORTED;
-    if (kSkinnyConfigs[idx].stages > 0 && (K % kSkinnyKc != 0 || K == 0)) return GF_ERR_UNSUPPORTED;
+    const SkinnyDesc& d = kSkinnyConfigs[idx];
+    if (d.stages == 1 && !skinny_vec_fits(M, K, d.unroll)) return GF_ERR_UNSUPPORTED;
+    if (d.stages >= 2 && (K % kSkinnyKc != 0 || K == 0)) return GF_ERR_UNSUPPORTED;
     return launch_status(g_skinny_table[idx](static_cast<const uint16_t*>(A),
                                              static_cast<const uint16_t*>(B),
                                              static_cast<uint16_t*>(C), M, N, K, stream));

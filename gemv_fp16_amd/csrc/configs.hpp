@@ -28,10 +28,12 @@ constexpr GemvDesc kGemvConfigs[] = {
 };
 constexpr int kNumGemv = sizeof(kGemvConfigs) / sizeof(kGemvConfigs[0]);
 
-// Skinny GEMM launch shapes: 16-row blocks of B per workgroup, waves per
-// workgroup, and either stages = 0 (direct form: unroll = k-steps per
-// register batch, two batches in flight per wave) or stages >= 2 (LDS-staged
-// form with that many 512-k chunks in the ring; unroll unused, 0).
+// Skinny GEMM launch shapes.  stages = 0: direct form (blocks = 16-row
+// blocks of B per workgroup, unroll = k-steps per register batch, two batches
+// in flight per wave).  stages >= 2: LDS-staged form (blocks as above, that
+// many 512-k chunks in the ring, unroll unused, 0).  stages = 1: vector form
+// for M <= 8 (blocks = rows of B per wave, unroll = 16-byte chunks per row
+// and lane per step).  waves: waves per workgroup.
 struct SkinnyDesc {
     int blocks, unroll, waves, stages;
 };
@@ -41,6 +43,8 @@ constexpr SkinnyDesc kSkinnyConfigs[] = {
     {1, 1, 16, 0}, {1, 2, 16, 0}, {1, 4, 16, 0}, {2, 1, 16, 0}, {2, 2, 16, 0}, {4, 1, 8, 0},
     {1, 0, 8, 2},  {1, 0, 8, 3},  {1, 0, 8, 4},  {1, 0, 4, 4},  {1, 0, 16, 4}, {2, 0, 8, 2},
     {2, 0, 8, 3},  {2, 0, 4, 3},  {3, 0, 8, 2},  {1, 0, 4, 3},
+    {1, 4, 8, 1},  {2, 2, 8, 1},  {2, 4, 8, 1},  {4, 2, 8, 1},  {2, 2, 16, 1}, {4, 1, 8, 1},
+    {1, 8, 8, 1},  {1, 4, 16, 1}, {1, 4, 4, 1},  {1, 2, 8, 1},  {1, 8, 4, 1},
 };
 constexpr int kNumSkinny = sizeof(kSkinnyConfigs) / sizeof(kSkinnyConfigs[0]);
 

@@ -16,6 +16,8 @@ void register_from()
         constexpr SkinnyDesc d = kSkinnyConfigs[I];
         if constexpr (d.stages == 0)
             g_skinny_table[I] = &launch_skinny<d.blocks, d.unroll, d.waves>;
+        else if constexpr (d.stages == 1)
+            g_skinny_table[I] = &launch_skinny_vec<d.blocks, d.unroll, d.waves>;
         else if constexpr (SkinnyLdsCfg<d.blocks, d.stages, d.waves>::kValid)
             g_skinny_table[I] = &launch_skinny_lds<d.blocks, d.stages, d.waves>;
         register_from<I + 1>();

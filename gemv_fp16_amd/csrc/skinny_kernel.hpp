@@ -19,6 +19,7 @@
 // Requires K % 8 == 0 and 16-byte aligned A and B (the 16-byte loads).
 #pragma once
 #include "common.hpp"
+#include "gemv_kernel.hpp"
 
 namespace gf {
 
@@ -267,4 +268,147 @@ hipError_t launch_skinny_lds(const uint16_t* A, const uint16_t* B, uint16_t* C, 
     return launch_skinny_lds_ma<NB, S, W, 16>(A, B, C, M, N, K, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Vector form (M <= 8): the GEMV's access pattern, M vectors at once
+// ---------------------------------------------------------------------------
+//
+// Both MFMA forms above pay for the matrix cores' operand layout: the direct
+// form reads 16 rows x 64 bytes of B per load instruction, the LDS form a
+// barrier per 512-k chunk.  For a handful of rows of A, B is streamed here
+// exactly as the GEMV streams W: a wave owns ROWS consecutive rows of B, its
+// 64 lanes split K (lane l takes the 16-byte chunks l, l + 64, ... of each
+// row, UNROLL per row per step, the next step's loads in flight while this
+// one is multiplied), non-temporal 128-bit loads straight into registers.
+// The M <= MV rows of A are staged once per workgroup in LDS (MV * K * 2
+// bytes, rows past M zero), after the wave's first loads of B are issued; each
+// chunk of B meets the M matching chunks of A in v_dot2_f32_f16 (fp32
+// accumulation).  When a wave finishes its rows it folds each of its ROWS x MV
+// sums across the lanes with DPP and writes the fp16 results.  One workgroup
+// per CU walks the row groups grid-stride, so A is staged once per CU.
+// Requires K % (512 * UNROLL) == 0 and MV * K * 2 <= 160 KiB.
+template <int MV, int ROWS, int UNROLL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* __restrict__ A,
+                                                                const uint16_t* __restrict__ B,
+                                                                uint16_t* __restrict__ C, int M, int N, int K)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(ROWS * MV <= kWave, "one lane stores each result");
+    extern __shared__ __attribute__((aligned(16))) char vec_smem[];
+    half8* as = (half8*)vec_smem;                      // [MV][K / 8]
+    constexpr int STEP = kWave * UNROLL;               // chunks of a row per step
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int nch = K / 8;
+    const int spg = nch / STEP;                        // steps per row group
+    const int groups = ceil_div(N, ROWS);
+    const int g0 = blockIdx.x * WAVES + wave, gstride = gridDim.x * WAVES;
+    const int my_groups = g0 < groups ? (groups - g0 + gstride - 1) / gstride : 0;
+    const int ntasks = my_groups * spg;
+    const half8* Bv = (const half8*)B;
+
+    half8 buf[2][ROWS][UNROLL];
+    auto load = [&](int i, half8 (&b)[ROWS][UNROLL]) __attribute__((always_inline)) {
+        const int g = g0 + (i / spg) * gstride;
+        const int c0 = (i % spg) * STEP + lane;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const half8* wr = Bv + (size_t)min(g * ROWS + r, N - 1) * nch + c0;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) b[r][u] = __builtin_nontemporal_load(wr + u * kWave);
+        }
+    };
+    if (ntasks > 0) load(0, buf[0]);                   // B traffic starts before A is staged
+    const half8* Av = (const half8*)A;
+    for (int j = threadIdx.x; j < MV * nch; j += WAVES * kWave) {
+        const int m = j / nch;
+        as[j] = m < M ? Av[(size_t)m * nch + (j - m * nch)] : half8{};
+    }
+    __syncthreads();
+
+    float acc[ROWS][MV];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < MV; ++m) acc[r][m] = 0.0f;
+    auto compute = [&](int i, const half8 (&b)[ROWS][UNROLL]) __attribute__((always_inline)) {
+        const int c0 = (i % spg) * STEP + lane;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int m = 0; m < MV; ++m) {
+                const half8 xv = as[m * nch + c0 + u * kWave];
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r) acc[r][m] = dot8(b[r][u], xv, acc[r][m]);
+            }
+        if (i % spg == spg - 1) {                      // the wave's rows are done
+            const int row0 = (g0 + (i / spg) * gstride) * ROWS;
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+                for (int m = 0; m < MV; ++m) {
+                    const float sum = wave_sum(acc[r][m]);
+                    if (lane == r * MV + m && m < M && row0 + r < N)
+                        C[(size_t)m * N + row0 + r] = f32_to_f16_bits(sum);
+                    acc[r][m] = 0.0f;
+                }
+        }
+    };
+    for (int i = 0; i < ntasks; i += 2) {
+        if (i + 1 < ntasks) load(i + 1, buf[1]);
+        compute(i, buf[0]);
+        if (i + 1 < ntasks) {
+            if (i + 2 < ntasks) load(i + 2, buf[0]);
+            compute(i + 1, buf[1]);
+        }
+    }
+#endif
+}
+
+constexpr int kSkinnyVecMaxM = 8;
+constexpr int kSkinnyVecGrid = 256;                    // one workgroup per CU
+
+// A-row capacity of the vector form for M rows: 1, 2, 4 or 8.
+__host__ __device__ constexpr int skinny_vec_mv(int M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+
+// Whether the vector form with `unroll` runs M x K.
+__host__ __device__ constexpr bool skinny_vec_fits(int M, int K, int unroll)
+{
+    return M >= 1 && M <= kSkinnyVecMaxM && K > 0 && unroll > 0 && K % (512 * unroll) == 0 &&
+           (long long)skinny_vec_mv(M) * K * 2 <= 160 * 1024;
+}
+
+template <int MV, int ROWS, int UNROLL, int WAVES>
+hipError_t launch_skinny_vec_mv(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                                hipStream_t stream)
+{
+    auto kern = skinny_vec_kernel<MV, ROWS, UNROLL, WAVES>;
+    static bool attr_set = false;   // dynamic LDS above 64 KiB must be opted into
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int groups = ceil_div(N, ROWS);
+    int grid = ceil_div(groups, WAVES);
+    if (grid > kSkinnyVecGrid) grid = kSkinnyVecGrid;
+    const size_t lds = (size_t)MV * K * 2;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, A, B, C, M, N, K);
+    return hipGetLastError();
+}
+
+// The vector-form launch for M rows; the caller has checked skinny_vec_fits.
+template <int ROWS, int UNROLL, int WAVES>
+hipError_t launch_skinny_vec(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                             hipStream_t stream)
+{
+    switch (skinny_vec_mv(M)) {
+    case 1: return launch_skinny_vec_mv<1, ROWS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    case 2: return launch_skinny_vec_mv<2, ROWS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    case 4: return launch_skinny_vec_mv<4, ROWS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    default: return launch_skinny_vec_mv<8, ROWS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    }
+}
+
 }  // namespace gf
+

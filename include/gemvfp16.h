@@ -192,13 +192,18 @@ int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int
  * gemm_f16_nt (fp32 accumulation, one fp16 rounding).  gemm_f16_nt takes
  * this path by itself when M <= 16, K % 8 == 0 and A and B are 16-byte
  * aligned; this entry point runs it explicitly and returns
- * GF_ERR_UNSUPPORTED outside those conditions.  cfg: launch shape (blocks =
- * 16-row blocks of B per workgroup, waves = waves per workgroup splitting K,
- * and stages = 0 for the direct form, whose loads go straight to registers
- * (unroll = k-steps per register batch, two batches in flight per wave), or
- * stages >= 2 for the LDS-staged form, which loads 1 KiB of one row per
- * instruction through a ring of that many 512-k chunks (needs K % 512 == 0;
- * unroll 0)), NULL = the library's choice.
+ * GF_ERR_UNSUPPORTED outside those conditions.  cfg: launch shape, NULL =
+ * the library's choice.  waves = waves per workgroup; then one of three forms:
+ *  - stages = 0, direct form on the matrix cores: blocks = 16-row blocks of
+ *    B per workgroup, waves split K, loads straight to registers (unroll =
+ *    k-steps per register batch, two batches in flight per wave);
+ *  - stages >= 2, LDS-staged form on the matrix cores: blocks as above,
+ *    1 KiB of one row per load instruction through a ring of that many
+ *    512-k chunks (needs K % 512 == 0; unroll 0);
+ *  - stages = 1, vector form for M <= 8: blocks = rows of B per wave, unroll
+ *    = 16-byte chunks per row and lane in flight; B streamed as by gemv_f16,
+ *    A staged in LDS (needs K % (512 * unroll) == 0 and M' * K * 2 <= 160 KiB,
+ *    M' = M rounded up to 1, 2, 4 or 8).
  * Defined by the TileLang GEMV page: GEMV as the degenerate GEMM with a
  * single row of A, here with up to 16 rows (C = A B^T of the TileLang FP16
  * matmul page, section 1).

@@ -252,18 +252,37 @@ def test_skinny(M, N, K):
     check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny %dx%dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 520, 1536), (3, 1000, 512), (9, 77, 2048), (6, 300, 1024)])
+def skinny_runs(cfg, M, K):
+    """Whether a launch shape accepts M x K (its documented limits)."""
+    if cfg["stages"] == 0:
+        return True
+    if cfg["stages"] >= 2:
+        return K > 0 and K % 512 == 0
+    mv = 1 if M <= 1 else (2 if M <= 2 else (4 if M <= 4 else 8))
+    return M <= 8 and K > 0 and K % (512 * cfg["unroll"]) == 0 and mv * K * 2 <= 160 * 1024
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 520, 1536), (3, 1000, 512), (9, 77, 2048), (6, 300, 1024),
+                                   (4, 1000, 4096), (8, 333, 2048), (1, 513, 2048), (2, 64, 8192),
+                                   (7, 130, 16384)])
 def test_skinny_every_config(M, N, K):
-    """Every launch shape, direct and LDS-staged (K a multiple of 512)."""
+    """Every launch shape: direct, LDS-staged (K a multiple of 512) and vector
+    form (M <= 8, K a multiple of 512 * unroll); shapes outside a form's
+    limits must be refused."""
     A, B = operands("integer", M, N, K, seed=6)
     ref = oracle.gemm_nt_f16(A, B)
     for cfg in gf.skinny_configs():
         _say("skinny cfg %s %dx%dx%d" % (cfg, M, N, K))
-        assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
+        if skinny_runs(cfg, M, K):
+            assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
+        else:
+            with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+                run_skinny(A, B, cfg)
     A, B = operands("uniform", M, N, K, seed=6)
     ref = oracle.gemm_nt_f16(A, B)
     for cfg in gf.skinny_configs():
-        check_f16_tolerance(run_skinny(A, B, cfg), ref, "skinny %s %dx%dx%d" % (cfg, M, N, K))
+        if skinny_runs(cfg, M, K):
+            check_f16_tolerance(run_skinny(A, B, cfg), ref, "skinny %s %dx%dx%d" % (cfg, M, N, K))
 
 
 def test_skinny_lds_form_needs_k_multiple_of_512():
