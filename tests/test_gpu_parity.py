@@ -264,11 +264,12 @@ def skinny_runs(cfg, M, K):
 
 @pytest.mark.parametrize("M,N,K", [(16, 520, 1536), (3, 1000, 512), (9, 77, 2048), (6, 300, 1024),
                                    (4, 1000, 4096), (8, 333, 2048), (1, 513, 2048), (2, 64, 8192),
-                                   (7, 130, 16384)])
+                                   (7, 130, 16384), (5, 9000, 2048)])
 def test_skinny_every_config(M, N, K):
     """Every launch shape: direct, LDS-staged (K a multiple of 512) and vector
-    form (M <= 8, K a multiple of 512 * unroll); shapes outside a form's
-    limits must be refused."""
+    form (M <= 8, K a multiple of 512 * unroll; (5, 9000, 2048) gives waves
+    more than one row group); shapes outside a form's limits must be
+    refused."""
     A, B = operands("integer", M, N, K, seed=6)
     ref = oracle.gemm_nt_f16(A, B)
     for cfg in gf.skinny_configs():
