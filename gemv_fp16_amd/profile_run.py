@@ -8,6 +8,8 @@ Ops (inputs are the seeded uniform[-1,1] fp16 workloads):
           stores B as K x N (and A as K x M) and runs gemm_f16 on them
   gemv    y = W . x at N = K = 8192, rotating 5 W copies (640 MiB)
   splitk  M = N = 1024, K = 16384, split 8: fp32 atomic, fp32 two-pass, fp16 two-pass
+  skinny  C = A . B^T with M = 4 and M = 16 rows of A against an 8192 x 8192 B (5 B copies
+          rotated, 640 MiB); the library's default form for each M
   sparse  2:4 sparse C = decompress(A_sparse, E) . B^T at M = N = K = 8192 (A compressed
           once on the GPU from a dense uniform A; default tile config)
   compress  2:4 compression of an 8192 x 8192 A, rotating 3 copies (384 MiB)
@@ -27,7 +29,7 @@ if ROOT not in sys.path:
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("op", choices=["gemm", "gemv", "splitk", "sparse", "compress", "copy"])
+    ap.add_argument("op", choices=["gemm", "gemv", "splitk", "skinny", "sparse", "compress", "copy"])
     ap.add_argument("--iters", type=int, default=10)
     ap.add_argument("--m", type=int, default=8192)
     ap.add_argument("--n", type=int, default=8192)
@@ -80,6 +82,13 @@ def main(argv=None):
             gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_ATOMIC, ws)
             gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_TWOPASS, ws)
             gf.gemm_f16_nt_splitk_f16(A, B, C16, 8, ws)
+    elif a.op == "skinny":
+        Bs = [torch.from_numpy(inputs.uniform_f16((a.n, a.k), i, 1)).cuda() for i in range(5)]
+        for m in (4, 16):
+            A = torch.from_numpy(inputs.uniform_f16((m, a.k), 0, 0)).cuda()
+            C = torch.empty((m, a.n), dtype=torch.float16, device="cuda")
+            for i in range(a.iters):
+                gf.gemm_f16_nt(A, Bs[i % len(Bs)], C)
     elif a.op == "sparse":
         A = torch.from_numpy(inputs.uniform_f16((a.m, a.k), 0, 0)).cuda()
         B = torch.from_numpy(inputs.uniform_f16((a.n, a.k), 0, 1)).cuda()
