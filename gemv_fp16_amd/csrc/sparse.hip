@@ -26,12 +26,24 @@ constexpr SpDesc sp_desc()
     return SpDesc{BM, BN, S, &launch_sp_gemm<SpCfg<BM, BN, S>, true>};
 }
 
+// The paired form (stages = 0): two B stages, A_sparse in K-tile pairs,
+// metadata eight K tiles at a time; half of each B tile's loads under the
+// last MFMA step of the tile two before.
+template <int BM, int BN, int S, int HB>
+constexpr SpDesc spp_desc()
+{
+    static_assert(S == 0 && SpPairCfg<BM, BN, HB>::kValid, "invalid paired sparse config");
+    return SpDesc{BM, BN, S, &launch_spp_gemm<SpPairCfg<BM, BN, HB>>};
+}
+
 // Compiled tile configs (the offline sweep times each of them).
 const SpDesc kSpConfigs[] = {
     sp_desc<256, 256, 2>(), sp_desc<256, 256, 3>(),
     sp_desc<256, 128, 2>(), sp_desc<256, 128, 3>(), sp_desc<256, 128, 4>(),
     sp_desc<128, 256, 2>(), sp_desc<128, 256, 3>(),
     sp_desc<128, 128, 2>(), sp_desc<128, 128, 3>(), sp_desc<128, 128, 4>(),
+    spp_desc<256, 256, 0, 4>(), spp_desc<256, 128, 0, 2>(), spp_desc<128, 256, 0, 4>(),
+    spp_desc<128, 128, 0, 2>(),
 };
 constexpr int kNumSp = sizeof(kSpConfigs) / sizeof(kSpConfigs[0]);
 
@@ -52,7 +64,10 @@ int find_sp(const gf_sp_cfg& c)
     return -1;
 }
 
-// The largest tile that still gives every CU a workgroup.
+// The largest tile that still gives every CU a workgroup.  At 256 x 128 the
+// paired form (stages = 0) is the faster one; at 256 x 256 it trails three
+// stages by about 3 %, and with fewer tiles than CUs (the 128 x 128 case
+// here) its shallower B pipeline loses.
 gf_sp_cfg default_sp_cfg(int M, int N)
 {
     gf_sp_cfg c;
@@ -60,7 +75,7 @@ gf_sp_cfg default_sp_cfg(int M, int N)
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t25612 = (int64_t)ceil_div(M, 256) * ceil_div(N, 128);
     if (t256 >= 256) { c.block_m = 256; c.block_n = 256; c.stages = 3; }
-    else if (t25612 >= 256) { c.block_m = 256; c.block_n = 128; c.stages = 3; }
+    else if (t25612 >= 256) { c.block_m = 256; c.block_n = 128; c.stages = 0; }
     else { c.block_m = 128; c.block_n = 128; c.stages = 3; }
     return c;
 }

@@ -37,7 +37,9 @@
 // has to process for E (the address path, not the MFMAs, sets the pace of
 // this kernel).  The schedule is the dense GEMM's one-wave-per-SIMD form: the
 // tile barrier sits before the last MFMA step, and the next tile's first
-// fragments and half of a later tile's loads go under that step.
+// fragments and half of a later tile's loads go under that step.  The paired
+// form at the end of this file stages A_sparse two K tiles and the metadata
+// eight K tiles at a time, beside two B stages.
 #pragma once
 #include "common.hpp"
 
@@ -493,6 +495,53 @@ __device__ __forceinline__ void sp_step(floatx16 (&acc)[Cfg::FM][Cfg::FN], const
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// fp16 C of one wave's (WTM x WTN) block through a per-wave LDS transpose
+// and 16-byte streaming stores (element stores on ragged or unaligned
+// edges).  Waits at a workgroup barrier first: the LDS must be free.
+template <class Cfg>
+__device__ __forceinline__ void sp_store_c(const floatx16 (&acc)[Cfg::FM][Cfg::FN], const SpArgs& a,
+                                           GF_LDS char* smem, int wrow0, int wcol0, int wave, int lane,
+                                           bool aligned)
+{
+    uint16_t* C = a.C;
+    lds_barrier();                                // operand buffers are free now
+    constexpr int LDW = Cfg::WTN + Cfg::EPAD;     // fp16 per LDS row
+    GF_LDS uint16_t* reg = (GF_LDS uint16_t*)(smem + wave * (Cfg::WTM * LDW * 2));
+#pragma unroll
+    for (int fm = 0; fm < Cfg::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Cfg::FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                // 32 x 32 block: accumulator i of lane l is row 8 (i/4) + 4 (l/32) + i%4, column l%32
+                const int r = fm * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+                const int c = fn * 32 + lane % 32;
+                reg[r * LDW + c] = f32_to_f16_bits(acc[fm][fn][i]);
+            }
+    asm volatile("" ::: "memory");
+    wait_lgkmcnt0();
+    constexpr int CPR = Cfg::WTN / 8;             // 16-byte chunks per sub-tile row
+    constexpr int ITERS = Cfg::WTM * CPR / kWave;
+    const bool vec_ok = aligned && (a.N % 8 == 0) && (((uintptr_t)C & 15) == 0);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int q = it * kWave + lane;
+        const int r = q / CPR, cc = q % CPR;
+        const u32x4 v = *(const GF_LDS u32x4*)(reg + r * LDW + cc * 8);
+        const int grow = wrow0 + r, gcol = wcol0 + cc * 8;
+        if (grow >= a.M) continue;
+        if (vec_ok && gcol + 8 <= a.N) {
+            __builtin_nontemporal_store(v, (u32x4*)(C + (size_t)grow * a.N + gcol));
+        } else {
+            const uint32_t parts[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2)
+                if (gcol + e2 < a.N)
+                    C[(size_t)grow * a.N + gcol + e2] = (uint16_t)(parts[e2 / 2] >> (16 * (e2 % 2)));
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -635,45 +684,7 @@ __global__ __launch_bounds__(256) void sp_gemm_kernel(SpArgs a)
         }
     }
 
-    // ---- epilogue: fp16 C through a per-wave LDS transpose ----
-    const int wrow0 = m0 + wm * Cfg::WTM, wcol0 = n0 + wn * Cfg::WTN;
-    uint16_t* C = a.C;
-    lds_barrier();                                // operand buffers are free now
-    constexpr int LDW = Cfg::WTN + Cfg::EPAD;     // fp16 per LDS row
-    GF_LDS uint16_t* reg = (GF_LDS uint16_t*)(smem + wave * (Cfg::WTM * LDW * 2));
-#pragma unroll
-    for (int fm = 0; fm < Cfg::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < Cfg::FN; ++fn)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                // 32 x 32 block: accumulator i of lane l is row 8 (i/4) + 4 (l/32) + i%4, column l%32
-                const int r = fm * 32 + 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
-                const int c = fn * 32 + lane % 32;
-                reg[r * LDW + c] = f32_to_f16_bits(acc[fm][fn][i]);
-            }
-    asm volatile("" ::: "memory");
-    wait_lgkmcnt0();
-    constexpr int CPR = Cfg::WTN / 8;             // 16-byte chunks per sub-tile row
-    constexpr int ITERS = Cfg::WTM * CPR / kWave;
-    const bool vec_ok = ALIGNED && (a.N % 8 == 0) && (((uintptr_t)C & 15) == 0);
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        const int q = it * kWave + lane;
-        const int r = q / CPR, cc = q % CPR;
-        const u32x4 v = *(const GF_LDS u32x4*)(reg + r * LDW + cc * 8);
-        const int grow = wrow0 + r, gcol = wcol0 + cc * 8;
-        if (grow >= a.M) continue;
-        if (vec_ok && gcol + 8 <= a.N) {
-            __builtin_nontemporal_store(v, (u32x4*)(C + (size_t)grow * a.N + gcol));
-        } else {
-            const uint32_t parts[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2)
-                if (gcol + e2 < a.N)
-                    C[(size_t)grow * a.N + gcol + e2] = (uint16_t)(parts[e2 / 2] >> (16 * (e2 % 2)));
-        }
-    }
+    sp_store_c<Cfg>(acc, a, smem, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, wave, lane, ALIGNED);
 #endif
 }
 
@@ -681,6 +692,416 @@ template <class Cfg, bool ALIGNED>
 hipError_t launch_sp_gemm(const SpArgs& a, hipStream_t stream)
 {
     auto kern = sp_gemm_kernel<Cfg, ALIGNED>;
+    static bool attr_set = false;   // dynamic LDS above 64 KiB must be opted into
+    if (!attr_set) {
+        hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             Cfg::LDS_BYTES);
+        if (err != hipSuccess) return err;
+        attr_set = true;
+    }
+    const int tiles = ceil_div(a.M, Cfg::BM) * ceil_div(a.N, Cfg::BN);
+    hipLaunchKernelGGL(kern, dim3(tiles, 1, 1), dim3(Cfg::NT, 1, 1), Cfg::LDS_BYTES, stream, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Paired form
+// ---------------------------------------------------------------------------
+//
+// The same product with fewer cache lines per loaded byte.  The address
+// unit handles a load instruction at a cost that grows with the number of
+// cache lines it touches, and in the form above it, not the matrix cores,
+// sets the pace.  Here:
+//  * A_sparse moves two K tiles at a time (128 bytes per row: one whole
+//    cache line per row, 8 rows per instruction, instead of half a line of
+//    16 rows) into a two-slot ring of K-tile pairs, half the pair's rows
+//    under each of two consecutive K tiles;
+//  * the metadata of eight K tiles (64 bytes per row) moves together into a
+//    two-slot ring, an eighth of the rows under each K tile, with 4-byte
+//    direct-to-LDS loads that cover 4 rows per instruction instead of 16;
+//  * B keeps one LDS stage per K tile, two stages.
+// Per 256 x 256 x 64 tile the loads touch 416 cache lines instead of 640.
+// With two B stages every wait is for all loads in flight.
+//
+// Metadata slot layout: row r's 16 dwords (dword 2 w + g = words 4 w + 2 g
+// and 4 w + 2 g + 1, i.e. lane group g's index words of K tile w of the
+// slot) sit at dword position d ^ key(r), key(r) = 2 ((r mod (BM/8)) / 4 mod 8):
+// the 64 lanes of one fragment's metadata read (32 rows x 2 lane groups)
+// then fall in 64 different banks.
+
+template <int BM_, int BN_, int HB_>
+struct SpPairCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 64, NT = 256;
+    static constexpr int WM = 2, WN = 2;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int KST = BK / 32;                    // sparse MFMA steps per K tile
+    static constexpr int CH = 8;                           // 16-byte chunks per row: A pair slot, B stage
+    static constexpr int A_SLOT = BM * CH * 16, B_STAGE = BN * CH * 16;
+    static constexpr int E_ROW = 64;                       // metadata bytes per row and slot (8 K tiles)
+    static constexpr int E_SLOT = BM * E_ROW, E_PIECE_ROWS = BM / 8;
+    static constexpr int A_BASE = 0, B_BASE = 2 * A_SLOT, E_BASE = B_BASE + 2 * B_STAGE;
+    // Loads per thread per K tile: half an A pair slot, a B stage, an eighth
+    // of a metadata slot.  HB of the B loads go under the last MFMA step of
+    // the tile before (with the A and metadata loads), the rest under the
+    // first step of the tile before.
+    static constexpr int LA = BM * CH / 2 / NT, LB = BN * CH / NT, LE = E_PIECE_ROWS * (E_ROW / 4) / NT;
+    static constexpr int HB = HB_;
+    static constexpr int EPAD = 8;                         // fp16 pad per epilogue row
+    static constexpr int EPI_BYTES = 4 * WTM * (WTN + EPAD) * 2;
+    static constexpr int MAIN_BYTES = E_BASE + 2 * E_SLOT;
+    static constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+    static constexpr bool kValid =
+        WTM % 32 == 0 && WTN % 32 == 0 && FM >= 1 && FN >= 1 && LA * NT * 2 == BM * CH &&
+        LB * NT == BN * CH && LE >= 1 && LE * NT == E_PIECE_ROWS * (E_ROW / 4) && 0 <= HB && HB <= LB &&
+        8 * LE + 2 * LA + LB < 64 && LDS_BYTES <= 160 * 1024;
+};
+
+template <class Cfg>
+__device__ __forceinline__ int spp_ekey(int row)
+{
+    return 2 * (((row % Cfg::E_PIECE_ROWS) / 4) % 8);
+}
+
+// Direct-to-LDS loader of the paired form.  All source offsets go in the
+// per-lane offset, where the buffer's range check sees them.
+template <class Cfg>
+struct SppLoader {
+    uint32_t va[2][Cfg::LA];   // A_sparse: load r of pair half h at k = 0 (rows clamped into range)
+    uint32_t vb[Cfg::LB];      // B: load r at k = 0 (rows clamped)
+    uint32_t ve[Cfg::LE];      // E: load r of eighth 0 of slot 0 (rows past M: range-checked or
+                               // other rows' words; they feed no stored output)
+    int tid;
+    __amdgpu_buffer_rsrc_t ra, rb, re;
+
+    // Slot s of a 128-byte-row region (A pair slot or B stage): row and the
+    // 16-byte chunk of the source row that it holds.
+    __device__ __forceinline__ static void chunk_source(int s, int& row, int& c)
+    {
+        row = s / Cfg::CH;
+        c = (s % Cfg::CH) ^ sp_key(row, Cfg::CH);
+    }
+
+    __device__ __forceinline__ void init(const SpArgs& a, int m0, int n0, int tid_)
+    {
+        tid = tid_;
+        static_for<2>([&](auto h_c) {
+            constexpr int H = decltype(h_c)::value;
+            static_for<Cfg::LA>([&](auto r_c) {
+                int row, c;
+                chunk_source(H * Cfg::BM * Cfg::CH / 2 + decltype(r_c)::value * Cfg::NT + tid, row, c);
+                va[H][decltype(r_c)::value] = (uint32_t)min(m0 + row, a.M - 1) * (uint32_t)a.K + 16u * c;
+            });
+        });
+        static_for<Cfg::LB>([&](auto r_c) {
+            int row, c;
+            chunk_source(decltype(r_c)::value * Cfg::NT + tid, row, c);
+            vb[decltype(r_c)::value] = ((uint32_t)min(n0 + row, a.N - 1) * (uint32_t)a.K + 8u * c) * 2u;
+        });
+        static_for<Cfg::LE>([&](auto r_c) {
+            const int s = decltype(r_c)::value * Cfg::NT + tid;
+            const int row = s / 16, d = (s % 16) ^ spp_ekey<Cfg>(row);
+            ve[decltype(r_c)::value] = (uint32_t)(m0 + row) * (uint32_t)(a.K / 8) + 4u * d;
+        });
+        constexpr int kRawBufferWord3 = 0x00020000;
+        ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.Asp, 0, (int)((uint32_t)a.M * (uint32_t)a.K),
+                                               kRawBufferWord3);
+        rb = __builtin_amdgcn_make_buffer_rsrc((void*)a.B, 0, (int)((uint32_t)a.N * (uint32_t)a.K * 2u),
+                                               kRawBufferWord3);
+        re = __builtin_amdgcn_make_buffer_rsrc((void*)a.E, 0, (int)((uint32_t)a.M * (uint32_t)(a.K / 8)),
+                                               kRawBufferWord3);
+    }
+
+    // Load R of half H of A pair j (K tiles 2j, 2j+1) into pair slot j % 2.
+    // MASKED: chunks at k >= K read 16 zero bytes.
+    template <int H, int R, bool MASKED>
+    __device__ __forceinline__ void issue_a(const SpArgs& a, GF_LDS char* smem, int j, int wave) const
+    {
+        GF_LDS char* dst = smem + Cfg::A_BASE + (j & 1) * Cfg::A_SLOT +
+                           (H * Cfg::BM * Cfg::CH / 2 + R * Cfg::NT + wave * kWave) * 16;
+        const uint32_t off = va[H][R] + (uint32_t)j * 128u;
+        if constexpr (!MASKED) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (GF_LDS void*)dst, 16, off, 0, 0, 0);
+        } else {
+            int row, c;
+            chunk_source(H * Cfg::BM * Cfg::CH / 2 + R * Cfg::NT + tid, row, c);
+            const void* src = j * 128 + 16 * c < a.K ? (const void*)((const char*)a.Asp + off)
+                                                     : (const void*)g_sp_zero16;
+            __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)dst, 16, 0, 0);
+        }
+    }
+
+    // Load R of the B tile at k0 into stage st.
+    template <int R, bool MASKED>
+    __device__ __forceinline__ void issue_b(const SpArgs& a, GF_LDS char* smem, int st, int k0, int wave) const
+    {
+        GF_LDS char* dst = smem + Cfg::B_BASE + st * Cfg::B_STAGE + (R * Cfg::NT + wave * kWave) * 16;
+        if constexpr (!MASKED) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (GF_LDS void*)dst, 16, vb[R], (uint32_t)k0 * 2u, 0, 0);
+        } else {
+            int row, c;
+            chunk_source(R * Cfg::NT + tid, row, c);
+            const void* src = k0 + 8 * c < a.K ? (const void*)((const char*)a.B + vb[R] + (size_t)k0 * 2)
+                                               : (const void*)g_sp_zero16;
+            __builtin_amdgcn_global_load_lds(src, (GF_LDS void*)dst, 16, 0, 0);
+        }
+    }
+
+    // Load R of eighth p of metadata slot j (K tiles 8j .. 8j+7); `eoff` is
+    // the eighth's and slot's part of the source offset (espan()).
+    template <int R>
+    __device__ __forceinline__ void issue_e(GF_LDS char* smem, int p, int j, uint32_t eoff, int wave) const
+    {
+        GF_LDS char* dst = smem + Cfg::E_BASE + (j & 1) * Cfg::E_SLOT +
+                           (p * Cfg::E_PIECE_ROWS * 16 + R * Cfg::NT + wave * kWave) * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (GF_LDS void*)dst, 4, ve[R] + eoff, 0, 0, 0);
+    }
+    __device__ __forceinline__ static uint32_t espan(int p, int j, int K)
+    {
+        return (uint32_t)(p * Cfg::E_PIECE_ROWS) * (uint32_t)(K / 8) + (uint32_t)j * 64u;
+    }
+
+    template <int H, bool MASKED>
+    __device__ __forceinline__ void issue_a_half(const SpArgs& a, GF_LDS char* smem, int j, int wave) const
+    {
+        static_for<Cfg::LA>([&](auto r) { issue_a<H, decltype(r)::value, MASKED>(a, smem, j, wave); });
+    }
+    template <int R0, int R1, bool MASKED>
+    __device__ __forceinline__ void issue_b_range(const SpArgs& a, GF_LDS char* smem, int st, int k0, int wave) const
+    {
+        static_for<R1 - R0>([&](auto r) { issue_b<R0 + decltype(r)::value, MASKED>(a, smem, st, k0, wave); });
+    }
+    __device__ __forceinline__ void issue_e_piece(GF_LDS char* smem, int p, int j, int K, int wave) const
+    {
+        const uint32_t eoff = espan(p, j, K);
+        static_for<Cfg::LE>([&](auto r) { issue_e<decltype(r)::value>(smem, p, j, eoff, wave); });
+    }
+};
+
+template <class Cfg>
+struct SppReader {
+    int oa, ob, oe;   // lane byte offsets of fragment 0: in an A pair slot, a B stage, a metadata slot
+    int qa, kb;       // A: the lane's chunk bits (2 g) ^ key; B: swizzle key
+    int g, ke;        // lane group; metadata key
+
+    __device__ __forceinline__ void init(int wm, int wn, int lane)
+    {
+        const int r = lane % 32;
+        g = lane / 32;
+        const int ra = wm * Cfg::WTM + r, rb = wn * Cfg::WTN + r;
+        oa = ra * Cfg::CH * 16;
+        qa = (2 * g) ^ sp_key(ra, Cfg::CH);
+        ob = rb * Cfg::CH * 16;
+        kb = sp_key(rb, Cfg::CH);
+        oe = ra * Cfg::E_ROW;
+        ke = spp_ekey<Cfg>(ra);
+    }
+    // Step S of K tile u (H = u % 2) from u's pair slot: compressed chunk
+    // 4 H + 2 g + S of the pair's row (the bits do not overlap, so the sum is
+    // an OR and commutes with the swizzle XOR).
+    template <int F, int H, int S>
+    __device__ __forceinline__ half8 a(const GF_LDS char* slot) const
+    {
+        return *(const GF_LDS half8*)(slot + oa + F * 32 * Cfg::CH * 16 + ((qa ^ (4 * H + S)) * 16));
+    }
+    template <int F, int S>
+    __device__ __forceinline__ half16 b(const GF_LDS char* stage) const
+    {
+        const GF_LDS char* p = stage + ob + F * 32 * Cfg::CH * 16;
+        const half8 lo = *(const GF_LDS half8*)(p + (((2 * S + g) ^ kb) * 16));
+        const half8 hi = *(const GF_LDS half8*)(p + (((2 * (Cfg::KST + S) + g) ^ kb) * 16));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    }
+    // Lane offset of K tile w's dword (w = u % 8) in a metadata slot.
+    __device__ __forceinline__ int eo(int w) const { return oe + (((2 * w + g) ^ ke) * 4); }
+    template <int F>
+    __device__ __forceinline__ uint32_t e(const GF_LDS char* slot, int eow) const
+    {
+        return *(const GF_LDS uint32_t*)(slot + eow + F * 32 * Cfg::E_ROW);
+    }
+};
+
+// One MFMA step of the paired form: the FM x FN sparse MFMAs on `cur` with
+// index words `idx`, with read(j) (read j of the next step's fragments, in
+// SpStepPlan's order) and load(l) (l < NL) woven into the stream.
+template <class Cfg, int RS, int NL, class Read, class Load>
+__device__ __forceinline__ void spp_step(floatx16 (&acc)[Cfg::FM][Cfg::FN], const SpFrags<Cfg>& cur,
+                                         const uint32_t (&idx)[Cfg::FM], Read&& read, Load&& load)
+{
+    typedef SpStepPlan<Cfg, RS, 0, NL> P;
+    static_for<P::NM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int fm = i / Cfg::FN, fn = i % Cfg::FN;
+        acc[fm][fn] = sp_mfma(cur.a[fm], cur.b[fn], acc[fm][fn], idx[fm]);
+        static_for<P::RPM>([&](auto r_c) {
+            constexpr int j = i * P::RPM + decltype(r_c)::value;
+            if constexpr (j < P::ND) read(std::integral_constant<int, j>{});
+        });
+        if constexpr (P::load_at(i) >= 0) load(std::integral_constant<int, P::load_at(i)>{});
+    });
+    static_for<NL>([&](auto j_c) {
+        if constexpr (decltype(j_c)::value >= P::NLS) load(j_c);
+    });
+    static_for<P::NM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        __builtin_amdgcn_sched_group_barrier(kSpSchedMfma, 1, 0);
+        if constexpr (P::nr(i) > 0) __builtin_amdgcn_sched_group_barrier(kSpSchedDsRead, P::nr(i), 0);
+        if constexpr (P::load_at(i) >= 0) __builtin_amdgcn_sched_group_barrier(kSpSchedVmemRead, 1, 0);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The paired-form kernel.  Needs A_sparse and B 16-byte aligned, E 4-byte
+// aligned and K % 32 == 0.
+//
+// Schedule (t = K tile; B(t) = the barrier before tile t's last MFMA step,
+// preceded by a wait for every load in flight):
+//  * step 0 of tile t: MFMAs of step 0; reads of tile t's step-1 fragments;
+//    loads HB .. LB-1 of B tile t+1 (stage (t+1) % 2).
+//  * B(t): tile t+1's B is complete; every wave has read all of tile t.
+//  * step 1 of tile t: MFMAs of step 1; reads of tile t+1's metadata and
+//    step-0 fragments; loads 0 .. HB-1 of B tile t+2 into stage t % 2, half
+//    (t+1) % 2 of A pair (t+3)/2, and eighth (t+1) % 8 of metadata slot
+//    (t+9)/8.
+// A pair j (tiles 2j, 2j+1) is loaded under tiles 2j-3 and 2j-2, after
+// B(2j-3) ended all reads of pair j-2 (tiles 2j-4, 2j-3) in the same slot,
+// and has landed by B(2j-2), before tile 2j-1's last step reads tile 2j.
+// Metadata slot j (tiles 8j .. 8j+7) is loaded under tiles 8j-9 .. 8j-2,
+// after B(8j-9) ended the reads of slot j-2 (tile 8j-9's metadata is read
+// under tile 8j-10), and has landed by B(8j-1), before tile 8j-1's last step
+// reads tile 8j's metadata.  The prologue issues what tiles -1 and earlier
+// would have.  Tiles past K are loaded as zeros (metadata past K: other
+// rows' words or range-checked zeros, which select zeros).
+template <class Cfg>
+__global__ __launch_bounds__(256) void spp_gemm_kernel(SpArgs a)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+    GF_LDS char* smem = (GF_LDS char*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+
+    const int tiles_m = ceil_div(a.M, Cfg::BM), tiles_n = ceil_div(a.N, Cfg::BN);
+    int tm, tn;
+    const int w = blockIdx.x;
+    if (a.raster > 0) {
+        grouped_tile(xcd_remap(w, tiles_m * tiles_n), tiles_m, tiles_n, a.raster, tm, tn);
+    } else {
+        tm = w / tiles_n;
+        tn = w % tiles_n;
+    }
+    const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+    const int nk = ceil_div(a.K, Cfg::BK);
+
+    floatx16 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int fm = 0; fm < Cfg::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Cfg::FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[fm][fn][i] = 0.0f;
+
+    SppLoader<Cfg> ld;
+    ld.init(a, m0, n0, tid);
+    SppReader<Cfg> rd;
+    rd.init(wm, wn, lane);
+    auto a_slot = [&](int u) { return smem + Cfg::A_BASE + ((u >> 1) & 1) * Cfg::A_SLOT; };
+    auto b_stage = [&](int st) { return smem + Cfg::B_BASE + st * Cfg::B_STAGE; };
+    auto e_slot = [&](int u) { return smem + Cfg::E_BASE + ((u >> 3) & 1) * Cfg::E_SLOT; };
+    SpFrags<Cfg> f0, f1;
+    uint32_t e[Cfg::FM], lo[Cfg::FM], hi[Cfg::FM];
+
+    if (nk > 0) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) ld.issue_e_piece(smem, p, 0, a.K, wave);
+        ld.template issue_a_half<0, true>(a, smem, 0, wave);
+        ld.template issue_a_half<1, true>(a, smem, 0, wave);
+        ld.template issue_b_range<0, Cfg::LB, true>(a, smem, 0, 0, wave);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (nk > 0) {
+        ld.template issue_b_range<0, Cfg::HB, true>(a, smem, 1, Cfg::BK, wave);
+        ld.template issue_a_half<0, true>(a, smem, 1, wave);
+        ld.issue_e_piece(smem, 0, 1, a.K, wave);
+    }
+    {
+        const int eo0 = rd.eo(0);
+        static_for<Cfg::FM>([&](auto f) { e[f] = rd.template e<decltype(f)::value>(e_slot(0), eo0); });
+        static_for<Cfg::FM>([&](auto f) { f0.a[f] = rd.template a<decltype(f)::value, 0, 0>(a_slot(0)); });
+        static_for<Cfg::FN>([&](auto f) { f0.b[f] = rd.template b<decltype(f)::value, 0>(b_stage(0)); });
+    }
+
+    // Tile t, H = t % 2 (compile-time: the loop runs tile pairs).  MASKED
+    // selects the load forms that turn chunks past K into zeros.
+    auto tile = [&](auto h_c, auto masked_c, int t) {
+        constexpr int H = decltype(h_c)::value;
+        constexpr bool MASKED = decltype(masked_c)::value;
+        typedef SpStepPlan<Cfg, 1, 0, 0> P1;
+        typedef SpStepPlan<Cfg, 0, 0, 0> P0;
+#pragma unroll
+        for (int f = 0; f < Cfg::FM; ++f) { lo[f] = e[f] & 0xffffu; hi[f] = e[f] >> 16; }
+        const GF_LDS char* as0 = a_slot(t);
+        const int k1 = (t + 1) * Cfg::BK;
+        spp_step<Cfg, 1, Cfg::LB - Cfg::HB>(
+            acc, f0, lo,
+            [&](auto j_c) {
+                constexpr int j = decltype(j_c)::value, f = P1::frag(j);
+                if constexpr (P1::is_b(j)) f1.b[f] = rd.template b<f, 1>(b_stage(H));
+                else f1.a[f] = rd.template a<f, H, 1>(as0);
+            },
+            [&](auto l_c) {
+                ld.template issue_b<Cfg::HB + decltype(l_c)::value, MASKED>(a, smem, 1 - H, k1, wave);
+            });
+        wait_vmcnt<0>();
+        lds_barrier();                            // B(t)
+        const GF_LDS char* as1 = a_slot(t + 1);
+        const GF_LDS char* es1 = e_slot(t + 1);
+        const int eo1 = rd.eo((t + 1) & 7);
+        const int k2 = (t + 2) * Cfg::BK, ja = (t + 3) >> 1, pe = (t + 1) & 7, je = (t + 9) >> 3;
+        const uint32_t eoff = SppLoader<Cfg>::espan(pe, je, a.K);
+        spp_step<Cfg, 0, Cfg::HB + Cfg::LA + Cfg::LE>(
+            acc, f1, hi,
+            [&](auto j_c) {
+                constexpr int j = decltype(j_c)::value, f = P0::frag(j);
+                if constexpr (j < P0::NE) e[f] = rd.template e<f>(es1, eo1);
+                else if constexpr (P0::is_b(j)) f0.b[f] = rd.template b<f, 0>(b_stage(1 - H));
+                else f0.a[f] = rd.template a<f, 1 - H, 0>(as1);
+            },
+            [&](auto l_c) {
+                constexpr int l = decltype(l_c)::value;
+                if constexpr (l < Cfg::HB)
+                    ld.template issue_b<l, MASKED>(a, smem, H, k2, wave);
+                else if constexpr (l < Cfg::HB + Cfg::LA)
+                    ld.template issue_a<1 - H, l - Cfg::HB, MASKED>(a, smem, ja, wave);
+                else
+                    ld.template issue_e<l - Cfg::HB - Cfg::LA>(smem, pe, je, eoff, wave);
+            });
+    };
+    // Steady state: every tile that tiles t and t+1 load (B up to t+3, A up
+    // to t+5) lies wholly inside K.
+    const int nfull = (nk > 0 && nk * Cfg::BK > a.K) ? nk - 1 : nk;
+    int t = 0;
+    for (; t + 6 <= nfull; t += 2) {
+        tile(std::integral_constant<int, 0>{}, std::false_type{}, t);
+        tile(std::integral_constant<int, 1>{}, std::false_type{}, t + 1);
+    }
+    for (; t < nk; t += 2) {
+        tile(std::integral_constant<int, 0>{}, std::true_type{}, t);
+        if (t + 1 < nk) tile(std::integral_constant<int, 1>{}, std::true_type{}, t + 1);
+    }
+    wait_vmcnt<0>();                              // no load may land after the epilogue starts
+    sp_store_c<Cfg>(acc, a, smem, m0 + wm * Cfg::WTM, n0 + wn * Cfg::WTN, wave, lane, true);
+#endif
+}
+
+template <class Cfg>
+hipError_t launch_spp_gemm(const SpArgs& a, hipStream_t stream)
+{
+    auto kern = spp_gemm_kernel<Cfg>;
     static bool attr_set = false;   // dynamic LDS above 64 KiB must be opted into
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,

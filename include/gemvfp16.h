@@ -274,7 +274,11 @@ int gemm_sp_f16_nt(const void* A_sparse, const void* E, const void* B, void* C, 
                    void* stream);
 
 /* Tile config of the sparse GEMM: block_m x block_n output tile (K tiles of
- * 64), `stages` LDS buffers, raster as in gf_gemm_cfg.  NULL = the
+ * 64), raster as in gf_gemm_cfg.  stages >= 2: that many LDS buffers, each
+ * holding one K tile of A_sparse and B.  stages = 0: the paired form, which
+ * loads A_sparse two K tiles and E eight K tiles at a time (fewer cache
+ * lines per byte) beside two B buffers; it needs the same alignment as the
+ * fast path and otherwise runs the register-staged path.  NULL = the
  * library's choice.  GF_ERR_UNSUPPORTED when no kernel is compiled for it. */
 typedef struct gf_sp_cfg {
     int block_m, block_n, stages, raster;

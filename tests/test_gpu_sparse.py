@@ -164,6 +164,29 @@ def test_sparse_gemm_every_config():
                 check(sp_run(Asp, E, B, c), ref, kind, "cfg %s" % c)
 
 
+# The paired form (stages = 0): A_sparse two K tiles per load, metadata eight.
+# K spans the steady loop and the masked tail, several metadata slots, a
+# ragged last K tile (K % 64 == 32) and an odd tile count; M and N are ragged.
+PAIR_SHAPES = [((520, 264, 2080), "integer"), ((777, 300, 1056), "uniform"), ((256, 512, 4160), "integer"),
+               ((300, 130, 96), "integer"), ((129, 257, 544), "uniform")]
+
+
+@pytest.mark.parametrize("shape,kind", PAIR_SHAPES)
+def test_sparse_paired_form(shape, kind):
+    M, N, K = shape
+    cfgs = [c for c in gf.sp_configs() if c["stages"] == 0]
+    assert cfgs, "no paired-form config compiled"
+    A = inputs.sparse24(kind, (M, K), seed=M + K)
+    B = inputs.make(kind, (N, K), seed=N + K, stream_id=inputs.STREAM_B)
+    Asp, E = oracle.sp24_compress(A)
+    ref = oracle.gemm_sp_nt_f16(Asp, E, B)
+    for cfg in cfgs:
+        for raster in (0, 1):
+            c = dict(cfg, raster=raster)
+            _say("sparse paired %s %s %s" % (c, shape, kind))
+            check(sp_run(Asp, E, B, c), ref, kind, "paired cfg %s %s" % (c, shape))
+
+
 def test_sparse_gemm_zero_k_writes_zeros():
     M, N = 70, 90
     Asp = np.zeros((M, 0), np.uint16)
@@ -227,4 +250,19 @@ def test_sparse_8192_integer_sampled():
     _say("sparse 8192 integer")
     got = sp_run(Asp, E, B)
     ij = sample_ij(M, N, 4000, seed=6)
+    assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))
+
+
+def test_sparse_default_paired_shape_sampled():
+    """A shape whose default tile is the paired form (256 x 128, stages 0):
+    integer inputs, the library's own launch configuration, sampled entries."""
+    M, N, K = 2048, 4096, 8192
+    assert gf.sp_default_config(M, N, K)["stages"] == 0
+    A = inputs.sparse24("integer", (M, K), seed=9)
+    B = inputs.make("integer", (N, K), seed=9, stream_id=inputs.STREAM_B)
+    Asp, E = oracle.sp24_compress(A)
+    _say("sparse default paired %dx%dx%d" % (M, N, K))
+    got = sp_run(Asp, E, B)
+    ij = sample_ij(M, N, 4000, seed=13)
+    ij = np.concatenate([ij, [[M - 1, N - 1], [0, N - 1], [M - 1, 0]]]).astype(np.int64)
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))
