@@ -6,8 +6,8 @@ Inputs: a seeded integer block of 1024 rows, tiled down the rows, with one
 entry per row changed so that rows 1024 apart differ (a row-offset mistake
 shows up as a wrong product).  Integer inputs in {-2..2} make every result
 exact, so the checks are bit-exact: GEMM on sampled entries including the last
-rows and columns, GEMV on every output, the 2:4 sparse product on sampled
-entries.
+rows and columns, GEMV on every output, the 2:4 sparse product (default tile
+and the paired form) on sampled entries.
 """
 import sys
 
@@ -75,7 +75,9 @@ def test_gemv_largest_w():
     assert np.array_equal(host_u16(y), oracle.gemv_f16(W, x))
 
 
-def test_sparse_largest_a():
+@pytest.mark.parametrize("cfg", [None, {"block_m": 256, "block_n": 128, "stages": 0, "raster": 1}],
+                         ids=["default", "paired"])
+def test_sparse_largest_a(cfg):
     N = 256
     block = inputs.sparse24("integer", (1024, K), 5, inputs.STREAM_A)
     bsp, be = oracle.sp24_compress(block)
@@ -84,8 +86,8 @@ def test_sparse_largest_a():
     E = np.tile(be, (reps, 1))[:ROWS]
     Asp[:, 0] = (((np.arange(ROWS) // 1024) % 5) - 2).astype(np.float16).view(np.uint16)
     B = inputs.integer_f16((N, K), 5, inputs.STREAM_B)
-    _say("sparse %dx%dx%d (A_sparse of %d elements)" % (ROWS, N, K, Asp.size))
-    C = gf.gemm_sp_f16_nt(dev(Asp.view(np.float16)), dev(E.view(np.int16)), dev(B))
+    _say("sparse %dx%dx%d (A_sparse of %d elements) cfg %s" % (ROWS, N, K, Asp.size, cfg))
+    C = gf.gemm_sp_f16_nt(dev(Asp.view(np.float16)), dev(E.view(np.int16)), dev(B), cfg=cfg)
     torch.cuda.synchronize()
     got = host_u16(C)
     del C
