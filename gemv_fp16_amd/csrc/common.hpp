@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 namespace gf {
@@ -61,6 +62,22 @@ __device__ __forceinline__ void static_for(F&& f)
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Dynamic LDS above 64 KiB must be opted into, per kernel and per device.
+// `done` holds one bit per device id below 64 whose opt-in is made (the
+// caller keeps one per kernel); host threads that race only repeat the
+// idempotent call.
+inline hipError_t opt_in_lds(const void* kern, int bytes, std::atomic<uint64_t>& done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t(1) << dev) : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+    return e;
+}
 
 // Map a linear workgroup index to a logical tile index so that each XCD
 // receives one contiguous run of tiles.  The hardware hands consecutive

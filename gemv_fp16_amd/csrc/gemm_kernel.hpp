@@ -924,13 +924,10 @@ template <class Cfg, int EPI, bool ALIGNED>
 hipError_t launch_gemm(const GemmArgs& a, int slices, hipStream_t stream)
 {
     auto kern = gemm_nt_kernel<Cfg, EPI, ALIGNED>;
-    static bool attr_set = false;   // dynamic LDS above 64 KiB must be opted into
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           Cfg::LDS_BYTES);
+    static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
+    {
+        const hipError_t e = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int tiles = ceil_div(a.M, Cfg::BM) * ceil_div(a.N, Cfg::BN);
     hipLaunchKernelGGL(kern, dim3(tiles, slices, 1), dim3(Cfg::NT, 1, 1), Cfg::LDS_BYTES, stream, a);

@@ -242,12 +242,10 @@ hipError_t launch_skinny_lds_ma(const uint16_t* A, const uint16_t* B, uint16_t* 
     typedef SkinnyLdsCfg<NB, S, W, MA> Cf;
     static_assert(Cf::kValid, "skinny LDS config");
     auto kern = skinny_lds_kernel<NB, S, W, MA>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Cf::LDS_BYTES);
+    static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
+    {
+        const hipError_t e = opt_in_lds((const void*)kern, Cf::LDS_BYTES, lds_opt_in);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int grid = ceil_div(N, NB * 16);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(W * kWave), Cf::LDS_BYTES, stream, A, B, C, M, N, K);
@@ -382,12 +380,10 @@ hipError_t launch_skinny_vec_mv(const uint16_t* A, const uint16_t* B, uint16_t* 
                                 hipStream_t stream)
 {
     auto kern = skinny_vec_kernel<MV, ROWS, UNROLL, WAVES>;
-    static bool attr_set = false;   // dynamic LDS above 64 KiB must be opted into
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           160 * 1024);
+    static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
+    {
+        const hipError_t e = opt_in_lds((const void*)kern, 160 * 1024, lds_opt_in);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int groups = ceil_div(N, ROWS);
     int grid = ceil_div(groups, WAVES);

@@ -692,12 +692,10 @@ template <class Cfg, bool ALIGNED>
 hipError_t launch_sp_gemm(const SpArgs& a, hipStream_t stream)
 {
     auto kern = sp_gemm_kernel<Cfg, ALIGNED>;
-    static bool attr_set = false;   // dynamic LDS above 64 KiB must be opted into
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             Cfg::LDS_BYTES);
+    static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
+    {
+        const hipError_t err = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in);
         if (err != hipSuccess) return err;
-        attr_set = true;
     }
     const int tiles = ceil_div(a.M, Cfg::BM) * ceil_div(a.N, Cfg::BN);
     hipLaunchKernelGGL(kern, dim3(tiles, 1, 1), dim3(Cfg::NT, 1, 1), Cfg::LDS_BYTES, stream, a);
@@ -1102,12 +1100,10 @@ template <class Cfg>
 hipError_t launch_spp_gemm(const SpArgs& a, hipStream_t stream)
 {
     auto kern = spp_gemm_kernel<Cfg>;
-    static bool attr_set = false;   // dynamic LDS above 64 KiB must be opted into
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             Cfg::LDS_BYTES);
+    static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
+    {
+        const hipError_t err = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in);
         if (err != hipSuccess) return err;
-        attr_set = true;
     }
     const int tiles = ceil_div(a.M, Cfg::BM) * ceil_div(a.N, Cfg::BN);
     hipLaunchKernelGGL(kern, dim3(tiles, 1, 1), dim3(Cfg::NT, 1, 1), Cfg::LDS_BYTES, stream, a);
