@@ -34,8 +34,8 @@
 // (16 bytes per row) moves together into a separate three-slot ring with
 // 4-byte direct-to-LDS loads, half a slot per K tile: a load instruction then
 // covers 16 rows instead of 32, which halves the cache lines the address unit
-// has to process for E (the address path, not the MFMAs, sets the pace of
-// this kernel).  The schedule is the dense GEMM's one-wave-per-SIMD form: the
+// has to process for E (the loads, not the MFMAs, set the pace of this
+// kernel).  The schedule is the dense GEMM's one-wave-per-SIMD form: the
 // tile barrier sits before the last MFMA step, and the next tile's first
 // fragments and half of a later tile's loads go under that step.  The paired
 // form at the end of this file stages A_sparse two K tiles and the metadata
@@ -706,10 +706,9 @@ hipError_t launch_sp_gemm(const SpArgs& a, hipStream_t stream)
 // Paired form
 // ---------------------------------------------------------------------------
 //
-// The same product with fewer cache lines per loaded byte.  The address
-// unit handles a load instruction at a cost that grows with the number of
-// cache lines it touches, and in the form above it, not the matrix cores,
-// sets the pace.  Here:
+// The same product with fewer cache lines per loaded byte: the address unit
+// handles a load instruction at a cost that grows with the number of cache
+// lines it touches.  Here:
 //  * A_sparse moves two K tiles at a time (128 bytes per row: one whole
 //    cache line per row, 8 rows per instruction, instead of half a line of
 //    16 rows) into a two-slot ring of K-tile pairs, half the pair's rows
@@ -719,13 +718,15 @@ hipError_t launch_sp_gemm(const SpArgs& a, hipStream_t stream)
 //    direct-to-LDS loads that cover 4 rows per instruction instead of 16;
 //  * B keeps one LDS stage per K tile, two stages.
 // Per 256 x 256 x 64 tile the loads touch 416 cache lines instead of 640.
-// With two B stages every wait is for all loads in flight.
+// With two B stages every wait is for all loads in flight.  The trade: the
+// smaller tiles gain from the lighter address work, while at 256 x 256 the
+// shallower B pipeline costs about what it saves.
 //
 // Metadata slot layout: row r's 16 dwords (dword 2 w + g = words 4 w + 2 g
 // and 4 w + 2 g + 1, i.e. lane group g's index words of K tile w of the
 // slot) sit at dword position d ^ key(r), key(r) = 2 ((r mod (BM/8)) / 4 mod 8):
-// the 64 lanes of one fragment's metadata read (32 rows x 2 lane groups)
-// then fall in 64 different banks.
+// with BM = 256 the 64 lanes of one fragment's metadata read (32 rows x 2
+// lane groups) then fall in 64 different banks (with BM = 128, in 32).
 
 template <int BM_, int BN_, int HB_>
 struct SpPairCfg {
@@ -740,9 +741,9 @@ struct SpPairCfg {
     static constexpr int E_SLOT = BM * E_ROW, E_PIECE_ROWS = BM / 8;
     static constexpr int A_BASE = 0, B_BASE = 2 * A_SLOT, E_BASE = B_BASE + 2 * B_STAGE;
     // Loads per thread per K tile: half an A pair slot, a B stage, an eighth
-    // of a metadata slot.  HB of the B loads go under the last MFMA step of
-    // the tile before (with the A and metadata loads), the rest under the
-    // first step of the tile before.
+    // of a metadata slot.  B tile u's first HB loads go under the last MFMA
+    // step of tile u - 2 (with that step's A and metadata loads), the rest
+    // under the first step of tile u - 1.
     static constexpr int LA = BM * CH / 2 / NT, LB = BN * CH / NT, LE = E_PIECE_ROWS * (E_ROW / 4) / NT;
     static constexpr int HB = HB_;
     static constexpr int EPAD = 8;                         // fp16 pad per epilogue row
