@@ -189,6 +189,32 @@ def main():
         sweep[str(K)] = round(achieved, 1)
         extra["gemm_k_sweep_tflops"] = sweep
 
+        # ---- GEMM at cube sizes whose 256 x 256 tiles leave the last round
+        # of workgroups mostly empty: the default call (leading rows in whole
+        # rounds, the rest with a smaller tile) vs one launch of the big tile
+        quant = {}
+        for n3 in (7168, 6144):
+            a3 = torch.from_numpy(inputs.uniform_f16((n3, n3), 0, 0)).cuda()
+            b3 = torch.from_numpy(inputs.uniform_f16((n3, n3), 0, 1)).cuda()
+            c3 = torch.empty((n3, n3), dtype=torch.float16, device="cuda")
+            f3 = 2.0 * n3 ** 3
+            # the two launch plans alternate batch by batch, so that both see
+            # the same clock and power state
+            plans = (gf.prepare_gemm_f16_nt(a3, b3, c3),
+                     gf.prepare_gemm_f16_nt(a3, b3, c3, cfg=gf.gemm_default_config(n3, n3, n3)))
+            times = ([], [])
+            for p in plans:
+                time_batch(torch, p, 1, 5, trials=1)
+            for _ in range(5):
+                for i, p in enumerate(plans):
+                    times[i].append(time_batch(torch, p, 10, 0, trials=1))
+            t_def, t_one = float(np.median(times[0])), float(np.median(times[1]))
+            quant["%d^3" % n3] = {"default_tflops": round(f3 / t_def / 1e12, 1),
+                                  "one_launch_tflops": round(f3 / t_one / 1e12, 1)}
+            del a3, b3, c3
+        log("gemm wave-quantised cubes: %s" % quant)
+        extra["gemm_row_split"] = quant
+
         # other operand layouts at 8192^3: B stored K x N (and A K x M)
         lay = {}
         Bt = B.t().contiguous()

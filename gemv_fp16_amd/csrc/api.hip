@@ -69,6 +69,36 @@ gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
     return make_cfg(64, 64, 64, 2, 256, 0);
 }
 
+// Wave quantisation of the default tile.  One 256 x 256 workgroup fills a
+// CU, so the tiles run in rounds of 256; when the last round is at most half
+// full (7168^2: 784 tiles = 3 rounds + 16 tiles, and those 16 take as long as
+// a full round), the leading tile-rows that fill whole rounds run as one
+// launch and the remaining rows (at most 1024) as a second launch with a
+// tile that spreads them over the chip.  Returns the row count of the first
+// part; M means no split.  A and C rows are contiguous, so both parts are
+// ordinary launches on row ranges, and every output of a 128 x 128 tail is
+// computed by the same 32 x 32 MFMAs over K in the same order as with the
+// big tile: the result does not depend on the split.
+int row_split(int M, int N, const gf_gemm_cfg& big)
+{
+    constexpr int64_t kCus = 256, kMaxTailRows = 1024;
+    if (big.block_m != 256 || big.block_n != 256) return M;
+    const int64_t tn = ceil_div(N, 256), tiles = (int64_t)ceil_div(M, 256) * tn;
+    const int64_t rounds = (tiles + kCus - 1) / kCus;
+    if (rounds < 2 || tiles - kCus * (rounds - 1) > kCus / 2) return M;
+    const int64_t m1 = (kCus * (rounds - 1) / tn) * 256;
+    if (m1 < 256 || m1 >= M || M - m1 > kMaxTailRows) return M;
+    return (int)m1;
+}
+
+// Tile of the rows past the split: 128 x 128 tiles, four stages when one
+// round of them covers the rows, else two stages (two workgroups per CU).
+gf_gemm_cfg tail_gemm_cfg(int M, int N)
+{
+    const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
+    return t128 <= 256 ? make_cfg(128, 128, 64, 4, 256, 0, 2) : make_cfg(128, 128, 64, 2, 256, 0, 2);
+}
+
 // Split-K tile: the largest tile (among the configs compiled with the fp32
 // epilogues) whose tiles x slices still give every CU a workgroup.  The
 // sweep at M = N = 1024, K = 16384 found exactly that: 128 x 128 / 3 stages
@@ -419,6 +449,21 @@ int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void
                            static_cast<hipStream_t>(stream));
     }
     const gf_gemm_cfg cfg = default_gemm_cfg(M, N, K);
+    const int m1 = row_split(M, N, cfg);
+    if (m1 < M) {
+        const int rc = validate_gemm(A, B, C, M, N, K, 2);
+        if (rc) return rc;
+        const int r1 = gemm_f16_nt_cfg(A, B, C, m1, N, K, &cfg, stream);
+        if (r1) return r1;
+        const char* At = static_cast<const char*>(A) + (size_t)m1 * K * 2;
+        char* Ct = static_cast<char*>(C) + (size_t)m1 * N * 2;
+        const int mt = M - m1;
+        if (skinny_fits(At, B, mt, K))
+            return skinny_impl(At, B, Ct, mt, N, K, default_skinny_cfg(mt, N, K),
+                               static_cast<hipStream_t>(stream));
+        const gf_gemm_cfg tail = tail_gemm_cfg(mt, N);
+        return gemm_f16_nt_cfg(At, B, Ct, mt, N, K, &tail, stream);
+    }
     return gemm_f16_nt_cfg(A, B, C, M, N, K, &cfg, stream);
 }
 

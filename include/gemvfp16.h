@@ -49,6 +49,12 @@ enum { GF_SPLITK_ATOMIC = 0, GF_SPLITK_TWOPASS = 1, GF_SPLITK_F16 = 2 };
  * Defined by the TileLang FP16 matmul autotune benchmark page, sections 1
  * and 2 (C = A B^T with A(M,K), B(N,K), C(M,N), fp16 operands, fp32
  * accumulation, transpose_B) and the autotune tutorial page's reference().
+ * The library picks the launch: M <= 16 takes the skinny kernel; when the
+ * default tile would leave its last round of workgroups at most half full,
+ * the call enqueues two launches on `stream`, the leading rows of C in whole
+ * rounds and the rest with a smaller tile (same result bits as one launch
+ * of the default tile, except where the rest is 16 rows or fewer and takes
+ * the skinny kernel).
  */
 int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void* stream);
 

@@ -167,6 +167,54 @@ def test_gemm_8192_integer_sampled():
 
 
 # ---------------------------------------------------------------------------
+# wave-quantised shapes: the default launch runs the leading tile-rows in whole
+# rounds of 256 x 256 tiles and the remaining rows as a second launch
+# ---------------------------------------------------------------------------
+
+def split_rows(M, N):
+    """The row count of the first launch (M: no split), from the library's
+    rule: the last round of 256 x 256 tiles over 256 CUs at most half full,
+    a tail of at most 1024 rows."""
+    tn = -(-N // 256)
+    tiles = -(-M // 256) * tn
+    rounds = -(-tiles // 256)
+    if rounds < 2 or tiles - 256 * (rounds - 1) > 128:
+        return M
+    m1 = (256 * (rounds - 1) // tn) * 256
+    return m1 if 256 <= m1 < M and M - m1 <= 1024 else M
+
+
+# (M, N, K, tail form): a 256-row tail (one round of 128 x 128 tiles), a
+# 768-row tail (two workgroups per CU), an 8-row tail (the skinny kernel), and
+# ragged N and K.
+ROW_SPLIT_SHAPES = [(7168, 7168, 512, "mfma"), (6144, 6144, 256, "mfma"), (6920, 7168, 256, "skinny"),
+                    (7268, 7000, 264, "mfma")]
+
+
+@pytest.mark.parametrize("M,N,K,tail", ROW_SPLIT_SHAPES)
+def test_gemm_row_split(M, N, K, tail):
+    m1 = split_rows(M, N)
+    assert m1 < M
+    ij = sample_ij(M, N, 3000, seed=M + K)
+    edge = [[r, c] for r in (0, m1 - 1, m1, min(m1 + 1, M - 1), M - 1) for c in (0, N // 2, N - 1)]
+    ij = np.concatenate([ij, edge]).astype(np.int64)
+    A, B = operands("integer", M, N, K, seed=3)
+    _say("gemm row split %dx%dx%d (rows %d + %d) integer" % (M, N, K, m1, M - m1))
+    got = run_gemm(A, B)
+    ref16, _ = oracle.gemm_nt_entries(A, B, ij)
+    assert np.array_equal(got[ij[:, 0], ij[:, 1]], ref16)
+    A, B = operands("uniform", M, N, K, seed=3)
+    _say("gemm row split %dx%dx%d uniform" % (M, N, K))
+    got = run_gemm(A, B)
+    ref16, _ = oracle.gemm_nt_entries(A, B, ij)
+    check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "row split %dx%dx%d" % (M, N, K))
+    if tail == "mfma":
+        # the same MFMAs over K in the same order: one launch of the big tile gives the same bits
+        whole = run_gemm(A, B, cfg=gf.gemm_default_config(M, N, K))
+        assert np.array_equal(got, whole), "row split changed the result"
+
+
+# ---------------------------------------------------------------------------
 # other operand layouts: A (M, K) or (K, M), B (N, K) or (K, N)
 # ---------------------------------------------------------------------------
 
