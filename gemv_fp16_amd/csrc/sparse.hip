@@ -80,6 +80,26 @@ gf_sp_cfg default_sp_cfg(int M, int N)
     return c;
 }
 
+// Wave quantisation of the 256 x 256 tile (one workgroup per CU, so tiles
+// run in rounds of 256): when the last round would be at most half full, the
+// leading tile-rows that fill whole rounds run as one launch and the
+// remaining rows (at most 1024) as a second launch with the tile the library
+// picks for their size.  Returns the row count of the first part; M means no
+// split.  A_sparse, E and C rows are contiguous, and every tile form issues
+// the same sparse MFMAs over K in the same order, so the result does not
+// depend on the split.
+int sp_row_split(int M, int N, const gf_sp_cfg& c)
+{
+    constexpr int64_t kCus = 256, kMaxTailRows = 1024;
+    if (c.block_m != 256 || c.block_n != 256) return M;
+    const int64_t tn = ceil_div(N, 256), tiles = (int64_t)ceil_div(M, 256) * tn;
+    const int64_t rounds = (tiles + kCus - 1) / kCus;
+    if (rounds < 2 || tiles - kCus * (rounds - 1) > kCus / 2) return M;
+    const int64_t m1 = (kCus * (rounds - 1) / tn) * 256;
+    if (m1 < 256 || m1 >= M || M - m1 > kMaxTailRows) return M;
+    return (int)m1;
+}
+
 int validate_sp(const void* Asp, const void* E, const void* B, const void* C, int M, int N, int K)
 {
     if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return GF_ERR_INVALID_ARG;
@@ -140,6 +160,16 @@ int gemm_sp_f16_nt_cfg(const void* A_sparse, const void* E, const void* B, void*
     const int v = validate_sp(A_sparse, E, B, C, M, N, K);
     if (v != GF_OK) return v;
     const gf_sp_cfg c = cfg ? *cfg : default_sp_cfg(M, N);
+    const int m1 = cfg ? M : sp_row_split(M, N, c);
+    if (m1 < M) {
+        const int rc = sp_impl(A_sparse, E, B, C, m1, N, K, c, (hipStream_t)stream);
+        if (rc != GF_OK) return rc;
+        // row m1 of A_sparse starts m1 * K bytes in, of E m1 * K / 8 bytes, of C m1 * N * 2 bytes
+        return sp_impl(static_cast<const char*>(A_sparse) + (size_t)m1 * K,
+                       static_cast<const char*>(E) + (size_t)m1 * (K / 8), B,
+                       static_cast<char*>(C) + (size_t)m1 * N * 2, M - m1, N, K, default_sp_cfg(M - m1, N),
+                       (hipStream_t)stream);
+    }
     return sp_impl(A_sparse, E, B, C, M, N, K, c, (hipStream_t)stream);
 }
 

@@ -275,6 +275,10 @@ int sp24_compress_f16(const void* A, void* A_sparse, void* E, int M, int K, void
  * gives an unspecified result for its row (no fault).  GF_ERR_INVALID_ARG for
  * K % 16 != 0, negative sizes, NULL or misaligned pointers, or any operand of
  * 2^31 elements or more.  M == 0 or N == 0 is a no-op; K == 0 writes +0.
+ * As for gemm_f16_nt, when the default tile would leave its last round of
+ * workgroups at most half full, the call enqueues two launches on `stream`
+ * (the leading rows in whole rounds, the rest with a smaller tile; the same
+ * result bits as one launch).
  */
 int gemm_sp_f16_nt(const void* A_sparse, const void* E, const void* B, void* C, int M, int N, int K,
                    void* stream);

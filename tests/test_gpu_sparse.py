@@ -266,3 +266,29 @@ def test_sparse_default_paired_shape_sampled():
     ij = sample_ij(M, N, 4000, seed=13)
     ij = np.concatenate([ij, [[M - 1, N - 1], [0, N - 1], [M - 1, 0]]]).astype(np.int64)
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))
+
+
+@pytest.mark.parametrize("M,N,K", [(7168, 7168, 512), (6144, 6144, 256)])
+def test_sparse_row_split(M, N, K):
+    """Shapes whose last round of 256 x 256 tiles is at most half full: the
+    default call splits the rows (7168: 6912 + 256, 6144: 5376 + 768).
+    Integer inputs bit-exact on sampled entries around the split; uniform
+    inputs give the same bits as one launch of the default tile."""
+    m1 = {7168: 6912, 6144: 5376}[M]
+    ij = sample_ij(M, N, 3000, seed=M + K)
+    edge = [[r, c] for r in (0, m1 - 1, m1, M - 1) for c in (0, N // 2, N - 1)]
+    ij = np.concatenate([ij, edge]).astype(np.int64)
+    A = inputs.sparse24("integer", (M, K), seed=4)
+    B = inputs.make("integer", (N, K), seed=4, stream_id=inputs.STREAM_B)
+    Asp, E = oracle.sp24_compress(A)
+    _say("sparse row split %dx%dx%d integer" % (M, N, K))
+    got = sp_run(Asp, E, B)
+    assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))
+    A = inputs.sparse24("uniform", (M, K), seed=4)
+    B = inputs.make("uniform", (N, K), seed=4, stream_id=inputs.STREAM_B)
+    Asp, E = oracle.sp24_compress(A)
+    _say("sparse row split %dx%dx%d uniform" % (M, N, K))
+    got = sp_run(Asp, E, B)
+    check_f16_tolerance(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij), "sparse row split")
+    whole = sp_run(Asp, E, B, gf.sp_default_config(M, N, K))
+    assert np.array_equal(got, whole), "row split changed the sparse result"
