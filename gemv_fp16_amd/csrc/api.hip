@@ -60,12 +60,25 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched
 // XCD-aware tile order is 5 % ahead at K = 1024, where each tile's short K
 // loop leaves operand re-reads less time to hide, ties at K = 4096, and is
 // within noise of plain order at K = 8192, where plain order is kept.
+// The largest tile that still gives every CU a workgroup, in the form
+// measured fastest for it (tile sweeps at 8192^3 and at 2048 x 4096,
+// 2048 x 2048 and 1024 x 4096 x 8192; candidates timed side by side at ten
+// mid-size shapes with K = 1024 .. 8192):
+//  * 256 x 128 needs K >= 2048: below that the per-workgroup start and
+//    epilogue weigh more, and two 128 x 128 workgroups per CU hide them;
+//  * 128 x 128 with four stages (one workgroup per CU) while one round of
+//    them covers the shape, two stages (two per CU, one round of 512) past it.
+// Every tile chosen here is compiled with its masked variant too, so
+// unaligned operands run the same tile.
 gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
 {
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+    const int64_t t25612 = (int64_t)ceil_div(M, 256) * ceil_div(N, 128);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     if (t256 >= 256) return make_cfg(256, 256, 64, 2, 256, K <= 4096 ? 1 : 0, 2);
-    if (t128 >= 128) return make_cfg(128, 128, 64, 2, 256, 0);
+    if (t25612 >= 256 && K >= 2048) return make_cfg(256, 128, 64, 3, 256, 0, 2);
+    if (t128 >= 128 && t128 <= 256) return make_cfg(128, 128, 64, 4, 256, 0, 2);
+    if (t128 > 256) return make_cfg(128, 128, 64, 2, 256, 0);
     return make_cfg(64, 64, 64, 2, 256, 0);
 }
 

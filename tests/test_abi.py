@@ -173,6 +173,13 @@ def test_config_tables(L):
     assert len(gf.gemv_configs()) >= 30
     d = gf.gemm_default_config(8192, 8192, 8192)
     assert (d["block_m"], d["block_n"]) == (256, 256)
+    # mid-size shapes: the largest tile that still fills the 256 CUs
+    d2 = gf.gemm_default_config(2048, 4096, 8192)
+    assert (d2["block_m"], d2["block_n"], d2["stages"], d2["schedule"]) == (256, 128, 3, 2)
+    d3 = gf.gemm_default_config(2048, 2048, 8192)
+    assert (d3["block_m"], d3["block_n"], d3["stages"], d3["schedule"]) == (128, 128, 4, 2)
+    d4 = gf.gemm_default_config(4096, 2048, 1024)        # short K: two 128 x 128 workgroups per CU
+    assert (d4["block_m"], d4["block_n"], d4["stages"]) == (128, 128, 2)
     assert any(c == {**d, "raster": 1} for c, ok in cfgs if ok)
     for c, ok in cfgs:
         if c["schedule"] == 1:

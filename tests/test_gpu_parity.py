@@ -135,6 +135,38 @@ def test_gemm_every_compiled_config():
     assert n >= 180
 
 
+def test_gemm_every_config_masked_path():
+    """Every tile config on operands the 128-bit path cannot take (K % 8 != 0,
+    ragged M and N): a config compiled with its masked variant computes the
+    product, any other one refuses with GF_ERR_UNSUPPORTED.  The configs
+    the library picks by default all have the masked variant."""
+    M, N, K = 140, 100, 1004
+    Ai = inputs.integer_f16((M, K), 7, 0)
+    Bi = inputs.integer_f16((N, K), 7, 1)
+    ref = oracle.gemm_nt_f16(Ai, Bi)
+    dA, dB = dev(Ai), dev(Bi)
+    ran = []
+    for cfg, ok in gf.gemm_configs():
+        if not ok:
+            continue
+        c = dict(cfg, raster=0)
+        try:
+            C = gf.gemm_f16_nt(dA, dB, cfg=c)
+        except RuntimeError as e:
+            assert "UNSUPPORTED" in str(e), e
+            continue
+        _say("masked cfg %s" % c)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(C), ref), c
+        ran.append(c)
+    for shape in ((8192, 8192, 8192), (2048, 4096, 8192), (2048, 2048, 8192), (4096, 2048, 1024), (300, 300, 64)):
+        d = dict(gf.gemm_default_config(*shape), raster=0)
+        assert d in ran, "default %s for %s has no masked variant" % (d, shape)
+    for tail in ({"block_m": 128, "block_n": 128, "block_k": 64, "stages": 4, "threads": 256, "raster": 0, "schedule": 2},
+                 {"block_m": 128, "block_n": 128, "block_k": 64, "stages": 2, "threads": 256, "raster": 0, "schedule": 2}):
+        assert tail in ran, "row-split tail %s has no masked variant" % tail
+
+
 def test_gemm_power_of_two_scaling_bit_exact():
     """Doubling A doubles every fp32 partial sum exactly, so C doubles."""
     A, B = operands("uniform", 384, 256, 512, seed=5)
