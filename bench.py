@@ -215,6 +215,21 @@ def main():
         log("gemm wave-quantised cubes: %s" % quant)
         extra["gemm_row_split"] = quant
 
+        # ---- GEMM at mid-size shapes (fewer than 256 tiles of 256 x 256)
+        mid = {}
+        for (m4, n4, k4) in ((2048, 4096, 8192), (2048, 2048, 8192), (1024, 4096, 8192)):
+            a4 = torch.from_numpy(inputs.uniform_f16((m4, k4), 0, 0)).cuda()
+            b4 = torch.from_numpy(inputs.uniform_f16((n4, k4), 0, 1)).cuda()
+            c4 = torch.empty((m4, n4), dtype=torch.float16, device="cuda")
+            t4 = time_batch(torch, gf.prepare_gemm_f16_nt(a4, b4, c4), 20, 5)
+            d4 = gf.gemm_default_config(m4, n4, k4)
+            mid["%dx%dx%d" % (m4, n4, k4)] = {"tflops": round(2.0 * m4 * n4 * k4 / t4 / 1e12, 1),
+                                              "tile": "%dx%d/%d stages/schedule %d" % (
+                                                  d4["block_m"], d4["block_n"], d4["stages"], d4["schedule"])}
+            del a4, b4, c4
+        log("gemm mid-size shapes: %s" % mid)
+        extra["gemm_mid_shapes"] = mid
+
         # other operand layouts at 8192^3: B stored K x N (and A K x M)
         lay = {}
         Bt = B.t().contiguous()

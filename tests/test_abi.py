@@ -180,6 +180,8 @@ def test_config_tables(L):
     assert (d3["block_m"], d3["block_n"], d3["stages"], d3["schedule"]) == (128, 128, 4, 2)
     d4 = gf.gemm_default_config(4096, 2048, 1024)        # short K: two 128 x 128 workgroups per CU
     assert (d4["block_m"], d4["block_n"], d4["stages"]) == (128, 128, 2)
+    d5 = gf.gemm_default_config(1024, 1024, 4096)        # small: 64 x 64, three stages
+    assert (d5["block_m"], d5["block_n"], d5["stages"]) == (64, 64, 3)
     assert any(c == {**d, "raster": 1} for c, ok in cfgs if ok)
     for c, ok in cfgs:
         if c["schedule"] == 1:

@@ -159,7 +159,8 @@ def test_gemm_every_config_masked_path():
         torch.cuda.synchronize()
         assert np.array_equal(host_u16(C), ref), c
         ran.append(c)
-    for shape in ((8192, 8192, 8192), (2048, 4096, 8192), (2048, 2048, 8192), (4096, 2048, 1024), (300, 300, 64)):
+    for shape in ((8192, 8192, 8192), (2048, 4096, 8192), (2048, 2048, 8192), (4096, 2048, 1024), (1024, 1024, 4096),
+                  (300, 300, 64)):
         d = dict(gf.gemm_default_config(*shape), raster=0)
         assert d in ran, "default %s for %s has no masked variant" % (d, shape)
     for tail in ({"block_m": 128, "block_n": 128, "block_k": 64, "stages": 4, "threads": 256, "raster": 0, "schedule": 2},
