@@ -402,17 +402,30 @@ int find_gemv(const gf_gemv_cfg& c)
 // per row in flight) is best when K/8 divides into 8 x 64 x 2 chunks; other
 // large shapes use one row per wave with 8 loads in flight; small ones are
 // launch-bound and take one chunk per lane at a time.
+// Launch shape from sweeps of every shape at N x K = 8192^2, 16384 x 4096,
+// 14336 x 4096, 4096 x 16384, 4096 x 14336, 2048^2 and 1024^2:
+//  * the split form (a workgroup's waves split K, the grid streams one band
+//    of W) where it was best, tall W with K a multiple of 8192;
+//  * else one row per wave, 4 chunks per lane in flight, 4 waves per
+//    workgroup: within 7 % of the best launch shape at every large shape;
+//  * smaller W: 2 chunks in flight and 1-wave workgroups from 2048^2 up,
+//    below that 8 waves with 1 chunk (launch-bound).
 gf_gemv_cfg default_gemv_cfg(int N, int K)
 {
     gf_gemv_cfg c;
-    if ((int64_t)N * K >= (int64_t)4096 * 4096) {
-        if (K % 8 == 0 && (K / 8) % (8 * 64 * 2) == 0 && K <= 32768) {
+    const int64_t nk = (int64_t)N * K;
+    c.blocks = 0;
+    c.rows_per_wave = 1;
+    if (nk >= (int64_t)4096 * 4096) {
+        if (N >= 8192 && K % 8192 == 0 && K <= 32768) {
             c.rows_per_wave = 2; c.unroll = 2; c.waves = 8; c.blocks = 512;
         } else {
-            c.rows_per_wave = 1; c.unroll = 8; c.waves = 8; c.blocks = 0;
+            c.unroll = 4; c.waves = 4;
         }
+    } else if (nk >= (int64_t)2048 * 2048) {
+        c.unroll = 2; c.waves = 1;
     } else {
-        c.rows_per_wave = 1; c.unroll = 1; c.waves = 8; c.blocks = 0;
+        c.unroll = 1; c.waves = 8;
     }
     return c;
 }

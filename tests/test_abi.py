@@ -191,6 +191,11 @@ def test_config_tables(L):
     assert d["raster"] in (0, 1)
     dg = gf.gemv_default_config(8192, 8192)
     assert {**dg, "blocks": 0} in gf.gemv_configs() and dg["blocks"] >= 0
+    assert dg["blocks"] > 0                                # tall W, K % 8192 == 0: the split form
+    dw = gf.gemv_default_config(4096, 16384)               # wide W: one row per wave
+    assert dw == {"rows_per_wave": 1, "unroll": 4, "waves": 4, "blocks": 0}
+    for n, k in ((16384, 4096), (2048, 2048), (1024, 1024), (7, 13)):
+        assert {**gf.gemv_default_config(n, k), "blocks": 0} in gf.gemv_configs()
     bad = gf.GemmCfg()
     assert L.gf_gemm_config_get(-1, ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
     assert L.gf_gemm_config_get(len(cfgs), ctypes.byref(bad)) == gf.GF_ERR_INVALID_ARG
