@@ -20,7 +20,8 @@ EXPORTS = (
     "gemm_f16_nt", "gemm_f16_nt_splitk", "gemv_f16",
     "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex", "gemm_f16_nt_splitk_f16",
     "gemm_f16_nt_cfg", "gemv_f16_cfg", "gemm_f16", "gemm_f16_nn", "gemm_f16_tn", "gemm_f16_cfg",
-    "gemm_f16_nt_skinny", "gf_skinny_config_count", "gf_skinny_config_get", "gemm_f16_nt_splitk_cfg",
+    "gemm_f16_nt_skinny", "gf_skinny_config_count", "gf_skinny_config_get", "gf_skinny_default_config",
+    "gemm_f16_nt_splitk_cfg",
     "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
     "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
     "sp24_compress_f16", "gemm_sp_f16_nt", "gemm_sp_f16_nt_cfg", "gf_sp_config_count",
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_nt_skinny.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.POINTER(SkinnyCfg), vp]
     L.gemm_f16_nt_splitk_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, ctypes.POINTER(GemmCfg), vp]
     L.gf_skinny_config_get.argtypes = [ci, ctypes.POINTER(SkinnyCfg)]
+    L.gf_skinny_default_config.argtypes = [ci, ci, ci, ctypes.POINTER(SkinnyCfg)]
     L.gemm_f16_nn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
     L.gemm_f16_tn.argtypes = [vp, vp, vp, ci, ci, ci, vp]
     L.gemm_f16_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ctypes.POINTER(GemmCfg), vp]
@@ -238,6 +240,12 @@ def skinny_configs() -> list:
         _check(L.gf_skinny_config_get(i, ctypes.byref(c)), "gf_skinny_config_get")
         out.append({"blocks": c.blocks, "unroll": c.unroll, "waves": c.waves, "stages": c.stages})
     return out
+
+
+def skinny_default_config(M: int, N: int, K: int) -> dict:
+    c = SkinnyCfg()
+    _check(lib().gf_skinny_default_config(M, N, K, ctypes.byref(c)), "gf_skinny_default_config")
+    return {"blocks": c.blocks, "unroll": c.unroll, "waves": c.waves, "stages": c.stages}
 
 
 def gemm_f16_nn(A, B, C=None, stream=None):

@@ -348,17 +348,36 @@ int find_skinny(const gf_skinny_cfg& c)
 // form (one 16-row block of B per workgroup, 4-step batches); from 5 rows
 // the LDS-staged form (three blocks of B share each A chunk, two chunks in
 // flight), when K is a multiple of its chunk.
-gf_skinny_cfg default_skinny_cfg(int M, int /*N*/, int K)
+// Skinny launch shape.  Tuned on an 8192 x 8192 B, then checked at
+// N x K = 4096 x 4096, 4096 x 14336, 2048 x 8192, 6144 x 6144, 14336 x 4096
+// and 28672 x 8192.  With fewer than 8192 rows of B:
+//  * the LDS form with one 16-row block per workgroup fills the chip (three
+//    blocks give 86 workgroups at N = 4096): 1.1-1.85x, also in place of
+//    the vector form for M = 5..8;
+//  * for M <= 2 and at least 32 M elements of B, 16-wave vector
+//    workgroups: 1.3-1.5x.
+gf_skinny_cfg default_skinny_cfg(int M, int N, int K)
 {
     gf_skinny_cfg c;
     c.waves = 8;
-    if (M <= kSkinnyVecMaxM && skinny_vec_fits(M, K, M <= 2 ? 8 : 4)) {
+    const bool small_n = N < 8192;
+    if (small_n && M <= 2 && (int64_t)N * K >= (int64_t)32 << 20 && skinny_vec_fits(M, K, 4)) {
+        c.blocks = 1; c.unroll = 4; c.waves = 16; c.stages = 1;
+        return c;
+    }
+    if (M <= kSkinnyVecMaxM && !(small_n && M > 4 && K % kSkinnyKc == 0) &&
+        skinny_vec_fits(M, K, M <= 2 ? 8 : 4)) {
         c.blocks = 1;
         c.unroll = M <= 2 ? 8 : 4;
         c.stages = 1;
         return c;
     }
-    if (M > 4 && K > 0 && K % kSkinnyKc == 0) {
+    if (M > 4 && K > 0 && K % kSkinnyKc == 0 && small_n) {
+        c.blocks = 1;
+        c.unroll = 0;
+        c.waves = N <= 4096 ? 16 : 8;
+        c.stages = N <= 4096 ? 4 : 3;
+    } else if (M > 4 && K > 0 && K % kSkinnyKc == 0) {
         c.blocks = 3;
         c.unroll = 0;
         c.stages = 2;
@@ -515,6 +534,13 @@ int gf_skinny_config_get(int i, gf_skinny_cfg* out)
     out->unroll = kSkinnyConfigs[i].unroll;
     out->waves = kSkinnyConfigs[i].waves;
     out->stages = kSkinnyConfigs[i].stages;
+    return GF_OK;
+}
+
+int gf_skinny_default_config(int M, int N, int K, gf_skinny_cfg* out)
+{
+    if (!out || M < 1 || M > kSkinnyMaxM || N < 0 || K < 0) return GF_ERR_INVALID_ARG;
+    *out = default_skinny_cfg(M, N, K);
     return GF_OK;
 }
 

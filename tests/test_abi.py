@@ -125,6 +125,31 @@ def test_skinny_validation(L):
     assert len(gf.skinny_configs()) >= 4
     out = gf.SkinnyCfg()
     assert L.gf_skinny_config_get(-1, ctypes.byref(out)) == gf.GF_ERR_INVALID_ARG
+    for m in (0, 17):
+        assert L.gf_skinny_default_config(m, 64, 64, ctypes.byref(out)) == gf.GF_ERR_INVALID_ARG
+    assert L.gf_skinny_default_config(4, 64, 64, None) == gf.GF_ERR_INVALID_ARG
+
+
+def test_skinny_default_rule():
+    """The skinny launch shape the library picks: every choice is compiled,
+    and the shape-dependent choices hold."""
+    compiled = gf.skinny_configs()
+    for n in (64, 2048, 4096, 6144, 8192, 28672):
+        for k in (64, 4096, 11008, 14336, 8192):
+            for m in range(1, 17):
+                assert gf.skinny_default_config(m, n, k) in compiled, (m, n, k)
+    d = gf.skinny_default_config
+    # 8192 rows of B and more: vector form to M = 8, then three 16-row blocks through LDS
+    assert d(1, 8192, 8192) == {"blocks": 1, "unroll": 8, "waves": 8, "stages": 1}
+    assert d(8, 8192, 8192) == {"blocks": 1, "unroll": 4, "waves": 8, "stages": 1}
+    assert d(16, 8192, 8192) == {"blocks": 3, "unroll": 0, "waves": 8, "stages": 2}
+    # fewer rows of B: one block per workgroup through LDS from M = 5
+    assert d(8, 4096, 14336) == {"blocks": 1, "unroll": 0, "waves": 16, "stages": 4}
+    assert d(16, 6144, 6144) == {"blocks": 1, "unroll": 0, "waves": 8, "stages": 3}
+    # and 16-wave vector workgroups for M <= 2 over a large B
+    assert d(1, 4096, 14336) == {"blocks": 1, "unroll": 4, "waves": 16, "stages": 1}
+    assert d(2, 2048, 8192)["waves"] == 8                   # 16 M elements: the 8-wave form
+    assert d(4, 6144, 6144) == {"blocks": 1, "unroll": 4, "waves": 8, "stages": 1}
 
 
 def test_splitk_f16_validation(L):

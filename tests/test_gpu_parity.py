@@ -389,6 +389,19 @@ def test_skinny_is_gemm_nt_for_small_m():
     assert np.array_equal(got, tiled)
 
 
+@pytest.mark.parametrize("M", [1, 2, 6, 16])
+@pytest.mark.parametrize("N,K", [(4096, 14336), (6144, 6144), (2056, 4096)])
+def test_skinny_default_fewer_rows_of_b(M, N, K):
+    """The library's launch shape with fewer than 8192 rows of B (16-wave
+    vector workgroups for M <= 2 over a large B, one 16-row block per
+    workgroup through LDS from M = 5), all outputs."""
+    A, B = operands("integer", M, N, K, seed=8)
+    _say("skinny default %dx%dx%d cfg %s" % (M, N, K, gf.skinny_default_config(M, N, K)))
+    assert np.array_equal(run_skinny(A, B), oracle.gemm_nt_f16(A, B))
+    A, B = operands("uniform", M, N, K, seed=8)
+    check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny %dx%dx%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("M", [4, 16])
 def test_skinny_decode_8192(M):
     """The decode-size case: M rows against an 8192 x 8192 B, all outputs."""
