@@ -348,39 +348,50 @@ int find_skinny(const gf_skinny_cfg& c)
 // form (one 16-row block of B per workgroup, 4-step batches); from 5 rows
 // the LDS-staged form (three blocks of B share each A chunk, two chunks in
 // flight), when K is a multiple of its chunk.
-// Skinny launch shape.  Tuned on an 8192 x 8192 B, then checked at
-// N x K = 4096 x 4096, 4096 x 14336, 2048 x 8192, 6144 x 6144, 14336 x 4096
-// and 28672 x 8192.  With fewer than 8192 rows of B:
-//  * the LDS form with one 16-row block per workgroup fills the chip (three
-//    blocks give 86 workgroups at N = 4096): 1.1-1.85x, also in place of
-//    the vector form for M = 5..8;
-//  * for M <= 2 and at least 32 M elements of B, 16-wave vector
-//    workgroups: 1.3-1.5x.
+// Skinny launch shape, from sweeps of the compiled shapes for M = 1..16 at
+// N x K = 8192^2, 4096^2, 4096 x 14336, 2048 x 8192, 6144^2, 4096 x 11008,
+// 8192 x 4096, 14336 x 4096, 16384 x 4096, 28672 x 4096, 8192 x 2048,
+// 16384 x 2048 and 12288 x 6144:
+//  * vector form (M <= 8): 8-wave workgroups where rows are long (K >= 8192)
+//    or B is small; otherwise 16 waves with 4 chunks per lane in flight, for
+//    M <= 2 over at least 32 M elements of B and for M <= 4 from 8192 rows
+//    of B.  The 16-wave form also covers K not a multiple of 4096, where the
+//    8-chunk form does not fit.
+//  * LDS form (K % 512 == 0) from M = 5 below 8192 rows of B, with one
+//    16-row block per workgroup (three blocks give 86 workgroups at
+//    N = 4096); from 8192 rows for M > 8, or M > 4 at K <= 2048, with one
+//    block per workgroup up to K = 4096 (two up to 2048) and three beyond.
 gf_skinny_cfg default_skinny_cfg(int M, int N, int K)
 {
     gf_skinny_cfg c;
     c.waves = 8;
     const bool small_n = N < 8192;
-    if (small_n && M <= 2 && (int64_t)N * K >= (int64_t)32 << 20 && skinny_vec_fits(M, K, 4)) {
-        c.blocks = 1; c.unroll = 4; c.waves = 16; c.stages = 1;
-        return c;
+    const bool lds_ok = K > 0 && K % kSkinnyKc == 0;
+    const bool lds_first = lds_ok && M > 4 && (small_n || K <= 2048);
+    if (M <= kSkinnyVecMaxM && !lds_first) {
+        const int unroll = M <= 2 ? 8 : 4;
+        const bool vec8 = skinny_vec_fits(M, K, unroll);
+        const bool vec16 = skinny_vec_fits(M, K, 4) &&
+                           (M <= 2 ? (int64_t)N * K >= (int64_t)32 << 20 : M <= 4 && !small_n);
+        if (vec8 && (K >= 8192 || !vec16)) {
+            c.blocks = 1;
+            c.unroll = unroll;
+            c.stages = 1;
+            return c;
+        }
+        if (vec16) {
+            c.blocks = 1;
+            c.unroll = 4;
+            c.waves = 16;
+            c.stages = 1;
+            return c;
+        }
     }
-    if (M <= kSkinnyVecMaxM && !(small_n && M > 4 && K % kSkinnyKc == 0) &&
-        skinny_vec_fits(M, K, M <= 2 ? 8 : 4)) {
-        c.blocks = 1;
-        c.unroll = M <= 2 ? 8 : 4;
-        c.stages = 1;
-        return c;
-    }
-    if (M > 4 && K > 0 && K % kSkinnyKc == 0 && small_n) {
-        c.blocks = 1;
+    if (lds_ok && M > 4) {
+        c.blocks = small_n ? 1 : (K <= 2048 ? 2 : (K <= 4096 ? 1 : 3));
         c.unroll = 0;
-        c.waves = N <= 4096 ? 16 : 8;
-        c.stages = N <= 4096 ? 4 : 3;
-    } else if (M > 4 && K > 0 && K % kSkinnyKc == 0) {
-        c.blocks = 3;
-        c.unroll = 0;
-        c.stages = 2;
+        c.waves = small_n && N <= 4096 ? 16 : 8;
+        c.stages = !small_n ? 2 : (N <= 4096 ? 4 : 3);
     } else {
         c.blocks = M <= 4 ? 1 : 2;
         c.unroll = M <= 4 ? 4 : 2;

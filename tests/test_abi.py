@@ -135,11 +135,11 @@ def test_skinny_default_rule():
     and the shape-dependent choices hold."""
     compiled = gf.skinny_configs()
     for n in (64, 2048, 4096, 6144, 8192, 28672):
-        for k in (64, 4096, 11008, 14336, 8192):
+        for k in (64, 2048, 2560, 4096, 6144, 11008, 14336, 8192, 12288):
             for m in range(1, 17):
                 assert gf.skinny_default_config(m, n, k) in compiled, (m, n, k)
     d = gf.skinny_default_config
-    # 8192 rows of B and more: vector form to M = 8, then three 16-row blocks through LDS
+    # 8192 x 8192: vector form to M = 8, then three 16-row blocks through LDS
     assert d(1, 8192, 8192) == {"blocks": 1, "unroll": 8, "waves": 8, "stages": 1}
     assert d(8, 8192, 8192) == {"blocks": 1, "unroll": 4, "waves": 8, "stages": 1}
     assert d(16, 8192, 8192) == {"blocks": 3, "unroll": 0, "waves": 8, "stages": 2}
@@ -150,6 +150,13 @@ def test_skinny_default_rule():
     assert d(1, 4096, 14336) == {"blocks": 1, "unroll": 4, "waves": 16, "stages": 1}
     assert d(2, 2048, 8192)["waves"] == 8                   # 16 M elements: the 8-wave form
     assert d(4, 6144, 6144) == {"blocks": 1, "unroll": 4, "waves": 8, "stages": 1}
+    # from 8192 rows of B with rows shorter than 8192: 16-wave vector workgroups for M <= 4
+    # (also where K is not a multiple of 4096), one or two blocks per LDS workgroup beyond
+    assert d(4, 28672, 4096) == {"blocks": 1, "unroll": 4, "waves": 16, "stages": 1}
+    assert d(1, 12288, 6144) == {"blocks": 1, "unroll": 4, "waves": 16, "stages": 1}
+    assert d(16, 16384, 4096) == {"blocks": 1, "unroll": 0, "waves": 8, "stages": 2}
+    assert d(8, 8192, 2048) == {"blocks": 2, "unroll": 0, "waves": 8, "stages": 2}
+    assert d(16, 8192, 2048) == {"blocks": 2, "unroll": 0, "waves": 8, "stages": 2}
 
 
 def test_splitk_f16_validation(L):

@@ -389,12 +389,13 @@ def test_skinny_is_gemm_nt_for_small_m():
     assert np.array_equal(got, tiled)
 
 
-@pytest.mark.parametrize("M", [1, 2, 6, 16])
-@pytest.mark.parametrize("N,K", [(4096, 14336), (6144, 6144), (2056, 4096)])
-def test_skinny_default_fewer_rows_of_b(M, N, K):
-    """The library's launch shape with fewer than 8192 rows of B (16-wave
-    vector workgroups for M <= 2 over a large B, one 16-row block per
-    workgroup through LDS from M = 5), all outputs."""
+@pytest.mark.parametrize("M", [1, 2, 4, 6, 16])
+@pytest.mark.parametrize("N,K", [(4096, 14336), (6144, 6144), (2056, 4096), (12288, 6144), (16384, 2048),
+                                 (8200, 4096)])
+def test_skinny_default_shapes(M, N, K):
+    """The library's launch shape where it depends on the size of B (16-wave
+    vector workgroups, one or two 16-row blocks per LDS workgroup), all
+    outputs."""
     A, B = operands("integer", M, N, K, seed=8)
     _say("skinny default %dx%dx%d cfg %s" % (M, N, K, gf.skinny_default_config(M, N, K)))
     assert np.array_equal(run_skinny(A, B), oracle.gemm_nt_f16(A, B))
