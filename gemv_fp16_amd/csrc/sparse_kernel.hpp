@@ -148,7 +148,8 @@ struct SpCfg {
     static constexpr int A_BYTES = BM * CHA * 16, B_BYTES = BN * CHB * 16;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     // Metadata ring: slot j holds K tiles 2j and 2j+1 of every tile row
-    // (16 bytes per row), three slots after the operand stages.
+    // (16 bytes per row, dword positions keyed by sp_ekey), three slots after
+    // the operand stages.
     static constexpr int E_SLOT = BM * EDW * 4 * 2, E_SLOTS = 3;
     static constexpr int E_BASE = STAGES * STAGE_BYTES;
     // Loads per thread per K tile: A_sparse chunks, B chunks, E dwords (half a
@@ -169,6 +170,15 @@ struct SpCfg {
 // lanes that the LDS serves together read one chunk index of 16 consecutive
 // rows, and the key puts those reads in 16 different bank slots.
 __device__ __forceinline__ int sp_key(int row, int ch) { return (row / (16 / ch)) % ch; }
+
+// Metadata ring slot: row r's 16 bytes are dwords d = 2 h + g (K tile 2 j + h
+// of the slot, lane group g's index words), stored at dword position
+// d ^ sp_ekey(r).  A 4-byte LDS read is served 32 lanes at a time from 32
+// banks; the 32 lanes of a lane group read 32 consecutive rows, 16 bytes
+// apart, so without the key rows 8 apart share a bank (measured: 8 cycles per
+// read instead of 2).  The key gives rows r, r + 8, r + 16 and r + 24
+// different positions, which puts the 32 reads in 32 banks.
+__device__ __forceinline__ int sp_ekey(int row) { return (row / 8) % 4; }
 
 // ---------------------------------------------------------------------------
 // Staging
@@ -201,9 +211,11 @@ struct SpLoader {
             row = s / Cfg::CHB;
             kk = ((s % Cfg::CHB) ^ sp_key(row, Cfg::CHB)) * 8;
         } else {
-            // dword d = s % 4 of the row's 16 metadata bytes of a two-tile slot
+            // position s % 4 of the row's 16 metadata bytes of a two-tile slot
+            // holds dword (s % 4) ^ key (the half's first row is a multiple of 32,
+            // so the key of the row within the half is that within the tile)
             row = s / 4;
-            kk = (s % 4) * 32;
+            kk = ((s % 4) ^ sp_ekey(row)) * 32;
         }
     }
 
@@ -347,7 +359,7 @@ __device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char
                    v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
         *(GF_LDS u32x4*)(stage + Cfg::A_BYTES + s * 16) = w;
     }
-    GF_LDS char* eslot = smem + Cfg::E_BASE + ((t / 2) % Cfg::E_SLOTS) * Cfg::E_SLOT + (t % 2) * 8;
+    GF_LDS char* eslot = smem + Cfg::E_BASE + ((t / 2) % Cfg::E_SLOTS) * Cfg::E_SLOT;
     for (int s = tid; s < Cfg::BM * Cfg::EDW; s += Cfg::NT) {
         const int row = s / Cfg::EDW, gr = m0 + row;
         const int w0 = (k0 + (s % Cfg::EDW) * 32) / 16;   // first metadata word
@@ -356,7 +368,7 @@ __device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char
             if (w0 < a.K / 16) d = a.E[(size_t)gr * (a.K / 16) + w0];
             if (w0 + 1 < a.K / 16) d |= (uint32_t)a.E[(size_t)gr * (a.K / 16) + w0 + 1] << 16;
         }
-        *(GF_LDS uint32_t*)(eslot + row * 16 + (s % Cfg::EDW) * 4) = d;
+        *(GF_LDS uint32_t*)(eslot + row * 16 + ((((t % 2) * 2 + s % Cfg::EDW) ^ sp_ekey(row)) * 4)) = d;
     }
 }
 
@@ -366,7 +378,8 @@ __device__ __forceinline__ void sp_load_tile_masked(const SpArgs& a, GF_LDS char
 
 template <class Cfg>
 struct SpReader {
-    int oa, ob, oe;   // lane byte offsets of fragment 0 in the A and B regions and in a metadata slot
+    int oa, ob;       // lane byte offsets of fragment 0 in the A and B regions
+    int oe0, oe1;     // the same in a metadata slot, for its first and its second K tile
     int ka, kb;       // swizzle keys (the same for every fragment of the lane)
     int g;            // lane group
 
@@ -379,7 +392,9 @@ struct SpReader {
         ka = sp_key(ra, Cfg::CHA);
         ob = Cfg::A_BYTES + rb * Cfg::CHB * 16;
         kb = sp_key(rb, Cfg::CHB);
-        oe = ra * 16 + g * 4;
+        const int ke = sp_ekey(ra);              // rows ra + 32 F share it
+        oe0 = ra * 16 + ((g ^ ke) * 4);
+        oe1 = ra * 16 + (((2 + g) ^ ke) * 4);
     }
     template <int F, int S>
     __device__ __forceinline__ half8 a(const GF_LDS char* st) const
@@ -395,15 +410,15 @@ struct SpReader {
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     }
     // Metadata words 2g (step 0, low half) and 2g + 1 (step 1, high half) of
-    // K tile u: `et` is the ring address of u's 8 bytes in row 0.
+    // K tile u: `et` is the lane's address of them for fragment 0 (e_tile).
     template <int F>
     __device__ __forceinline__ uint32_t e(const GF_LDS char* et) const
     {
-        return *(const GF_LDS uint32_t*)(et + oe + F * 32 * 16);
+        return *(const GF_LDS uint32_t*)(et + F * 32 * 16);
     }
-    __device__ __forceinline__ static const GF_LDS char* e_tile(const GF_LDS char* smem, int u)
+    __device__ __forceinline__ const GF_LDS char* e_tile(const GF_LDS char* smem, int u) const
     {
-        return smem + Cfg::E_BASE + ((u / 2) % Cfg::E_SLOTS) * Cfg::E_SLOT + (u % 2) * 8;
+        return smem + Cfg::E_BASE + ((u / 2) % Cfg::E_SLOTS) * Cfg::E_SLOT + ((u & 1) ? oe1 : oe0);
     }
 };
 
@@ -626,7 +641,7 @@ __global__ __launch_bounds__(256) void sp_gemm_kernel(SpArgs a)
         lds_barrier();
         if (nk > 0) ld.template issue_range<0, H>(a, stage_ptr(S - 1), (S - 1) * Cfg::BK, no_e, wave);
         {
-            const GF_LDS char* et = SpReader<Cfg>::e_tile(smem, 0);
+            const GF_LDS char* et = rd.e_tile(smem, 0);
             static_for<Cfg::FM>([&](auto f) { e[f] = rd.template e<decltype(f)::value>(et); });
         }
         static_for<Cfg::FM>([&](auto f) { f0.a[f] = rd.template a<decltype(f)::value, 0>(stage_ptr(0)); });
@@ -644,7 +659,7 @@ __global__ __launch_bounds__(256) void sp_gemm_kernel(SpArgs a)
                                          (t + S - 1) * Cfg::BK, eh, wave);
             wait_vmcnt<Cfg::LPS * (S - 2)>();    // tile t + 1 landed
             lds_barrier();                        // B(t)
-            sp_step<Cfg, 0, 0, H>(acc, f1, hi, f0, e, rd, stage_ptr(s1), SpReader<Cfg>::e_tile(smem, t + 1), ld,
+            sp_step<Cfg, 0, 0, H>(acc, f1, hi, f0, e, rd, stage_ptr(s1), rd.e_tile(smem, t + 1), ld,
                                   stage_ptr(s0), (t + S) * Cfg::BK, no_e, wave);
         }
         for (; t < nk; ++t) {
@@ -658,7 +673,7 @@ __global__ __launch_bounds__(256) void sp_gemm_kernel(SpArgs a)
             lds_barrier();
             ld.template issue_range<0, H>(a, stage_ptr(s0), (t + S) * Cfg::BK, no_e, wave);
             // After the last tile these reads fetch stale data that no MFMA uses.
-            sp_step<Cfg, 0, 0, 0>(acc, f1, hi, f0, e, rd, stage_ptr(s1), SpReader<Cfg>::e_tile(smem, t + 1), ld,
+            sp_step<Cfg, 0, 0, 0>(acc, f1, hi, f0, e, rd, stage_ptr(s1), rd.e_tile(smem, t + 1), ld,
                                   nullptr, 0, no_e, wave);
         }
         wait_vmcnt<0>();                          // no load may land after the epilogue starts
@@ -668,7 +683,7 @@ __global__ __launch_bounds__(256) void sp_gemm_kernel(SpArgs a)
             sp_load_tile_masked<Cfg>(a, stage_ptr(0), smem, m0, n0, t, tid);
             lds_barrier();
             const GF_LDS char* st = stage_ptr(0);
-            const GF_LDS char* et = SpReader<Cfg>::e_tile(smem, t);
+            const GF_LDS char* et = rd.e_tile(smem, t);
             static_for<Cfg::FM>([&](auto f) { e[f] = rd.template e<decltype(f)::value>(et); });
             static_for<Cfg::FM>([&](auto f) { f0.a[f] = rd.template a<decltype(f)::value, 0>(st); });
             static_for<Cfg::FN>([&](auto f) { f0.b[f] = rd.template b<decltype(f)::value, 0>(st); });
@@ -724,9 +739,13 @@ hipError_t launch_sp_gemm(const SpArgs& a, hipStream_t stream)
 //
 // Metadata slot layout: row r's 16 dwords (dword 2 w + g = words 4 w + 2 g
 // and 4 w + 2 g + 1, i.e. lane group g's index words of K tile w of the
-// slot) sit at dword position d ^ key(r), key(r) = 2 ((r mod (BM/8)) / 4 mod 8):
-// with BM = 256 the 64 lanes of one fragment's metadata read (32 rows x 2
-// lane groups) then fall in 64 different banks (with BM = 128, in 32).
+// slot) sit at dword position d ^ key(r), key(r) = (r / 2) mod (BM / 16).
+// A 4-byte LDS read is served 32 lanes (one lane group, 32 consecutive rows
+// 64 bytes apart) at a time from 32 banks, so rows of equal parity share a
+// bank unless their positions differ: with BM = 256 the key gives the 16 rows
+// of each parity 16 different positions and the read has no conflict; with
+// BM = 128 the key repeats every 16 rows (the loads fill the slot in
+// 16-row pieces), leaving rows r and r + 16 in one bank.
 
 template <int BM_, int BN_, int HB_>
 struct SpPairCfg {
@@ -759,7 +778,7 @@ struct SpPairCfg {
 template <class Cfg>
 __device__ __forceinline__ int spp_ekey(int row)
 {
-    return 2 * (((row % Cfg::E_PIECE_ROWS) / 4) % 8);
+    return (row / 2) % (Cfg::E_PIECE_ROWS / 2);
 }
 
 // Direct-to-LDS loader of the paired form.  All source offsets go in the
