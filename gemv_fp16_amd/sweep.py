@@ -82,8 +82,14 @@ def _emit(path, rec):
     line = json.dumps(rec, sort_keys=True)
     print(line, flush=True)
     if path:
+        sep = ""
+        if os.path.exists(path) and os.path.getsize(path) > 0:
+            with open(path, "rb") as f:
+                f.seek(-1, os.SEEK_END)
+                if f.read(1) != b"\n":
+                    sep = "\n"   # a record cut short by an interrupted run keeps its own line
         with open(path, "a") as f:
-            f.write(line + "\n")
+            f.write(sep + line + "\n")
 
 
 def _parse_only(only):
