@@ -152,7 +152,10 @@ int gemm_f16_nt_splitk_f16(const void* A, const void* B, void* C, int M, int N, 
  * 1 = XCD-aware grouped order with panels of 10 tile-rows; n >= 2 = the
  * same with panels of n tile-rows.  schedule: 0 = every wave interleaves
  * its operand loads with its MFMAs; 1 = two wave groups alternate a memory
- * phase and an MFMA-only phase ("ping-pong", 512 threads only). */
+ * phase and an MFMA-only phase ("ping-pong", 512 threads only); 2 = one
+ * wave per SIMD (256 threads), the tile barrier before the last MFMA step
+ * and the next tile's first reads and loads under it; 3 = schedule 2 with
+ * 16x16x32 MFMAs. */
 typedef struct gf_gemm_cfg {
     int block_m, block_n, block_k, stages, threads, raster, schedule;
 } gf_gemm_cfg;
