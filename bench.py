@@ -179,7 +179,7 @@ def main():
     if not args.no_extra:
         # ---- GEMM, K swept ----
         sweep = {}
-        for k2 in (1024, 4096, 16384):
+        for k2 in (256, 512, 1024, 4096, 16384):
             a2 = torch.from_numpy(inputs.uniform_f16((M, k2), 0, 0)).cuda()
             b2 = torch.from_numpy(inputs.uniform_f16((N, k2), 0, 1)).cuda()
             t2 = time_batch(torch, gf.prepare_gemm_f16_nt(a2, b2, C), 10, 3)

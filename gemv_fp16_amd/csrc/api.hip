@@ -60,6 +60,13 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched
 // XCD-aware tile order is 5 % ahead at K = 1024, where each tile's short K
 // loop leaves operand re-reads less time to hide, ties at K = 4096, and is
 // within noise of plain order at K = 8192, where plain order is kept.
+// Short K (timed side by side at K = 128 .. 4096 on 8192^2, and at 4096^2,
+// 6144^2, 8192 x 4096 and 16384 x 8192) favours 512-thread tiles: up to
+// K = 512, tiles that leave room for more than one workgroup per CU --
+// 128 x 256 x 32 with three stages at K <= 256 given at least 1024 of them
+// (1.24-1.61x), else 256 x 128 x 64 with one stage (1.12-1.27x); up to
+// K = 1536, the 8-wave 256 x 256 kernel in plain order (1.03-1.10x; even at
+// K = 2048, behind from K = 4096).
 // The largest tile that still gives every CU a workgroup, in the form
 // measured fastest for it (tile sweeps at 8192^3 and at 2048 x 4096,
 // 2048 x 2048 and 1024 x 4096 x 8192; candidates timed side by side at ten
@@ -77,7 +84,16 @@ gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t25612 = (int64_t)ceil_div(M, 256) * ceil_div(N, 128);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    if (t256 >= 256) return make_cfg(256, 256, 64, 2, 256, K <= 4096 ? 1 : 0, 2);
+    if (t256 >= 256) {
+        // Short K: the C write outweighs the operand reads (at K = 256 it is
+        // 8x them), and tiles that leave room for more than one workgroup
+        // per CU overlap one workgroup's epilogue with another's main loop.
+        const int64_t t12825 = (int64_t)ceil_div(M, 128) * ceil_div(N, 256);
+        if (K <= 256 && t12825 >= 1024) return make_cfg(128, 256, 32, 3, 512, 0);
+        if (K <= 512) return make_cfg(256, 128, 64, 1, 512, 0);
+        if (K <= 1536) return make_cfg(256, 256, 64, 2, 512, 0);
+        return make_cfg(256, 256, 64, 2, 256, K <= 4096 ? 1 : 0, 2);
+    }
     if (t25612 >= 256 && K >= 2048) return make_cfg(256, 128, 64, 3, 256, 0, 2);
     if (t128 >= 128 && t128 <= 256) return make_cfg(128, 128, 64, 4, 256, 0, 2);
     if (t128 > 256) return make_cfg(128, 128, 64, 2, 256, 0);

@@ -205,6 +205,15 @@ def test_config_tables(L):
     assert len(gf.gemv_configs()) >= 30
     d = gf.gemm_default_config(8192, 8192, 8192)
     assert (d["block_m"], d["block_n"]) == (256, 256)
+    # short K: 512-thread tiles that leave room for more than one workgroup per CU
+    assert gf.gemm_default_config(8192, 8192, 256) == dict(
+        block_m=128, block_n=256, block_k=32, stages=3, threads=512, raster=0, schedule=0)
+    assert gf.gemm_default_config(4096, 4096, 256) == dict(
+        block_m=256, block_n=128, block_k=64, stages=1, threads=512, raster=0, schedule=0)
+    assert gf.gemm_default_config(8192, 8192, 512)["block_n"] == 128
+    assert gf.gemm_default_config(8192, 8192, 1024) == dict(
+        block_m=256, block_n=256, block_k=64, stages=2, threads=512, raster=0, schedule=0)
+    assert gf.gemm_default_config(8192, 8192, 2048)["threads"] == 256
     # mid-size shapes: the largest tile that still fills the 256 CUs
     d2 = gf.gemm_default_config(2048, 4096, 8192)
     assert (d2["block_m"], d2["block_n"], d2["stages"], d2["schedule"]) == (256, 128, 3, 2)

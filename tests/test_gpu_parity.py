@@ -160,7 +160,7 @@ def test_gemm_every_config_masked_path():
         assert np.array_equal(host_u16(C), ref), c
         ran.append(c)
     for shape in ((8192, 8192, 8192), (2048, 4096, 8192), (2048, 2048, 8192), (4096, 2048, 1024), (1024, 1024, 4096),
-                  (300, 300, 64)):
+                  (300, 300, 64), (8192, 8192, 256), (4096, 4096, 512), (8192, 8192, 1024)):
         d = dict(gf.gemm_default_config(*shape), raster=0)
         assert d in ran, "default %s for %s has no masked variant" % (d, shape)
     for tail in ({"block_m": 128, "block_n": 128, "block_k": 64, "stages": 4, "threads": 256, "raster": 0, "schedule": 2},
@@ -177,7 +177,7 @@ def test_gemm_power_of_two_scaling_bit_exact():
     assert np.array_equal(C2[normal], 2 * C1[normal])
 
 
-@pytest.mark.parametrize("K", [1024, 4096, 8192, 16384])
+@pytest.mark.parametrize("K", [256, 512, 1024, 4096, 8192, 16384])
 def test_gemm_8192_sampled(K):
     """M = N = 8192, K swept, default (bench) launch: sampled entries."""
     M = N = 8192
@@ -219,13 +219,16 @@ def split_rows(M, N):
 
 # (M, N, K, tail form): a 256-row tail (one round of 128 x 128 tiles), a
 # 768-row tail (two workgroups per CU), an 8-row tail (the skinny kernel), and
-# ragged N and K.
-ROW_SPLIT_SHAPES = [(7168, 7168, 512, "mfma"), (6144, 6144, 256, "mfma"), (6920, 7168, 256, "skinny"),
-                    (7268, 7000, 264, "mfma")]
+# ragged N and K; K where the default tile is 256 x 256 (one wave per SIMD at
+# K = 2048, 8 waves at K <= 1536).
+ROW_SPLIT_SHAPES = [(7168, 7168, 2048, "mfma"), (6144, 6144, 1024, "mfma"), (6920, 7168, 1024, "skinny"),
+                    (7268, 7000, 1032, "mfma")]
 
 
 @pytest.mark.parametrize("M,N,K,tail", ROW_SPLIT_SHAPES)
 def test_gemm_row_split(M, N, K, tail):
+    d = gf.gemm_default_config(M, N, K)
+    assert (d["block_m"], d["block_n"]) == (256, 256), "the split applies to 256 x 256 tiles only"
     m1 = split_rows(M, N)
     assert m1 < M
     ij = sample_ij(M, N, 3000, seed=M + K)
