@@ -74,7 +74,9 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched
 //  * 256 x 128 needs K >= 2048: below that the per-workgroup start and
 //    epilogue weigh more, and two 128 x 128 workgroups per CU hide them;
 //  * 128 x 128 with four stages (one workgroup per CU) while one round of
-//    them covers the shape, two stages (two per CU, one round of 512) past it;
+//    them covers the shape (for K <= 512, 64 x 128 with two stages instead:
+//    1.18-1.37x at 2048^2 x 256 / x 512 and 1024 x 4096 x 512), two stages
+//    (two per CU, one round of 512) past it;
 //  * below 128 of those, 64 x 64 with three stages: 1.5-1.9x the two-stage
 //    form at every small shape measured (M = 32 .. 1024, K = 1024 .. 8192).
 // Every tile chosen here is compiled with its masked variant too, so
@@ -95,7 +97,8 @@ gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
         return make_cfg(256, 256, 64, 2, 256, K <= 4096 ? 1 : 0, 2);
     }
     if (t25612 >= 256 && K >= 2048) return make_cfg(256, 128, 64, 3, 256, 0, 2);
-    if (t128 >= 128 && t128 <= 256) return make_cfg(128, 128, 64, 4, 256, 0, 2);
+    if (t128 >= 128 && t128 <= 256)
+        return K <= 512 ? make_cfg(64, 128, 64, 2, 256, 0) : make_cfg(128, 128, 64, 4, 256, 0, 2);
     if (t128 > 256) return make_cfg(128, 128, 64, 2, 256, 0);
     return make_cfg(64, 64, 64, 3, 256, 0);
 }

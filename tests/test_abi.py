@@ -214,6 +214,8 @@ def test_config_tables(L):
     assert gf.gemm_default_config(8192, 8192, 1024) == dict(
         block_m=256, block_n=256, block_k=64, stages=2, threads=512, raster=0, schedule=0)
     assert gf.gemm_default_config(8192, 8192, 2048)["threads"] == 256
+    assert gf.gemm_default_config(2048, 2048, 256) == dict(
+        block_m=64, block_n=128, block_k=64, stages=2, threads=256, raster=0, schedule=0)
     # mid-size shapes: the largest tile that still fills the 256 CUs
     d2 = gf.gemm_default_config(2048, 4096, 8192)
     assert (d2["block_m"], d2["block_n"], d2["stages"], d2["schedule"]) == (256, 128, 3, 2)

@@ -160,7 +160,8 @@ def test_gemm_every_config_masked_path():
         assert np.array_equal(host_u16(C), ref), c
         ran.append(c)
     for shape in ((8192, 8192, 8192), (2048, 4096, 8192), (2048, 2048, 8192), (4096, 2048, 1024), (1024, 1024, 4096),
-                  (300, 300, 64), (8192, 8192, 256), (4096, 4096, 512), (8192, 8192, 1024)):
+                  (300, 300, 64), (8192, 8192, 256), (4096, 4096, 512), (8192, 8192, 1024),
+                  (2048, 2048, 256)):
         d = dict(gf.gemm_default_config(*shape), raster=0)
         assert d in ran, "default %s for %s has no masked variant" % (d, shape)
     for tail in ({"block_m": 128, "block_n": 128, "block_k": 64, "stages": 4, "threads": 256, "raster": 0, "schedule": 2},
