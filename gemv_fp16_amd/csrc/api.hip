@@ -601,13 +601,18 @@ int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int
     return launch_status(fn(a, 1, static_cast<hipStream_t>(stream)));
 }
 
+// A K-major operand runs the schedule-2 tiles (the only ones with the
+// transposing fragment reads): 256 x 256 once 256 of them fill the CUs,
+// else 128 x 128 with two stages, two workgroups per CU -- which is also
+// 1.14-1.18x ahead of 256 x 256 for K <= 256 (8192^2 and 4096^2, NN and TN,
+// timed side by side; even at K = 512, behind from K = 1024).
 int gemm_f16(const void* A, const void* B, void* C, int M, int N, int K, int a_kmajor, int b_kmajor,
              void* stream)
 {
     gf_gemm_cfg cfg = default_gemm_cfg(M, N, K);
     if (a_kmajor || b_kmajor) {
         const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
-        cfg = t256 >= 256 ? make_cfg(256, 256, 64, 2, 256, 0, 2) : make_cfg(128, 128, 64, 2, 256, 0, 2);
+        cfg = t256 >= 256 && K > 256 ? make_cfg(256, 256, 64, 2, 256, 0, 2) : make_cfg(128, 128, 64, 2, 256, 0, 2);
     }
     return gemm_f16_cfg(A, B, C, M, N, K, a_kmajor, b_kmajor, &cfg, stream);
 }

@@ -306,15 +306,17 @@ def test_gemm_layouts_every_config():
     assert n >= 24
 
 
-def test_gemm_nn_8192_sampled():
-    """The plain row-major product at 8192^3 (default config), sampled."""
-    M = N = K = 8192
+@pytest.mark.parametrize("K,lay", [(8192, (0, 1)), (256, (0, 1)), (256, (1, 1))])
+def test_gemm_layout_8192_sampled(K, lay):
+    """K-major operands at M = N = 8192 with the library's tile (256 x 256;
+    128 x 128 at K = 256), sampled."""
+    M = N = 8192
     A, B = operands("uniform", M, N, K)
-    _say("gemm nn 8192^3")
-    got = run_layout(A, B, 0, 1)
+    _say("gemm layout %s 8192^2 x %d" % (lay, K))
+    got = run_layout(A, B, *lay)
     ij = sample_ij(M, N, 3000, seed=11)
     ref16, _ = oracle.gemm_nt_entries(A, B, ij)
-    check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "gemm nn 8192^3 sampled")
+    check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "gemm layout %s 8192^2 x %d sampled" % (lay, K))
 
 
 # ---------------------------------------------------------------------------
