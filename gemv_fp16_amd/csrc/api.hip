@@ -52,33 +52,35 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched
     return c;
 }
 
-// The tile config for a shape: the largest tile that still gives every CU
-// at least one workgroup.  For the large case the offline sweeps at
-// M = N = 8192 rank 256 x 256 x 64 / 2 stages with the one-wave-per-SIMD
-// schedule first at K = 1024, 4096 and 8192 (in side-by-side runs it matched
-// or beat the 8-wave interleaved schedule by up to 4 %).  The grouped,
-// XCD-aware tile order is 5 % ahead at K = 1024, where each tile's short K
-// loop leaves operand re-reads less time to hide, ties at K = 4096, and is
-// within noise of plain order at K = 8192, where plain order is kept.
-// Short K (timed side by side at K = 128 .. 4096 on 8192^2, and at 4096^2,
-// 6144^2, 8192 x 4096 and 16384 x 8192) favours 512-thread tiles: up to
-// K = 512, tiles that leave room for more than one workgroup per CU --
-// 128 x 256 x 32 with three stages at K <= 256 given at least 1024 of them
-// (1.24-1.61x), else 256 x 128 x 64 with one stage (1.12-1.27x); up to
-// K = 1536, the 8-wave 256 x 256 kernel in plain order (1.03-1.10x; even at
-// K = 2048, behind from K = 4096).
-// The largest tile that still gives every CU a workgroup, in the form
-// measured fastest for it (tile sweeps at 8192^3 and at 2048 x 4096,
-// 2048 x 2048 and 1024 x 4096 x 8192; candidates timed side by side at ten
-// mid-size shapes with K = 1024 .. 8192):
-//  * 256 x 128 needs K >= 2048: below that the per-workgroup start and
-//    epilogue weigh more, and two 128 x 128 workgroups per CU hide them;
-//  * 128 x 128 with four stages (one workgroup per CU) while one round of
-//    them covers the shape (for K <= 512, 64 x 128 with two stages instead:
-//    1.18-1.37x at 2048^2 x 256 / x 512 and 1024 x 4096 x 512), two stages
-//    (two per CU, one round of 512) past it;
-//  * below 128 of those, 64 x 64 with three stages: 1.5-1.9x the two-stage
-//    form at every small shape measured (M = 32 .. 1024, K = 1024 .. 8192).
+// The tile config for a shape: the largest tile that still gives every CU a
+// workgroup, in the form measured fastest for it (offline tile sweeps, then
+// candidates timed side by side, alternating batch by batch).
+//  * At least 256 tiles of 256 x 256:
+//    - K > 1536: 256 x 256 x 64, two stages, one wave per SIMD (schedule 2),
+//      first in the sweeps at M = N = 8192 for K = 4096 and 8192 and up to
+//      4 % ahead of the 8-wave kernel side by side; grouped, XCD-aware tile
+//      order up to K = 4096 (5 % ahead at K = 1024, tied at 4096), plain
+//      order above, where the two are within noise.
+//    - K <= 1536 (timed at K = 128 .. 4096 on 8192^2, and at 4096^2, 6144^2,
+//      8192 x 4096 and 16384 x 8192): 512-thread tiles.  Up to K = 512 the
+//      C write outweighs the operand reads (8x at K = 256), and tiles that
+//      leave room for more than one workgroup per CU overlap one
+//      workgroup's epilogue with another's main loop: 128 x 256 x 32 with
+//      three stages at K <= 256 given at least 1024 of them (1.24-1.61x),
+//      else 256 x 128 x 64 with one stage (1.12-1.27x).  Up to K = 1536, the
+//      8-wave 256 x 256 kernel in plain order (1.03-1.10x; even at 2048).
+//  * Fewer (tile sweeps at 2048 x 4096, 2048 x 2048 and 1024 x 4096 x 8192;
+//    candidates at ten mid-size shapes with K = 1024 .. 8192):
+//    - 256 x 128 once 256 of them fill the CUs, given K >= 2048: below that
+//      the per-workgroup start and epilogue weigh more, and two 128 x 128
+//      workgroups per CU hide them;
+//    - 128 x 128 with four stages (one workgroup per CU) while one round of
+//      them covers the shape (for K <= 512, 64 x 128 with two stages
+//      instead: 1.17-1.41x at six shapes), two stages (two per CU, one
+//      round of 512) past it;
+//    - below 128 of those, 64 x 64 with three stages: 1.5-1.9x the
+//      two-stage form at every small shape measured (M = 32 .. 1024,
+//      K = 1024 .. 8192).
 // Every tile chosen here is compiled with its masked variant too, so
 // unaligned operands run the same tile.
 gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
@@ -87,9 +89,6 @@ gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
     const int64_t t25612 = (int64_t)ceil_div(M, 256) * ceil_div(N, 128);
     const int64_t t128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     if (t256 >= 256) {
-        // Short K: the C write outweighs the operand reads (at K = 256 it is
-        // 8x them), and tiles that leave room for more than one workgroup
-        // per CU overlap one workgroup's epilogue with another's main loop.
         const int64_t t12825 = (int64_t)ceil_div(M, 128) * ceil_div(N, 256);
         if (K <= 256 && t12825 >= 1024) return make_cfg(128, 256, 32, 3, 512, 0);
         if (K <= 512) return make_cfg(256, 128, 64, 1, 512, 0);
