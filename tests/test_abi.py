@@ -275,3 +275,24 @@ def test_sparse_validation(L):
     assert gf.sp_default_config(2048, 2048, 8192) == {"block_m": 128, "block_n": 128, "stages": 3, "raster": 1}
     out = gf.SpCfg()
     assert L.gf_sp_config_get(len(cfgs), ctypes.byref(out)) == gf.GF_ERR_INVALID_ARG
+
+
+def test_every_default_tile_has_its_masked_and_fp32_variants():
+    """Whatever tile the library picks for gemm_f16_nt must also run unaligned
+    operands (its masked variant), so it must be one the config table marks
+    for those variants: checked over a dense grid of shapes."""
+    import itertools
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "gemv_fp16_amd", "csrc", "gemm_configs.def")).read()
+    core = {tuple(int(v) for v in m.groups()[:6])
+            for m in re.finditer(r"^GF_GEMM\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), 1\)", src, re.M)}
+    assert len(core) >= 10
+    sizes = (17, 64, 256, 1000, 1024, 2048, 3072, 4096, 6144, 7168, 8192, 16384)
+    ks = (8, 128, 256, 384, 512, 640, 1024, 1536, 2048, 4096, 8192, 16384)
+    seen = set()
+    for M, N, K in itertools.product(sizes, sizes, ks):
+        d = gf.gemm_default_config(M, N, K)
+        seen.add((d["block_m"], d["block_n"], d["block_k"], d["stages"], d["threads"], d["schedule"]))
+    assert seen <= core, sorted(seen - core)
+    assert len(seen) >= 7
