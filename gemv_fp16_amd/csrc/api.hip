@@ -387,17 +387,17 @@ gf_skinny_cfg default_skinny_cfg(int M, int N, int K)
     const bool lds_ok = K > 0 && K % kSkinnyKc == 0;
     const bool lds_first = lds_ok && M > 4 && (small_n || K <= 2048);
     if (M <= kSkinnyVecMaxM && !lds_first) {
-        const int unroll = M <= 2 ? 8 : 4;
-        const bool vec8 = skinny_vec_fits(M, K, unroll);
-        const bool vec16 = skinny_vec_fits(M, K, 4) &&
-                           (M <= 2 ? (int64_t)N * K >= (int64_t)32 << 20 : M <= 4 && !small_n);
-        if (vec8 && (K >= 8192 || !vec16)) {
+        const int unroll = M <= 2 ? 8 : 4;      // chunks in flight per lane in 8-wave workgroups
+        const bool fits_8w = skinny_vec_fits(M, K, unroll);
+        const bool wants_16w = skinny_vec_fits(M, K, 4) &&
+                               (M <= 2 ? (int64_t)N * K >= (int64_t)32 << 20 : M <= 4 && !small_n);
+        if (fits_8w && (K >= 8192 || !wants_16w)) {
             c.blocks = 1;
             c.unroll = unroll;
             c.stages = 1;
             return c;
         }
-        if (vec16) {
+        if (wants_16w) {
             c.blocks = 1;
             c.unroll = 4;
             c.waves = 16;
