@@ -218,7 +218,8 @@ def gemm_f16(A, B, C=None, a_kmajor: bool = False, b_kmajor: bool = False, strea
 
 
 def gemm_f16_nt_skinny(A, B, C=None, stream=None, cfg: dict | None = None):
-    """C = A . B^T for 1 <= M <= 16 rows of A through the skinny kernel."""
+    """C = A . B^T for 1 <= M <= 64 rows of A through the skinny kernel
+    (17 to 64 rows: the LDS-staged form only, K % 512 == 0)."""
     import torch
     M, N, K = _gemm_shapes(A, B)
     if C is None:

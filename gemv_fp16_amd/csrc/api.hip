@@ -383,6 +383,22 @@ gf_skinny_cfg default_skinny_cfg(int M, int N, int K)
 {
     gf_skinny_cfg c;
     c.waves = 8;
+    if (M > kSkinnyMaxM) {
+        // 17 .. 64 rows: the LDS form with A in 16-row blocks (timed against
+        // the tiles and each other at N x K = 8192^2, 4096 x 14336,
+        // 2048 x 8192, 4096^2 and 1024 x 4096): three 16-row blocks of B
+        // per workgroup at 8192 rows of B up to M = 32, two up to 48, else
+        // one; below 8192 rows one block, three stages up to M = 32.
+        c.unroll = 0;
+        if (N >= 8192) {
+            c.blocks = M <= 32 ? 3 : (M <= 48 ? 2 : 1);
+            c.stages = 2;
+        } else {
+            c.blocks = 1;
+            c.stages = M <= 32 ? 3 : 2;
+        }
+        return c;
+    }
     const bool small_n = N < 8192;
     const bool lds_ok = K > 0 && K % kSkinnyKc == 0;
     const bool lds_first = lds_ok && M > 4 && (small_n || K <= 2048);
@@ -423,6 +439,14 @@ bool skinny_fits(const void* A, const void* B, int M, int K)
     return M >= 1 && M <= kSkinnyMaxM && K % 8 == 0 && aligned(A, 16) && aligned(B, 16);
 }
 
+// M = 17 .. 64 rows of A: the LDS form only, A staged in 16-row blocks.
+constexpr int kSkinnyWideMaxM = 64;
+bool skinny_wide_fits(const void* A, const void* B, int M, int K)
+{
+    return M > kSkinnyMaxM && M <= kSkinnyWideMaxM && K > 0 && K % kSkinnyKc == 0 && aligned(A, 16) &&
+           aligned(B, 16);
+}
+
 int skinny_impl(const void* A, const void* B, void* C, int M, int N, int K, const gf_skinny_cfg& cfg,
                 hipStream_t stream)
 {
@@ -431,6 +455,8 @@ int skinny_impl(const void* A, const void* B, void* C, int M, int N, int K, cons
     const SkinnyDesc& d = kSkinnyConfigs[idx];
     if (d.stages == 1 && !skinny_vec_fits(M, K, d.unroll)) return GF_ERR_UNSUPPORTED;
     if (d.stages >= 2 && (K % kSkinnyKc != 0 || K == 0)) return GF_ERR_UNSUPPORTED;
+    if (M > kSkinnyMaxM && (d.stages < 2 || M > skinny_lds_max_m(d.blocks, d.stages, d.waves)))
+        return GF_ERR_UNSUPPORTED;
     return launch_status(g_skinny_table[idx](static_cast<const uint16_t*>(A),
                                              static_cast<const uint16_t*>(B),
                                              static_cast<uint16_t*>(C), M, N, K, stream));
@@ -445,11 +471,6 @@ int find_gemv(const gf_gemv_cfg& c)
     return -1;
 }
 
-// Launch shape for a GEMV.  From the offline sweep at N = K = 8192: a grid of
-// 512 eight-wave workgroups whose waves split K (2 rows per step, 2 loads
-// per row in flight) is best when K/8 divides into 8 x 64 x 2 chunks; other
-// large shapes use one row per wave with 8 loads in flight; small ones are
-// launch-bound and take one chunk per lane at a time.
 // Launch shape from sweeps of every shape at N x K = 8192^2, 16384 x 4096,
 // 14336 x 4096, 4096 x 16384, 4096 x 14336, 2048^2 and 1024^2:
 //  * the split form (a workgroup's waves split K, the grid streams one band
@@ -517,8 +538,13 @@ int gemm_f16_nt_cfg(const void* A, const void* B, void* C, int M, int N, int K,
 
 int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void* stream)
 {
-    // A handful of rows of A: the skinny kernel streams B once.
-    if (M > 0 && N > 0 && skinny_fits(A, B, M, K)) {
+    // A handful of rows of A: the skinny kernel streams B once.  From 17 to
+    // 64 rows too where B has at most 8192 rows and K >= 4096: there a
+    // 64-row tile grid leaves most CUs idle (128 workgroups at N = 8192), and
+    // the LDS form ran 1.07-3.3x faster; from 14336 rows of B, or at
+    // K = 2048, the tiles were ahead.
+    if (M > 0 && N > 0 &&
+        (skinny_fits(A, B, M, K) || (skinny_wide_fits(A, B, M, K) && N <= 8192 && K >= 4096))) {
         const int rc = validate_gemm(A, B, C, M, N, K, 2);
         if (rc) return rc;
         return skinny_impl(A, B, C, M, N, K, default_skinny_cfg(M, N, K),
@@ -549,7 +575,7 @@ int gemm_f16_nt_skinny(const void* A, const void* B, void* C, int M, int N, int 
     int rc = validate_gemm(A, B, C, M, N, K, 2);
     if (rc) return rc;
     if (M == 0 || N == 0) return GF_OK;
-    if (!skinny_fits(A, B, M, K)) return GF_ERR_UNSUPPORTED;
+    if (!skinny_fits(A, B, M, K) && !skinny_wide_fits(A, B, M, K)) return GF_ERR_UNSUPPORTED;
     const gf_skinny_cfg c = cfg ? *cfg : default_skinny_cfg(M, N, K);
     return skinny_impl(A, B, C, M, N, K, c, static_cast<hipStream_t>(stream));
 }
@@ -568,7 +594,7 @@ int gf_skinny_config_get(int i, gf_skinny_cfg* out)
 
 int gf_skinny_default_config(int M, int N, int K, gf_skinny_cfg* out)
 {
-    if (!out || M < 1 || M > kSkinnyMaxM || N < 0 || K < 0) return GF_ERR_INVALID_ARG;
+    if (!out || M < 1 || M > kSkinnyWideMaxM || N < 0 || K < 0) return GF_ERR_INVALID_ARG;
     *out = default_skinny_cfg(M, N, K);
     return GF_OK;
 }

@@ -145,9 +145,10 @@ struct SkinnyLdsCfg {
     static constexpr int CHUNK_BYTES = ROWS * kSkinnyKc * 2;
     static constexpr int LW = ROWS / W;                 // loads per wave per chunk
     static constexpr int LDS_BYTES = S * CHUNK_BYTES;
+    static constexpr int MB = MA > 16 ? MA / 16 : 1;     // 16-row blocks of A
     static constexpr bool kValid =
         W <= 16 && ROWS % W == 0 && LDS_BYTES <= 160 * 1024 && S >= 2 && LW * S < 64 &&
-        (MA == 4 || MA == 8 || MA == 16);
+        (MA == 4 || MA == 8 || MA == 16 || MA == 32 || MA == 48 || MA == 64);
 };
 
 template <int NB, int S, int W, int MA>
@@ -187,14 +188,17 @@ __global__ __launch_bounds__(W * kWave) void skinny_lds_kernel(
     // lane l reads row 16 * blk + l % 16, 16-byte chunk 4 * ks + l / 16.
     const int r16 = lane % 16, kq = lane / 16;
     auto frag = [&](int slot, int blk, int ks) {
-        const int rr = blk == NB ? min(r16, MA - 1) : r16;   // row within the 16-row block
+        const int rr = (blk == NB && MA < 16) ? min(r16, MA - 1) : r16;   // row within the 16-row block
         const int row = 16 * blk + rr;
         const int c = (4 * ks + kq) ^ rr;
         return *(const GF_LDS half8*)(smem + slot * Cf::CHUNK_BYTES + row * (kSkinnyKc * 2) + c * 16);
     };
-    floatx4 acc[NB];
+    constexpr int MB = Cf::MB;
+    floatx4 acc[MB][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[b][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     // Prologue: chunks 0 .. S-2 (chunk indices past the end load a valid
     // chunk 0 again, keeping the count of loads in flight fixed).
 #pragma unroll
@@ -208,27 +212,34 @@ __global__ __launch_bounds__(W * kWave) void skinny_lds_kernel(
 #pragma unroll
         for (int ks = 0; ks < kSkinnyKc / 32; ++ks) {
             if (ks % W != wave % W) continue;    // wave-uniform
-            const half8 a = frag(slot, NB, ks);
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, frag(slot, j, ks), acc[j], 0, 0, 0);
+            for (int b = 0; b < MB; ++b) {
+                const half8 a = frag(slot, NB + b, ks);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, frag(slot, j, ks), acc[b][j], 0, 0, 0);
+            }
         }
     }
     wait_vmcnt<0>();
     lds_barrier();                               // stage memory is free: reuse it for the partials
-    floatx4* part = (floatx4*)smem_raw;         // [W][NB][64]
+    floatx4* part = (floatx4*)smem_raw;         // [W][MB * NB][64]
 #pragma unroll
-    for (int j = 0; j < NB; ++j) part[(wave * NB + j) * kWave + lane] = acc[j];
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) part[((wave * MB + b) * NB + j) * kWave + lane] = acc[b][j];
     __syncthreads();
-    if (threadIdx.x < NB * kWave) {
-        const int j = threadIdx.x / kWave, l = threadIdx.x % kWave;
-        floatx4 sum = part[j * kWave + l];
+    static_assert(MB * NB <= W, "one thread per partial tile lane");
+    if (threadIdx.x < MB * NB * kWave) {
+        const int bj = threadIdx.x / kWave, l = threadIdx.x % kWave;   // bj = b * NB + j
+        const int b = bj / NB, j = bj % NB;
+        floatx4 sum = part[bj * kWave + l];
 #pragma unroll
-        for (int w = 1; w < W; ++w) sum += part[(w * NB + j) * kWave + l];
+        for (int w = 1; w < W; ++w) sum += part[(w * MB * NB + bj) * kWave + l];
         const int n = n0 + j * 16 + l % 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int m = 4 * (l / 16) + i;
+            const int m = 16 * b + 4 * (l / 16) + i;
             if (m < M && n < N) C[(size_t)m * N + n] = f32_to_f16_bits(sum[i]);
         }
     }
@@ -252,8 +263,10 @@ hipError_t launch_skinny_lds_ma(const uint16_t* A, const uint16_t* B, uint16_t* 
     return hipGetLastError();
 }
 
-// The LDS-staged launch for M rows of A: the fewest staged A rows (4, 8 or
-// 16) that cover M and divide evenly over the waves.
+// The LDS-staged launch for M rows of A: the fewest staged A rows (4, 8, 16,
+// or 32, 48, 64 in 16-row blocks) that cover M and divide evenly over the
+// waves.  M past what the config's LDS holds (skinny_lds_max_m) returns
+// hipErrorInvalidValue; callers check it first.
 template <int NB, int S, int W>
 hipError_t launch_skinny_lds(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
                              hipStream_t stream)
@@ -263,7 +276,27 @@ hipError_t launch_skinny_lds(const uint16_t* A, const uint16_t* B, uint16_t* C, 
         if (M <= 4) return launch_skinny_lds_ma<NB, S, W, 4>(A, B, C, M, N, K, stream);
     if constexpr (SkinnyLdsCfg<NB, S, W, 8>::kValid)
         if (M <= 8) return launch_skinny_lds_ma<NB, S, W, 8>(A, B, C, M, N, K, stream);
-    return launch_skinny_lds_ma<NB, S, W, 16>(A, B, C, M, N, K, stream);
+    if (M <= 16) return launch_skinny_lds_ma<NB, S, W, 16>(A, B, C, M, N, K, stream);
+    if constexpr (SkinnyLdsCfg<NB, S, W, 32>::kValid)
+        if (M <= 32) return launch_skinny_lds_ma<NB, S, W, 32>(A, B, C, M, N, K, stream);
+    if constexpr (SkinnyLdsCfg<NB, S, W, 48>::kValid)
+        if (M <= 48) return launch_skinny_lds_ma<NB, S, W, 48>(A, B, C, M, N, K, stream);
+    if constexpr (SkinnyLdsCfg<NB, S, W, 64>::kValid)
+        if (M <= 64) return launch_skinny_lds_ma<NB, S, W, 64>(A, B, C, M, N, K, stream);
+    return hipErrorInvalidValue;
+}
+
+// The most rows of A the LDS form of (NB, S, W) takes: 16, or the largest of
+// 32, 48, 64 up to which every block count fits (the launch above).
+constexpr int skinny_lds_max_m(int NB, int S, int W)
+{
+    int best = 16;
+    for (int ma = 32; ma <= 64; ma += 16) {
+        const int rows = 16 * NB + ma;
+        if (!(rows % W == 0 && S * rows * kSkinnyKc * 2 <= 160 * 1024 && (rows / W) * S < 64)) break;
+        best = ma;
+    }
+    return best;
 }
 
 // ---------------------------------------------------------------------------

@@ -49,7 +49,8 @@ enum { GF_SPLITK_ATOMIC = 0, GF_SPLITK_TWOPASS = 1, GF_SPLITK_F16 = 2 };
  * Defined by the TileLang FP16 matmul autotune benchmark page, sections 1
  * and 2 (C = A B^T with A(M,K), B(N,K), C(M,N), fp16 operands, fp32
  * accumulation, transpose_B) and the autotune tutorial page's reference().
- * The library picks the launch: M <= 16 takes the skinny kernel; when the
+ * The library picks the launch: M <= 16 takes the skinny kernel, and so do
+ * 17 <= M <= 64 when N <= 8192, K >= 4096 and K % 512 == 0; when the
  * default tile would leave its last round of workgroups at most half full,
  * the call enqueues two launches on `stream`, the leading rows of C in whole
  * rounds and the rest with a smaller tile (same result bits as one launch
@@ -195,13 +196,16 @@ int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int
                  int b_kmajor, const gf_gemm_cfg* cfg, void* stream);
 
 /*
- * Skinny fp16 NT GEMM: gemm_f16_nt for 1 <= M <= 16 rows of A (a decode
+ * Skinny fp16 NT GEMM: gemm_f16_nt for 1 <= M <= 64 rows of A (a decode
  * batch against one large B): every byte of B is streamed once and the rows
  * of A ride along in the MFMA operand.  Same result contract as
- * gemm_f16_nt (fp32 accumulation, one fp16 rounding).  gemm_f16_nt takes
- * this path by itself when M <= 16, K % 8 == 0 and A and B are 16-byte
- * aligned; this entry point runs it explicitly and returns
- * GF_ERR_UNSUPPORTED outside those conditions.  cfg: launch shape, NULL =
+ * gemm_f16_nt (fp32 accumulation, one fp16 rounding).  Needs A and B
+ * 16-byte aligned and K % 8 == 0; 17 <= M <= 64 needs the LDS-staged form
+ * (K % 512 == 0) with a ring that holds those rows: 16 * blocks + M rounded
+ * up to 32, 48 or 64 rows of 1 KiB per stage, within 160 KiB and a multiple
+ * of waves.  gemm_f16_nt takes this path by itself as described there; this
+ * entry point runs it explicitly and returns GF_ERR_UNSUPPORTED outside
+ * those conditions.  cfg: launch shape, NULL =
  * the library's choice.  waves = waves per workgroup; then one of three forms:
  *  - stages = 0, direct form on the matrix cores: blocks = 16-row blocks of
  *    B per workgroup, waves split K, loads straight to registers (unroll =

@@ -115,7 +115,7 @@ def test_layout_validation(L):
 def test_skinny_validation(L):
     s = NULL
     sk = L.gemm_f16_nt_skinny
-    assert sk(FAKE, FAKE, FAKE, 17, 64, 64, None, s) == gf.GF_ERR_UNSUPPORTED      # M > 16
+    assert sk(FAKE, FAKE, FAKE, 17, 64, 64, None, s) == gf.GF_ERR_UNSUPPORTED      # M > 16 needs K % 512 == 0
     assert sk(FAKE, FAKE, FAKE, 4, 64, 60, None, s) == gf.GF_ERR_UNSUPPORTED       # K % 8 != 0
     assert sk(ctypes.c_void_p(0x10002), FAKE, FAKE, 4, 64, 64, None, s) == gf.GF_ERR_UNSUPPORTED
     bad = gf.SkinnyCfg(3, 3, 8, 0)
@@ -125,8 +125,16 @@ def test_skinny_validation(L):
     assert len(gf.skinny_configs()) >= 4
     out = gf.SkinnyCfg()
     assert L.gf_skinny_config_get(-1, ctypes.byref(out)) == gf.GF_ERR_INVALID_ARG
-    for m in (0, 17):
+    for m in (0, 65):
         assert L.gf_skinny_default_config(m, 64, 64, ctypes.byref(out)) == gf.GF_ERR_INVALID_ARG
+    assert L.gf_skinny_default_config(40, 8192, 8192, ctypes.byref(out)) == gf.GF_OK
+    assert (out.blocks, out.unroll, out.waves, out.stages) == (2, 0, 8, 2)      # 17..64 rows: LDS form
+    assert gf.skinny_default_config(24, 4096, 8192) == {"blocks": 1, "unroll": 0, "waves": 8, "stages": 3}
+    assert gf.skinny_default_config(64, 8192, 8192) == {"blocks": 1, "unroll": 0, "waves": 8, "stages": 2}
+    assert sk(FAKE, FAKE, FAKE, 65, 64, 512, None, s) == gf.GF_ERR_UNSUPPORTED     # M > 64
+    assert sk(FAKE, FAKE, FAKE, 40, 64, 1000, None, s) == gf.GF_ERR_UNSUPPORTED    # 17..64 rows need K % 512 == 0
+    direct = gf.SkinnyCfg(1, 4, 8, 0)
+    assert sk(FAKE, FAKE, FAKE, 40, 64, 512, ctypes.byref(direct), s) == gf.GF_ERR_UNSUPPORTED   # not the LDS form
     assert L.gf_skinny_default_config(4, 64, 64, None) == gf.GF_ERR_INVALID_ARG
 
 

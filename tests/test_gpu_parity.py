@@ -395,6 +395,66 @@ def test_skinny_is_gemm_nt_for_small_m():
     assert np.array_equal(got, tiled)
 
 
+def lds_max_m(cfg):
+    """Rows of A the LDS form of a launch shape takes: 16, or the largest of
+    32, 48, 64 up to which its LDS ring (two or more 512-k chunks of
+    16 * blocks + those rows, 1 KiB each, within 160 KiB) holds every count."""
+    best = 16
+    for ma in (32, 48, 64):
+        rows = 16 * cfg["blocks"] + ma
+        if not (rows % cfg["waves"] == 0 and cfg["stages"] * rows * 1024 <= 160 * 1024
+                and (rows // cfg["waves"]) * cfg["stages"] < 64):
+            break
+        best = ma
+    return best
+
+
+@pytest.mark.parametrize("M", [17, 24, 32, 33, 48, 64])
+@pytest.mark.parametrize("N,K", [(520, 1536), (77, 2048), (1000, 512)])
+def test_skinny_wide_every_lds_config(M, N, K):
+    """17 to 64 rows of A through the LDS form (A staged in 16-row blocks):
+    every launch shape whose ring holds the rows, bit-exact on integers;
+    the others, and the other forms, refused."""
+    A, B = operands("integer", M, N, K, seed=12)
+    ref = oracle.gemm_nt_f16(A, B)
+    ran = 0
+    for cfg in gf.skinny_configs():
+        _say("skinny wide cfg %s %dx%dx%d" % (cfg, M, N, K))
+        if cfg["stages"] >= 2 and M <= lds_max_m(cfg):
+            assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
+            ran += 1
+        else:
+            with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+                run_skinny(A, B, cfg)
+    assert ran >= 1                                                  # M = 64: one shape's ring holds it
+    assert np.array_equal(run_skinny(A, B), ref)                     # the library's shape
+    A, B = operands("uniform", M, N, K, seed=12)
+    check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny wide %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(24, 2048, 4096), (40, 8192, 4608), (64, 1000, 4096), (48, 9000, 4096),
+                                   (32, 2048, 2048)])
+def test_gemm_nt_takes_skinny_for_up_to_64_rows(M, N, K):
+    """gemm_f16_nt routes 17 to 64 rows to the skinny kernel where B has at
+    most 8192 rows and K >= 4096 (same bits as the explicit call), and to
+    the tiles elsewhere; bit-exact on integers either way."""
+    A, B = operands("integer", M, N, K, seed=13)
+    _say("gemm nt %dx%dx%d (17..64 rows)" % (M, N, K))
+    got = run_gemm(A, B)
+    assert np.array_equal(got, oracle.gemm_nt_f16(A, B))
+    if N <= 8192 and K >= 4096:
+        assert np.array_equal(got, run_skinny(A, B))
+
+
+@pytest.mark.parametrize("M", [32, 64])
+def test_skinny_wide_8192(M):
+    """17 to 64 rows against an 8192 x 8192 B, all outputs."""
+    N = K = 8192
+    A, B = operands("uniform", M, N, K)
+    _say("skinny wide M=%d 8192^2" % M)
+    check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny wide M=%d 8192^2" % M)
+
+
 @pytest.mark.parametrize("M", [1, 2, 4, 6, 16])
 @pytest.mark.parametrize("N,K", [(4096, 14336), (6144, 6144), (2056, 4096), (12288, 6144), (16384, 2048),
                                  (8200, 4096)])
