@@ -276,10 +276,11 @@ def main():
                             "traffic": measured_traffic("gemv_kernel", "8192^2")}
         extra["gemv"] = gemv
 
-        # ---- skinny GEMM: M = 2..16 rows against an 8192 x 8192 B (decode batches) ----
+        # ---- skinny GEMM: M = 2..64 rows against an 8192 x 8192 B (decode batches;
+        # gemm_f16_nt takes the skinny kernel for all of them) ----
         Bsk = [torch.from_numpy(inputs.uniform_f16((8192, 8192), i, 1)).cuda() for i in range(5)]
         sk_res = {}
-        for mm in (2, 4, 8, 16):
+        for mm in (2, 4, 8, 16, 32, 64):
             Ask = torch.from_numpy(inputs.uniform_f16((mm, 8192), 0, 0)).cuda()
             Csk = torch.empty((mm, 8192), dtype=torch.float16, device="cuda")
             state = [0]
