@@ -131,7 +131,10 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, uint16_t* C, int 
 // loads its 16 * NB rows of B and MA rows of A, MA = 4, 8 or 16, the fewest
 // that cover M (rows past M are clamped to a valid row; an MFMA row of A only
 // reaches the same row of the result, and those rows are not stored, so the
-// fragment reads of the 16 - MA rows that are not staged re-read row MA - 1).  Chunk c of a row sits at 16-byte slot
+// fragment reads of the 16 - MA rows that are not staged re-read row
+// MA - 1).  For 17 to 64 rows MA = 32, 48 or 64: A sits in 16-row blocks,
+// each of which meets every B fragment with accumulators of its own, so B
+// is still read once.  Chunk c of a row sits at 16-byte slot
 // c ^ (row % 16), so the 16 lanes that read one fragment (16 rows, same k)
 // hit 16 different bank groups.  S chunks ring through LDS; every wave
 // issues the same number of loads per chunk, so each wait is a constant.
