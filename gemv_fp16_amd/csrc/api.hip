@@ -543,8 +543,10 @@ int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void
     // 64-row tile grid leaves most CUs idle (128 workgroups at N = 8192), and
     // the LDS form ran 1.07-3.3x faster; from 14336 rows of B, or at
     // K = 2048, the tiles were ahead.
-    if (M > 0 && N > 0 &&
-        (skinny_fits(A, B, M, K) || (skinny_wide_fits(A, B, M, K) && N <= 8192 && K >= 4096))) {
+    auto takes_skinny = [&](const void* a, int m) {
+        return skinny_fits(a, B, m, K) || (skinny_wide_fits(a, B, m, K) && N <= 8192 && K >= 4096);
+    };
+    if (M > 0 && N > 0 && takes_skinny(A, M)) {
         const int rc = validate_gemm(A, B, C, M, N, K, 2);
         if (rc) return rc;
         return skinny_impl(A, B, C, M, N, K, default_skinny_cfg(M, N, K),
@@ -560,7 +562,7 @@ int gemm_f16_nt(const void* A, const void* B, void* C, int M, int N, int K, void
         const char* At = static_cast<const char*>(A) + (size_t)m1 * K * 2;
         char* Ct = static_cast<char*>(C) + (size_t)m1 * N * 2;
         const int mt = M - m1;
-        if (skinny_fits(At, B, mt, K))
+        if (takes_skinny(At, mt))
             return skinny_impl(At, B, Ct, mt, N, K, default_skinny_cfg(mt, N, K),
                                static_cast<hipStream_t>(stream));
         const gf_gemm_cfg tail = tail_gemm_cfg(mt, N);

@@ -219,11 +219,11 @@ def split_rows(M, N):
 
 
 # (M, N, K, tail form): a 256-row tail (one round of 128 x 128 tiles), a
-# 768-row tail (two workgroups per CU), an 8-row tail (the skinny kernel), and
-# ragged N and K; K where the default tile is 256 x 256 (one wave per SIMD at
+# 768-row tail (two workgroups per CU), an 8-row and a 40-row tail (the
+# skinny kernel), and ragged N and K; K where the default tile is 256 x 256 (one wave per SIMD at
 # K = 2048, 8 waves at K <= 1536).
 ROW_SPLIT_SHAPES = [(7168, 7168, 2048, "mfma"), (6144, 6144, 1024, "mfma"), (6920, 7168, 1024, "skinny"),
-                    (7268, 7000, 1032, "mfma")]
+                    (7268, 7000, 1032, "mfma"), (6184, 8192, 4096, "skinny")]
 
 
 @pytest.mark.parametrize("M,N,K,tail", ROW_SPLIT_SHAPES)
