@@ -228,8 +228,9 @@ int gemm_f16_nt_skinny(const void* A, const void* B, void* C, int M, int N, int 
                        const gf_skinny_cfg* cfg, void* stream);
 int gf_skinny_config_count(void);
 int gf_skinny_config_get(int i, gf_skinny_cfg* out);
-/* The launch shape gemm_f16_nt_skinny (and gemm_f16_nt for M <= 16) would
- * pick for a shape; GF_ERR_INVALID_ARG unless 1 <= M <= 16, N >= 0, K >= 0. */
+/* The launch shape gemm_f16_nt_skinny (and gemm_f16_nt where it takes the
+ * skinny kernel) would pick for a shape; GF_ERR_INVALID_ARG unless
+ * 1 <= M <= 64, N >= 0, K >= 0. */
 int gf_skinny_default_config(int M, int N, int K, gf_skinny_cfg* out);
 
 /* gemv_f16 with an explicit launch shape; GF_ERR_UNSUPPORTED when the
