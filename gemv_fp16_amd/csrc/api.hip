@@ -189,17 +189,52 @@ __global__ void zero_f32x4_kernel(floatx4* __restrict__ p, int64_t n4)
     for (int64_t t = i; t < n4; t += stride) p[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
+// Slices s0 .. s0+NB-1 of element t (slice s at ws[s * stride + t]) added
+// to acc in ascending s; every load is issued before the first add, so a
+// thread keeps NB requests in flight instead of waiting out each load's
+// latency in turn.
+template <int NB, class V>
+__device__ __forceinline__ V add_slices(V acc, const V* __restrict__ ws, int64_t stride, int64_t t,
+                                        int s0)
+{
+    V v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) v[j] = ws[(int64_t)(s0 + j) * stride + t];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc += v[j];
+    return acc;
+}
+
+// The slices of element t summed in fp32 in ascending s from +0: the fixed
+// order that makes the two-pass result reproducible.  (A partial is an MFMA
+// sum that started from +0, so it is never -0, and +0 + p == p: the sum
+// equals the one that starts from slice 0 itself.)  Loads go out 8 slices
+// at a time.
+template <class V>
+__device__ __forceinline__ V sum_slices(const V* __restrict__ ws, int64_t stride, int64_t t, int slices)
+{
+    V acc = {};
+    int s0 = 0;
+    for (; s0 + 8 <= slices; s0 += 8) acc = add_slices<8>(acc, ws, stride, t, s0);
+    switch (slices - s0) {
+    case 1: return add_slices<1>(acc, ws, stride, t, s0);
+    case 2: return add_slices<2>(acc, ws, stride, t, s0);
+    case 3: return add_slices<3>(acc, ws, stride, t, s0);
+    case 4: return add_slices<4>(acc, ws, stride, t, s0);
+    case 5: return add_slices<5>(acc, ws, stride, t, s0);
+    case 6: return add_slices<6>(acc, ws, stride, t, s0);
+    case 7: return add_slices<7>(acc, ws, stride, t, s0);
+    default: return acc;
+    }
+}
+
 // C32[i] = sum over s = 0 .. slices-1, ascending, of ws[s][i].
 __global__ void splitk_reduce_x4_kernel(const floatx4* __restrict__ ws, floatx4* __restrict__ c,
                                         int64_t n4, int slices)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = i; t < n4; t += stride) {
-        floatx4 s = ws[t];
-        for (int k = 1; k < slices; ++k) s += ws[(int64_t)k * n4 + t];
-        c[t] = s;
-    }
+    for (int64_t t = i; t < n4; t += stride) c[t] = sum_slices(ws, n4, t, slices);
 }
 
 __global__ void splitk_reduce_kernel(const float* __restrict__ ws, float* __restrict__ c, int64_t n,
@@ -207,11 +242,12 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, float* __rest
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = i; t < n; t += stride) {
-        float s = ws[t];
-        for (int k = 1; k < slices; ++k) s += ws[(int64_t)k * n + t];
-        c[t] = s;
-    }
+    for (int64_t t = i; t < n; t += stride) c[t] = sum_slices(ws, n, t, slices);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    return f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
 }
 
 // C16[i] = fp16_rne(sum over s = 0 .. slices-1, ascending, of ws[s][i]):
@@ -220,20 +256,16 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ ws, float* __rest
 __global__ void splitk_reduce_f16x8_kernel(const floatx4* __restrict__ ws, u32x4* __restrict__ c,
                                            int64_t n8, int slices)
 {
+    typedef float floatx8 __attribute__((ext_vector_type(8)));
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t n4 = 2 * n8;
     for (int64_t t = i; t < n8; t += stride) {
-        floatx4 lo = ws[2 * t], hi = ws[2 * t + 1];
-        for (int k = 1; k < slices; ++k) {
-            lo += ws[(int64_t)k * n4 + 2 * t];
-            hi += ws[(int64_t)k * n4 + 2 * t + 1];
-        }
+        const floatx8 v = sum_slices((const floatx8*)ws, n8, t, slices);
         u32x4 o;
-        o.x = f32_to_f16_bits(lo.x) | ((uint32_t)f32_to_f16_bits(lo.y) << 16);
-        o.y = f32_to_f16_bits(lo.z) | ((uint32_t)f32_to_f16_bits(lo.w) << 16);
-        o.z = f32_to_f16_bits(hi.x) | ((uint32_t)f32_to_f16_bits(hi.y) << 16);
-        o.w = f32_to_f16_bits(hi.z) | ((uint32_t)f32_to_f16_bits(hi.w) << 16);
+        o.x = pack_f16x2(v[0], v[1]);
+        o.y = pack_f16x2(v[2], v[3]);
+        o.z = pack_f16x2(v[4], v[5]);
+        o.w = pack_f16x2(v[6], v[7]);
         c[t] = o;
     }
 }
@@ -243,11 +275,7 @@ __global__ void splitk_reduce_f16_kernel(const float* __restrict__ ws, uint16_t*
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t t = i; t < n; t += stride) {
-        float s = ws[t];
-        for (int k = 1; k < slices; ++k) s += ws[(int64_t)k * n + t];
-        c[t] = f32_to_f16_bits(s);
-    }
+    for (int64_t t = i; t < n; t += stride) c[t] = f32_to_f16_bits(sum_slices(ws, n, t, slices));
 }
 
 __global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n)

@@ -40,8 +40,9 @@ struct GemmArgs {
     const uint16_t* B;
     void* C;            // fp16 C, fp32 C32, or the fp32 slice workspace
     int M, N, K;
-    int kt_per_slice;   // K tiles per split-K slice (gridDim.y slices)
+    int kt_per_slice;   // K tiles per split-K slice
     int raster;         // 0: plain tile order; > 0: XCD remap + panel of this many rows
+    int slices;         // split-K slices (set by launch_gemm); the grid is (tiles, slices)
 };
 
 // 16 zero bytes: the source of direct-to-LDS chunks that lie beyond K.
@@ -630,21 +631,35 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 
-    // ---- which tile ----
+    // ---- which tile, and which K slice ----
     const int tiles_m = ceil_div(a.M, Cfg::BM), tiles_n = ceil_div(a.N, Cfg::BN);
-    int tm, tn;
-    const int w = blockIdx.x;
-    if (a.raster > 0) {
-        grouped_tile(xcd_remap(w, tiles_m * tiles_n), tiles_m, tiles_n, a.raster, tm, tn);
+    const int ntiles = tiles_m * tiles_n;
+    int tm, tn, slice = 0;
+    int w = blockIdx.x;
+    if (a.slices > 1) {
+        // Split-K: the grid (tiles, slices) enumerates (slice, tile) work
+        // items slice by slice in dispatch order.  With the XCD remap each
+        // XCD receives one contiguous run of items -- every tile of one K
+        // slice (or of a few) -- so the A and B panels of that K range are
+        // fetched into the XCD's L2 once and shared by its workgroups,
+        // instead of every XCD streaming the whole K extent of a few tiles.
+        w += blockIdx.y * gridDim.x;
+        const int L = a.raster > 0 ? xcd_remap(w, ntiles * a.slices) : w;
+        slice = L / ntiles;
+        w = L - slice * ntiles;
+        tm = w / tiles_n;
+        tn = w % tiles_n;
+    } else if (a.raster > 0) {
+        grouped_tile(xcd_remap(w, ntiles), tiles_m, tiles_n, a.raster, tm, tn);
     } else {
         tm = w / tiles_n;
         tn = w % tiles_n;
     }
     const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
 
-    // ---- which K tiles (split-K slice = blockIdx.y) ----
+    // ---- which K tiles ----
     const int nkt_total = ceil_div(a.K, Cfg::BK);
-    const int kt_begin = blockIdx.y * a.kt_per_slice;
+    const int kt_begin = slice * a.kt_per_slice;
     const int kt_end = min(nkt_total, kt_begin + a.kt_per_slice);
     const int nk = max(0, kt_end - kt_begin);
 
@@ -903,7 +918,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
                         unsafeAtomicAdd(C + (size_t)grow * a.N + gcol, acc[fm][fn][i]);
                 }
     } else {
-        float* W = (float*)a.C + (size_t)blockIdx.y * a.M * a.N;
+        float* W = (float*)a.C + (size_t)slice * a.M * a.N;
 #pragma unroll
         for (int fm = 0; fm < Cfg::FM; ++fm)
 #pragma unroll
@@ -921,8 +936,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
 
 // Host-side launch of one instantiation: grid = (tiles, slices).
 template <class Cfg, int EPI, bool ALIGNED>
-hipError_t launch_gemm(const GemmArgs& a, int slices, hipStream_t stream)
+hipError_t launch_gemm(const GemmArgs& args, int slices, hipStream_t stream)
 {
+    GemmArgs a = args;
+    a.slices = slices;
     auto kern = gemm_nt_kernel<Cfg, EPI, ALIGNED>;
     static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
     {
