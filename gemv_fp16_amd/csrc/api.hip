@@ -6,6 +6,7 @@
 
 #include "../../include/gemvfp16.h"
 #include "configs.hpp"
+#include "gemv_kernel.hpp"
 #include "skinny_kernel.hpp"
 
 namespace gf {
@@ -156,13 +157,19 @@ gf_gemm_cfg default_splitk_cfg(int M, int N, int K, int split_k)
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GF_OK : GF_ERR_HIP; }
 
+// Whether the 128-bit operand path applies: 16-byte aligned A and B, K % 8 == 0.
+bool operands_aligned(const void* A, const void* B, int K)
+{
+    return aligned(A, 16) && aligned(B, 16) && (K % 8 == 0);
+}
+
 // One GEMM launch of epilogue `epi` over `slices` K slices of kt_per tiles.
 int run_gemm(const void* A, const void* B, void* C, int M, int N, int K, const gf_gemm_cfg& cfg,
              int epi, int slices, int kt_per, bool c16_aligned, hipStream_t stream)
 {
     const int idx = find_gemm(cfg);
     if (idx < 0) return GF_ERR_UNSUPPORTED;
-    const bool al = aligned(A, 16) && aligned(B, 16) && (K % 8 == 0) && c16_aligned;
+    const bool al = operands_aligned(A, B, K) && c16_aligned;
     GemmLaunchFn fn = g_gemm_table[idx][epi * 2 + (al ? 1 : 0)];
     if (!fn) return GF_ERR_UNSUPPORTED;
     GemmArgs a;
@@ -303,6 +310,35 @@ int zero_f32(float* p, int64_t n, hipStream_t stream)
     return launch_status(hipGetLastError());
 }
 
+// The slice sums of a two-pass workspace into C32 (fp32) or C16 (fp16).
+int splitk_reduce(const void* ws, void* C, bool out_f16, int64_t mn, int slices, hipStream_t stream)
+{
+    if (!out_f16 && aligned(ws, 16) && aligned(C, 16) && mn % 4 == 0) {
+        hipLaunchKernelGGL(splitk_reduce_x4_kernel, dim3(grid_for(mn / 4, 256)), dim3(256), 0, stream,
+                           static_cast<const floatx4*>(ws), static_cast<floatx4*>(C), mn / 4, slices);
+    } else if (!out_f16) {
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
+                           static_cast<const float*>(ws), static_cast<float*>(C), mn, slices);
+    } else if (aligned(ws, 16) && aligned(C, 16) && mn % 8 == 0) {
+        hipLaunchKernelGGL(splitk_reduce_f16x8_kernel, dim3(grid_for(mn / 8, 256)), dim3(256), 0,
+                           stream, static_cast<const floatx4*>(ws), static_cast<u32x4*>(C), mn / 8,
+                           slices);
+    } else {
+        hipLaunchKernelGGL(splitk_reduce_f16_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
+                           static_cast<const float*>(ws), static_cast<uint16_t*>(C), mn, slices);
+    }
+    return launch_status(hipGetLastError());
+}
+
+// Tile-aligned split-K slices: kt_per K tiles each; only non-empty slices
+// run (slices == 0 for K == 0).
+void slice_plan(int K, int block_k, int split_k, int& kt_per, int& slices)
+{
+    const int nkt = ceil_div(K, block_k);
+    kt_per = nkt > 0 ? ceil_div(nkt, split_k) : 0;
+    slices = nkt > 0 ? ceil_div(nkt, kt_per) : 0;
+}
+
 int splitk_impl(const void* A, const void* B, float* C32, int M, int N, int K, int split_k,
                 int mode, void* ws, size_t ws_bytes, const gf_gemm_cfg& cfg, hipStream_t stream)
 {
@@ -318,11 +354,8 @@ int splitk_impl(const void* A, const void* B, float* C32, int M, int N, int K, i
     if (find_gemm(cfg) < 0) return GF_ERR_UNSUPPORTED;
     if (mn == 0) return GF_OK;
 
-    // Tile-aligned slices: kt_per K tiles each; only non-empty slices run.
-    const int nkt = ceil_div(K, cfg.block_k);
-    const int kt_per = nkt > 0 ? ceil_div(nkt, split_k) : 0;
-    const int slices = nkt > 0 ? ceil_div(nkt, kt_per) : 0;
-
+    int kt_per, slices;
+    slice_plan(K, cfg.block_k, split_k, kt_per, slices);
     if (mode == GF_SPLITK_ATOMIC || slices == 0) {
         rc = zero_f32(C32, mn, stream);
         if (rc || slices == 0) return rc;
@@ -330,15 +363,7 @@ int splitk_impl(const void* A, const void* B, float* C32, int M, int N, int K, i
     }
     rc = run_gemm(A, B, ws, M, N, K, cfg, EPI_F32_STORE, slices, kt_per, true, stream);
     if (rc) return rc;
-    if (aligned(ws, 16) && aligned(C32, 16) && mn % 4 == 0) {
-        hipLaunchKernelGGL(splitk_reduce_x4_kernel, dim3(grid_for(mn / 4, 256)), dim3(256), 0, stream,
-                           reinterpret_cast<const floatx4*>(ws), reinterpret_cast<floatx4*>(C32),
-                           mn / 4, slices);
-    } else {
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
-                           static_cast<const float*>(ws), C32, mn, slices);
-    }
-    return launch_status(hipGetLastError());
+    return splitk_reduce(ws, C32, false, mn, slices, stream);
 }
 
 // Split-K with an fp16 output: pass 1 stores each slice's fp32 partial tile
@@ -356,9 +381,8 @@ int splitk_f16_impl(const void* A, const void* B, void* C, int M, int N, int K, 
     if (find_gemm(cfg) < 0) return GF_ERR_UNSUPPORTED;
     if (mn == 0) return GF_OK;
 
-    const int nkt = ceil_div(K, cfg.block_k);
-    const int kt_per = nkt > 0 ? ceil_div(nkt, split_k) : 0;
-    const int slices = nkt > 0 ? ceil_div(nkt, kt_per) : 0;
+    int kt_per, slices;
+    slice_plan(K, cfg.block_k, split_k, kt_per, slices);
     if (slices == 0) {                           // K == 0: the empty sum
         hipLaunchKernelGGL(zero_u16_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
                            static_cast<uint16_t*>(C), mn);
@@ -366,15 +390,7 @@ int splitk_f16_impl(const void* A, const void* B, void* C, int M, int N, int K, 
     }
     rc = run_gemm(A, B, ws, M, N, K, cfg, EPI_F32_STORE, slices, kt_per, true, stream);
     if (rc) return rc;
-    if (aligned(ws, 16) && aligned(C, 16) && mn % 8 == 0) {
-        hipLaunchKernelGGL(splitk_reduce_f16x8_kernel, dim3(grid_for(mn / 8, 256)), dim3(256), 0,
-                           stream, reinterpret_cast<const floatx4*>(ws), static_cast<u32x4*>(C),
-                           mn / 8, slices);
-    } else {
-        hipLaunchKernelGGL(splitk_reduce_f16_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
-                           static_cast<const float*>(ws), static_cast<uint16_t*>(C), mn, slices);
-    }
-    return launch_status(hipGetLastError());
+    return splitk_reduce(ws, C, true, mn, slices, stream);
 }
 
 int find_skinny(const gf_skinny_cfg& c)
@@ -499,12 +515,19 @@ int find_gemv(const gf_gemv_cfg& c)
     return -1;
 }
 
-// Launch shape from sweeps of every shape at N x K = 8192^2, 16384 x 4096,
-// 14336 x 4096, 4096 x 16384, 4096 x 14336, 2048^2 and 1024^2:
-//  * the split form (a workgroup's waves split K, the grid streams one band
-//    of W) where it was best, tall W with K a multiple of 8192;
-//  * else one row per wave, 4 chunks per lane in flight, 4 waves per
-//    workgroup: within 7 % of the best launch shape at every large shape;
+// Launch shape, from sweeps of the compiled shapes (batches of back-to-back
+// calls, W rotated over more than the MALL) at N x K = 8192^2, 16384 x 8192,
+// 8192 x 16384, 4096 x 8192, 16384 x 4096, 14336 x 4096, 28672 x 4096,
+// 8192 x 4096, 4096^2, 4096 x 14336, 12288 x 6144 and 2048 x 8192:
+//  * the split form (a workgroup's 8 waves split K, one workgroup per CU,
+//    the grid streaming one band of W) where K is a multiple of 8192 and W
+//    has at least 4096 rows: two rows per task up to K = 8192 (8192^2:
+//    21.0 us = 6.39 TB/s, 4096 x 8192: 11.7 us), one row beyond (8192 x
+//    16384: 38.9 us = 6.91 TB/s, where two rows per task take 44.9);
+//  * else one row per wave: 8 chunks per lane in flight and 2-wave
+//    workgroups when each row splits into whole 512-chunk steps (K % 4096
+//    == 0; 1-2 % ahead of 4 chunks at every such shape), else 4 chunks and
+//    4-wave workgroups;
 //  * smaller W: 2 chunks in flight and 1-wave workgroups from 2048^2 up,
 //    below that 8 waves with 1 chunk (launch-bound).
 gf_gemv_cfg default_gemv_cfg(int N, int K)
@@ -514,8 +537,10 @@ gf_gemv_cfg default_gemv_cfg(int N, int K)
     c.blocks = 0;
     c.rows_per_wave = 1;
     if (nk >= (int64_t)4096 * 4096) {
-        if (N >= 8192 && K % 8192 == 0 && K <= 32768) {
-            c.rows_per_wave = 2; c.unroll = 2; c.waves = 8; c.blocks = 512;
+        if (N >= 4096 && K % 8192 == 0 && K <= kGemvXldsMaxK) {
+            c.rows_per_wave = K <= 8192 ? 2 : 1; c.unroll = 2; c.waves = 8; c.blocks = 256;
+        } else if (K % 4096 == 0) {
+            c.unroll = 8; c.waves = 2;
         } else {
             c.unroll = 4; c.waves = 4;
         }

@@ -75,14 +75,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __rest
     extern __shared__ __attribute__((aligned(16))) char gemv_smem[];
 
     const half8* xv4 = (const half8*)x;
+    GF_LDS half8* xs = (GF_LDS half8*)gemv_smem;
     if constexpr (XLDS) {
         // Stage x once per workgroup; the only barrier in the kernel.
-        half8* xs = (half8*)gemv_smem;
         const int nch = K / 8;
         for (int j = threadIdx.x; j < nch; j += WAVES * kWave) xs[j] = xv4[j];
         __syncthreads();
-        xv4 = (const half8*)gemv_smem;
     }
+    // x chunk j: from LDS (an LDS-space pointer, so that the read is a
+    // ds_read and its wait does not also wait for the W loads in flight)
+    // or from global memory.
+    auto xchunk = [&](int j) __attribute__((always_inline)) {
+        if constexpr (XLDS) return xs[j];
+        else return xv4[j];
+    };
 
     const int groups = (N + ROWS - 1) / ROWS;
     for (int gidx = blockIdx.x * WAVES + wave; gidx < groups; gidx += gridDim.x * WAVES) {
@@ -109,14 +115,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __rest
                     for (int r = 0; r < ROWS; ++r)
                         wv[r][u] = __builtin_nontemporal_load(wr[r] + j + u * kWave);
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u) xv[u] = xv4[j + u * kWave];
+                for (int u = 0; u < UNROLL; ++u) xv[u] = xchunk(j + u * kWave);
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
                     for (int r = 0; r < ROWS; ++r) acc[r] = dot8(wv[r][u], xv[u], acc[r]);
             }
             for (; j < nch; j += kWave) {                            // ragged end of the row
-                const half8 xc = xv4[j];
+                const half8 xc = xchunk(j);
 #pragma unroll
                 for (int r = 0; r < ROWS; ++r)
                     acc[r] = dot8(__builtin_nontemporal_load(wr[r] + j), xc, acc[r]);
@@ -142,19 +148,31 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __rest
 
 constexpr int kGemvXldsMaxK = 32768;   // x staged in LDS up to 64 KiB
 
+// 16-byte W loads per lane per task of the split kernel.
+template <int ROWS, int UNROLL>
+constexpr int ntasks_loads()
+{
+    return ROWS * UNROLL;
+}
+
 // Bounded-grid GEMV with the workgroup's waves splitting K.  A workgroup owns
 // ROWS consecutive rows at a time (row groups walked grid-stride); wave w
 // streams chunks [w * CPW, (w + 1) * CPW) of each row, CPW = K / 8 / WAVES,
 // UNROLL * 64 chunks per step.  All workgroups together therefore read one
 // contiguous band of W at a time (the order HBM serves best), instead of
-// one stripe of every row in flight.  Loads of the next (row group, step)
-// task are issued before the current one is multiplied.  Per row group,
-// each wave folds its partial sums with DPP and parks them in LDS; after the
-// group's single barrier, wave 0 adds the WAVES partials in wave order
-// (deterministic) and writes y.  The LDS slots alternate between groups, so
-// the next group's partials never overwrite slots wave 0 is still reading.
-// x is staged in LDS once.  Requires 16-byte alignment, K % 8 == 0,
-// K <= kGemvXldsMaxK and (K / 8) % (WAVES * 64 * UNROLL) == 0.
+// one stripe of every row in flight.  The loads of the next (row group,
+// step) task are issued before the current one is multiplied, and in the
+// steady-state loop they are issued unconditionally, so that the wait before
+// each multiply leaves that next task's loads in flight (a load under a
+// branch, or a read of x through a generic pointer, would make the compiler
+// wait for every load first).  Per row group, each wave folds its partial
+// sums with DPP and parks them in LDS; after the group's single barrier,
+// wave 0 adds the WAVES partials in wave order (deterministic) and writes y.
+// The LDS slots alternate between groups, so the next group's partials
+// never overwrite slots wave 0 is still reading.  x is staged in LDS once,
+// by direct-to-LDS loads issued before the first W loads.  Requires 16-byte
+// alignment, K % 8 == 0, K <= kGemvXldsMaxK and
+// (K / 8) % (WAVES * 64 * UNROLL) == 0.
 template <int ROWS, int UNROLL, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemv_split_kernel(const uint16_t* __restrict__ W,
                                                                 const uint16_t* __restrict__ x,
@@ -162,12 +180,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_split_kernel(const uint16_t* 
                                                                 int K)
 {
     constexpr int STEP = kWave * UNROLL;               // chunks of a row per wave per task
+    constexpr int NT = WAVES * kWave;
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
     extern __shared__ __attribute__((aligned(16))) char gemv_smem[];
-    float* red = (float*)gemv_smem;                    // [2][WAVES][ROWS] partial sums
-    half8* xs = (half8*)(gemv_smem + 2 * WAVES * ROWS * 4 + 12);
-    xs = (half8*)(((uintptr_t)xs + 15) & ~(uintptr_t)15);
+    GF_LDS float* red = (GF_LDS float*)gemv_smem;      // [2][WAVES][ROWS] partial sums
+    GF_LDS half8* xs = (GF_LDS half8*)(gemv_smem + ((2 * WAVES * ROWS * 4 + 15) & ~15));
 
     const int nch = K / 8;
     const int cpw = nch / WAVES;                       // chunks per wave per row
@@ -176,8 +194,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_split_kernel(const uint16_t* 
     const int ngroups = (int)blockIdx.x < groups ? (groups - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
     const int ntasks = ngroups * spg;
     const int cbase = wave * cpw + lane;
+    if (ntasks == 0) return;                           // no rows for this workgroup
 
-    half8 buf[2][ROWS][UNROLL];
+    // x -> LDS: each wave instruction fills 64 consecutive 16-byte slots.
+    for (int j0 = wave * kWave; j0 < nch; j0 += NT)
+        if (j0 + lane < nch)
+            __builtin_amdgcn_global_load_lds((const void*)((const half8*)x + j0 + lane),
+                                             (GF_LDS void*)(xs + j0), 16, 0, 0);
+
     auto load = [&](int i, half8 (&b)[ROWS][UNROLL]) __attribute__((always_inline)) {
         const int g = blockIdx.x + (i / spg) * gridDim.x;
         const int s = i % spg;
@@ -188,9 +212,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_split_kernel(const uint16_t* 
             for (int u = 0; u < UNROLL; ++u) b[r][u] = __builtin_nontemporal_load(wr + u * kWave);
         }
     };
-    if (ntasks > 0) load(0, buf[0]);                   // W traffic starts before x staging
-    for (int j = threadIdx.x; j < nch; j += WAVES * kWave) xs[j] = ((const half8*)x)[j];
-    __syncthreads();
+    half8 buf0[ROWS][UNROLL], buf1[ROWS][UNROLL];
+    load(0, buf0);
+    wait_vmcnt<ntasks_loads<ROWS, UNROLL>()>();        // x has landed; task 0's loads may fly
+    lds_barrier();
 
     float acc[ROWS];
 #pragma unroll
@@ -205,14 +230,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_split_kernel(const uint16_t* 
         }
         if (s == spg - 1) {                            // row group done
             const int gi = i / spg;
-            float* slot = red + (gi & 1) * WAVES * ROWS;
+            GF_LDS float* slot = red + (gi & 1) * WAVES * ROWS;
 #pragma unroll
             for (int r = 0; r < ROWS; ++r) {
                 const float sum = wave_sum(acc[r]);
                 if (lane == 0) slot[wave * ROWS + r] = sum;
                 acc[r] = 0.0f;
             }
-            __syncthreads();
+            lds_barrier();
             if (wave == 0 && lane < ROWS) {
                 const int row = (blockIdx.x + gi * gridDim.x) * ROWS + lane;
                 float t = 0.0f;
@@ -222,13 +247,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_split_kernel(const uint16_t* 
             }
         }
     };
-    for (int i = 0; i < ntasks; i += 2) {
-        if (i + 1 < ntasks) load(i + 1, buf[1]);
-        compute(i, buf[0]);
-        if (i + 1 < ntasks) {
-            if (i + 2 < ntasks) load(i + 2, buf[0]);
-            compute(i + 1, buf[1]);
-        }
+    int i = 0;
+    for (; i + 2 < ntasks; i += 2) {                   // tasks i + 1 and i + 2 exist
+        load(i + 1, buf1);
+        compute(i, buf0);
+        load(i + 2, buf0);
+        compute(i + 1, buf1);
+    }
+    if (i + 1 < ntasks) {
+        load(i + 1, buf1);
+        compute(i, buf0);
+        compute(i + 1, buf1);
+    } else if (i < ntasks) {
+        compute(i, buf0);
     }
 }
 

@@ -243,8 +243,13 @@ def test_config_tables(L):
     dg = gf.gemv_default_config(8192, 8192)
     assert {**dg, "blocks": 0} in gf.gemv_configs() and dg["blocks"] >= 0
     assert dg["blocks"] > 0                                # tall W, K % 8192 == 0: the split form
-    dw = gf.gemv_default_config(4096, 16384)               # wide W: one row per wave
-    assert dw == {"rows_per_wave": 1, "unroll": 4, "waves": 4, "blocks": 0}
+    assert dg == {"rows_per_wave": 2, "unroll": 2, "waves": 8, "blocks": 256}
+    dw = gf.gemv_default_config(4096, 16384)               # long rows: one row per split task
+    assert dw == {"rows_per_wave": 1, "unroll": 2, "waves": 8, "blocks": 256}
+    # K not a multiple of 8192: one row per wave, 8 chunks in flight when
+    # rows split into whole 512-chunk steps, else 4
+    assert gf.gemv_default_config(16384, 4096) == {"rows_per_wave": 1, "unroll": 8, "waves": 2, "blocks": 0}
+    assert gf.gemv_default_config(4096, 14336) == {"rows_per_wave": 1, "unroll": 4, "waves": 4, "blocks": 0}
     for n, k in ((16384, 4096), (2048, 2048), (1024, 1024), (7, 13)):
         assert {**gf.gemv_default_config(n, k), "blocks": 0} in gf.gemv_configs()
     bad = gf.GemmCfg()
