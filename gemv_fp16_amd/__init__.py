@@ -118,6 +118,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _alloc(stream, fn):
+    """Allocate a tensor that the call enqueued on `stream` will use: under
+    that stream, so that torch's caching allocator does not hand the block
+    to another stream's work while the call may still be running."""
+    import torch
+    if stream is None:
+        return fn()
+    with torch.cuda.stream(stream if isinstance(stream, torch.cuda.Stream)
+                           else torch.cuda.ExternalStream(int(stream))):
+        return fn()
+
+
 def _dev(t, dtype, name):
     import torch
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -179,7 +191,7 @@ def gemm_f16_nt(A, B, C=None, stream=None, cfg: dict | None = None):
     import torch
     M, N, K = _gemm_shapes(A, B)
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        C = _alloc(stream, lambda: torch.empty((M, N), dtype=torch.float16, device=A.device))
     if tuple(C.shape) != (M, N):
         raise ValueError("C must be (M, N)")
     args = (_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"), _dev(C, torch.float16, "C"),
@@ -204,7 +216,7 @@ def gemm_f16(A, B, C=None, a_kmajor: bool = False, b_kmajor: bool = False, strea
     if K != Kb:
         raise ValueError("A and B disagree on K (%d vs %d)" % (K, Kb))
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        C = _alloc(stream, lambda: torch.empty((M, N), dtype=torch.float16, device=A.device))
     if tuple(C.shape) != (M, N):
         raise ValueError("C must be (M, N)")
     args = (_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"), _dev(C, torch.float16, "C"),
@@ -223,7 +235,7 @@ def gemm_f16_nt_skinny(A, B, C=None, stream=None, cfg: dict | None = None):
     import torch
     M, N, K = _gemm_shapes(A, B)
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        C = _alloc(stream, lambda: torch.empty((M, N), dtype=torch.float16, device=A.device))
     if tuple(C.shape) != (M, N):
         raise ValueError("C must be (M, N)")
     c = ctypes.byref(SkinnyCfg(**cfg)) if cfg is not None else None
@@ -268,7 +280,7 @@ def gemm_f16_nt_splitk(A, B, C32=None, split_k: int = 4, stream=None):
     import torch
     M, N, K = _gemm_shapes(A, B)
     if C32 is None:
-        C32 = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        C32 = _alloc(stream, lambda: torch.empty((M, N), dtype=torch.float32, device=A.device))
     if tuple(C32.shape) != (M, N):
         raise ValueError("C32 must be (M, N)")
     _check(lib().gemm_f16_nt_splitk(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
@@ -286,12 +298,13 @@ def gemm_f16_nt_splitk_ex(A, B, C32=None, split_k: int = 4, mode: int = GF_SPLIT
     import torch
     M, N, K = _gemm_shapes(A, B)
     if C32 is None:
-        C32 = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        C32 = _alloc(stream, lambda: torch.empty((M, N), dtype=torch.float32, device=A.device))
     ws_ptr, ws_bytes = ctypes.c_void_p(0), 0
     if mode == GF_SPLITK_TWOPASS:
         need = gemm_f16_nt_splitk_workspace_bytes(M, N, split_k)
         if workspace is None:
-            workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=A.device)
+            workspace = _alloc(stream, lambda: torch.empty(max(1, need // 4), dtype=torch.float32,
+                                                           device=A.device))
         ws_ptr = _dev(workspace, torch.float32, "workspace")
         ws_bytes = workspace.numel() * 4
     _check(lib().gemm_f16_nt_splitk_ex(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
@@ -324,12 +337,13 @@ def gemm_f16_nt_splitk_f16(A, B, C=None, split_k: int = 4, workspace=None, strea
     import torch
     M, N, K = _gemm_shapes(A, B)
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=A.device)
+        C = _alloc(stream, lambda: torch.empty((M, N), dtype=torch.float16, device=A.device))
     if tuple(C.shape) != (M, N):
         raise ValueError("C must be (M, N)")
     need = gemm_f16_nt_splitk_workspace_bytes(M, N, split_k)
     if workspace is None:
-        workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=A.device)
+        workspace = _alloc(stream, lambda: torch.empty(max(1, need // 4), dtype=torch.float32,
+                                                       device=A.device))
     _check(lib().gemm_f16_nt_splitk_f16(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
                                         _dev(C, torch.float16, "C"), M, N, K, split_k,
                                         _dev(workspace, torch.float32, "workspace"),
@@ -345,7 +359,7 @@ def gemv_f16(W, x, y=None, stream=None, cfg: dict | None = None):
         raise ValueError("W must be (N, K) and x (K,)")
     N, K = W.shape
     if y is None:
-        y = torch.empty((N,), dtype=torch.float16, device=W.device)
+        y = _alloc(stream, lambda: torch.empty((N,), dtype=torch.float16, device=W.device))
     if tuple(y.shape) != (N,):
         raise ValueError("y must be (N,)")
     args = (_dev(W, torch.float16, "W"), _dev(x, torch.float16, "x"), _dev(y, torch.float16, "y"), N, K)
@@ -433,9 +447,9 @@ def sp24_compress_f16(A, A_sparse=None, E=None, stream=None):
         raise ValueError("A must be (M, K)")
     M, K = A.shape
     if A_sparse is None:
-        A_sparse = torch.empty((M, K // 2), dtype=torch.float16, device=A.device)
+        A_sparse = _alloc(stream, lambda: torch.empty((M, K // 2), dtype=torch.float16, device=A.device))
     if E is None:
-        E = torch.empty((M, K // 16), dtype=torch.int16, device=A.device)
+        E = _alloc(stream, lambda: torch.empty((M, K // 16), dtype=torch.int16, device=A.device))
     if tuple(A_sparse.shape) != (M, K // 2) or tuple(E.shape) != (M, K // 16):
         raise ValueError("A_sparse must be (M, K/2) and E (M, K/16)")
     _check(lib().sp24_compress_f16(_dev(A, torch.float16, "A"), _dev(A_sparse, torch.float16, "A_sparse"),
@@ -443,7 +457,7 @@ def sp24_compress_f16(A, A_sparse=None, E=None, stream=None):
     return A_sparse, E
 
 
-def _sp_args(A_sparse, E, B, C):
+def _sp_args(A_sparse, E, B, C, stream=None):
     import torch
     if A_sparse.dim() != 2 or E.dim() != 2 or B.dim() != 2:
         raise ValueError("A_sparse must be (M, K/2), E (M, K/16), B (N, K)")
@@ -452,7 +466,7 @@ def _sp_args(A_sparse, E, B, C):
     if B.shape[1] != K or tuple(E.shape) != (M, K // 16):
         raise ValueError("A_sparse must be (M, K/2), E (M, K/16), B (N, K)")
     if C is None:
-        C = torch.empty((M, N), dtype=torch.float16, device=B.device)
+        C = _alloc(stream, lambda: torch.empty((M, N), dtype=torch.float16, device=B.device))
     if tuple(C.shape) != (M, N):
         raise ValueError("C must be (M, N)")
     args = (_dev(A_sparse, torch.float16, "A_sparse"), _dev(E, torch.int16, "E"), _dev(B, torch.float16, "B"),
@@ -462,7 +476,7 @@ def _sp_args(A_sparse, E, B, C):
 
 def gemm_sp_f16_nt(A_sparse, E, B, C=None, stream=None, cfg: dict | None = None):
     """C = decompress(A_sparse, E) . B^T (fp16 in, fp32 accumulate, fp16 out)."""
-    C, args = _sp_args(A_sparse, E, B, C)
+    C, args = _sp_args(A_sparse, E, B, C, stream)
     if cfg is None:
         _check(lib().gemm_sp_f16_nt(*args, _stream(stream)), "gemm_sp_f16_nt")
     else:
@@ -473,7 +487,7 @@ def gemm_sp_f16_nt(A_sparse, E, B, C=None, stream=None, cfg: dict | None = None)
 
 def prepare_gemm_sp_f16_nt(A_sparse, E, B, C, stream=None, cfg: dict | None = None):
     """Zero-argument callable that launches the sparse product on `stream`."""
-    C, args = _sp_args(A_sparse, E, B, C)
+    C, args = _sp_args(A_sparse, E, B, C, stream)
     s = _stream(stream)
     L = lib()
     c = SpCfg(**cfg) if cfg is not None else None

@@ -149,3 +149,33 @@ def test_concurrent_streams():
     assert np.array_equal(host_u16(o["y"]), oracle.gemv_f16(host["W"], host["x"]))
     rAsp, rE = oracle.sp24_compress(host["PA"])
     assert np.array_equal(host_u16(o["sp"]), oracle.gemm_sp_nt_f16(rAsp, rE, host["PB"]))
+
+
+def test_binding_allocations_on_explicit_stream():
+    """Outputs and two-pass workspaces that the binding allocates for a call
+    on an explicit, non-current stream belong to that stream: while the
+    side stream is still busy with the call, the current stream reallocates
+    and overwrites freed memory, and the results must stay intact."""
+    side = torch.cuda.Stream()
+    A = inputs.integer_f16((SM, SK), 400, 0)
+    B = inputs.integer_f16((SN, SK), 400, 1)
+    dA, dB = dev(A), dev(B)
+    torch.cuda.synchronize()
+    outs = []
+    _say("binding allocations on a side stream")
+    for _ in range(4):
+        # no workspace and no output passed: the binding allocates both
+        outs.append(gf.gemm_f16_nt_splitk_ex(dA, dB, split_k=SPLIT, mode=gf.GF_SPLITK_TWOPASS,
+                                             stream=side))
+        outs.append(gf.gemm_f16_nt_splitk_f16(dA, dB, split_k=SPLIT, stream=side))
+        # the current stream grabs and scribbles over whatever is free now
+        junk = [torch.full((SPLIT * SM * SN,), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+        del junk
+    torch.cuda.synchronize()
+    ref32 = oracle.gemm_nt_f32(A, B)
+    ref16 = oracle.gemm_nt_f16(A, B)
+    for i, o in enumerate(outs):
+        if i % 2 == 0:
+            assert np.array_equal(o.cpu().numpy(), ref32)
+        else:
+            assert np.array_equal(host_u16(o), ref16)
