@@ -81,7 +81,7 @@ def splitmix64(seed: int, stream_id: int, count: int, start: int = 0) -> np.ndar
     return out
 
 
-def _draw(seed: int, stream_id: int, count: int, integer: bool) -> np.ndarray:
+def _draw(seed: int, stream_id: int, count: int, integer: bool, start: int = 0) -> np.ndarray:
     out = np.empty(count, dtype=np.float16)
     u = np.empty(min(count, _CHUNK), dtype=np.float64)
 
@@ -99,7 +99,7 @@ def _draw(seed: int, stream_id: int, count: int, integer: bool) -> np.ndarray:
             np.subtract(uu, 1.0, out=uu)         # 2u - 1
         out[lo:hi] = uu                          # round-to-nearest-even to fp16
 
-    _fill(seed, stream_id, count, 0, emit)
+    _fill(seed, stream_id, count, start, emit)
     return out
 
 
@@ -118,6 +118,21 @@ def integer_f16(shape, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarray:
     """fp16 values drawn from {-2, -1, 0, 1, 2}, as a float16 array of ``shape``."""
     n = int(np.prod(shape)) if len(shape) else 1
     return _draw(seed, stream_id, n, integer=True).reshape(shape)
+
+
+def rows_f16(kind: str, shape, rows, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarray:
+    """Rows ``rows`` of ``make(kind, shape, seed, stream_id)`` (a 2-D shape),
+    drawn on their own: the generator is counter based, so row r is elements
+    r * shape[1] .. of the stream."""
+    if kind not in ("uniform", "integer"):
+        raise ValueError("kind must be 'uniform' or 'integer'")
+    n = int(shape[1])
+    out = np.empty((len(rows), n), dtype=np.float16)
+    for t, r in enumerate(rows):
+        if not 0 <= int(r) < int(shape[0]):
+            raise IndexError("row %d outside %d rows" % (int(r), int(shape[0])))
+        out[t] = _draw(seed, stream_id, n, kind == "integer", start=int(r) * n)
+    return out
 
 
 def make(kind: str, shape, seed: int = 0, stream_id: int = STREAM_A) -> np.ndarray:

@@ -60,7 +60,7 @@ def test_gemm_largest_b():
     torch.cuda.synchronize()
     got = host_u16(C)
     del C
-    ij = sample_ij(M, NG, 4000, seed=11)
+    ij = sample_ij(M, NG, 10000, seed=11)
     ij = np.concatenate([ij, [[M - 1, NG - 1], [0, NG - 1], [M - 1, NG - 1024]]]).astype(np.int64)
     ref16, _ = oracle.gemm_nt_entries(A, B, ij)
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], ref16)
@@ -91,6 +91,6 @@ def test_sparse_largest_a(cfg):
     torch.cuda.synchronize()
     got = host_u16(C)
     del C
-    ij = sample_ij(ROWS, N, 4000, seed=12)
+    ij = sample_ij(ROWS, N, 10000, seed=12)
     ij = np.concatenate([ij, [[ROWS - 1, N - 1], [ROWS - 1, 0], [ROWS - 1025, 7]]]).astype(np.int64)
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))

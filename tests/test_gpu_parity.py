@@ -185,7 +185,7 @@ def test_gemm_8192_sampled(K):
     A, B = operands("uniform", M, N, K)
     _say("gemm 8192x8192x%d uniform" % K)
     got = run_gemm(A, B)
-    ij = sample_ij(M, N, 4000, seed=K)
+    ij = sample_ij(M, N, 10000, seed=K)
     ref16, _ = oracle.gemm_nt_entries(A, B, ij)
     check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "8192x8192x%d" % K)
 
@@ -195,7 +195,7 @@ def test_gemm_8192_integer_sampled():
     A, B = operands("integer", M, N, K)
     _say("gemm 8192^3 integer")
     got = run_gemm(A, B)
-    ij = sample_ij(M, N, 4000, seed=1)
+    ij = sample_ij(M, N, 10000, seed=1)
     ref16, _ = oracle.gemm_nt_entries(A, B, ij)
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], ref16)
 
@@ -232,7 +232,7 @@ def test_gemm_row_split(M, N, K, tail):
     assert (d["block_m"], d["block_n"]) == (256, 256), "the split applies to 256 x 256 tiles only"
     m1 = split_rows(M, N)
     assert m1 < M
-    ij = sample_ij(M, N, 3000, seed=M + K)
+    ij = sample_ij(M, N, 10000, seed=M + K)
     edge = [[r, c] for r in (0, m1 - 1, m1, min(m1 + 1, M - 1), M - 1) for c in (0, N // 2, N - 1)]
     ij = np.concatenate([ij, edge]).astype(np.int64)
     A, B = operands("integer", M, N, K, seed=3)
@@ -314,7 +314,7 @@ def test_gemm_layout_8192_sampled(K, lay):
     A, B = operands("uniform", M, N, K)
     _say("gemm layout %s 8192^2 x %d" % (lay, K))
     got = run_layout(A, B, *lay)
-    ij = sample_ij(M, N, 3000, seed=11)
+    ij = sample_ij(M, N, 10000, seed=11)
     ref16, _ = oracle.gemm_nt_entries(A, B, ij)
     check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "gemm layout %s 8192^2 x %d sampled" % (lay, K))
 
@@ -501,7 +501,7 @@ def test_splitk_1024_16384(split_k, mode):
     A, B = operands("uniform", M, N, K)
     _say("splitk 1024x1024x16384 s=%d %s" % (split_k, mode))
     got = run_splitk(A, B, split_k, mode)
-    ij = sample_ij(M, N, 4000, seed=split_k)
+    ij = sample_ij(M, N, 10000, seed=split_k)
     _, ref32 = oracle.gemm_nt_entries(A, B, ij)
     check_f32_splitk_tolerance(got[ij[:, 0], ij[:, 1]], ref32, K, "splitk s=%d %s" % (split_k, mode))
     Ai, Bi = operands("integer", M, N, K)
@@ -587,7 +587,7 @@ def test_splitk_f16_1024_16384(split_k):
     A, B = operands("uniform", M, N, K)
     _say("splitk f16 1024x1024x16384 s=%d" % split_k)
     got = run_splitk_f16(A, B, split_k)
-    ij = sample_ij(M, N, 4000, seed=100 + split_k)
+    ij = sample_ij(M, N, 10000, seed=100 + split_k)
     ref16, _ = oracle.gemm_nt_entries(A, B, ij)
     check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "splitk f16 s=%d" % split_k)
     Ai, Bi = operands("integer", M, N, K)

@@ -236,7 +236,7 @@ def test_sparse_end_to_end_8192_sampled():
     rAsp, rE = oracle.sp24_compress(A)
     assert np.array_equal(host_e(E_t), rE)
     assert np.array_equal(host_u16(Asp_t), rAsp)
-    ij = sample_ij(M, N, 4000, seed=5)
+    ij = sample_ij(M, N, 10000, seed=5)
     got = host_u16(C)[ij[:, 0], ij[:, 1]]
     ref = oracle.gemm_sp_nt_entries(rAsp, rE, B, ij)
     check_f16_tolerance(got, ref, "sparse 8192 sampled")
@@ -249,7 +249,7 @@ def test_sparse_8192_integer_sampled():
     Asp, E = oracle.sp24_compress(A)
     _say("sparse 8192 integer")
     got = sp_run(Asp, E, B)
-    ij = sample_ij(M, N, 4000, seed=6)
+    ij = sample_ij(M, N, 10000, seed=6)
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))
 
 
@@ -263,7 +263,7 @@ def test_sparse_default_paired_shape_sampled():
     Asp, E = oracle.sp24_compress(A)
     _say("sparse default paired %dx%dx%d" % (M, N, K))
     got = sp_run(Asp, E, B)
-    ij = sample_ij(M, N, 4000, seed=13)
+    ij = sample_ij(M, N, 10000, seed=13)
     ij = np.concatenate([ij, [[M - 1, N - 1], [0, N - 1], [M - 1, 0]]]).astype(np.int64)
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))
 
@@ -275,7 +275,7 @@ def test_sparse_row_split(M, N, K):
     Integer inputs bit-exact on sampled entries around the split; uniform
     inputs give the same bits as one launch of the default tile."""
     m1 = {7168: 6912, 6144: 5376}[M]
-    ij = sample_ij(M, N, 3000, seed=M + K)
+    ij = sample_ij(M, N, 10000, seed=M + K)
     edge = [[r, c] for r in (0, m1 - 1, m1, M - 1) for c in (0, N // 2, N - 1)]
     ij = np.concatenate([ij, edge]).astype(np.int64)
     A = inputs.sparse24("integer", (M, K), seed=4)

@@ -367,3 +367,45 @@ def test_generator_counter_based_and_ranges():
     z = inputs.integer_f16((100000,), 0, 0).astype(np.int64)
     assert set(np.unique(z)) == {-2, -1, 0, 1, 2}
     assert not np.array_equal(inputs.uniform_f16((64,), 0, 0), inputs.uniform_f16((64,), 0, 1))
+
+
+# ----------------------------------------------------------------------------
+# The double oracle against exact integer sums on the full-size workloads
+# ----------------------------------------------------------------------------
+
+def test_row_draws_match_the_full_draw():
+    """inputs.rows_f16 (used below to draw only the rows that sampled
+    entries need) gives exactly the rows of the full draw."""
+    for kind in ("uniform", "integer"):
+        full = inputs.make(kind, (37, 129), 5, 1)
+        rows = [36, 0, 17, 17, 3]
+        got = inputs.rows_f16(kind, (37, 129), rows, 5, 1)
+        assert np.array_equal(got.view(np.uint16), full[rows].view(np.uint16))
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 1024), (8192, 8192, 4096), (8192, 8192, 8192),
+                                   (8192, 8192, 16384), (1024, 1024, 16384)])
+def test_oracle_exact_on_workload_entries(M, N, K):
+    """At least 10,000 entries of each large workload (the seeded uniform
+    operands of the 8192^2 x K products and of the split-K product): the
+    double oracle's fp16 and fp32 results equal, bit for bit, the exact sums
+    rounded with integer round-to-nearest-even.  Uniform fp16 values in
+    [-1, 1] are m * 2^-24 with |m| <= 2^24, so each product is below 2^48 and
+    a sum of K <= 2^14 of them fits in int64: the exact sum is an int64
+    matrix product of the scaled operands."""
+    rng = np.random.default_rng(M + K)
+    ri = np.sort(rng.choice(M, 100, replace=False))
+    rj = np.sort(rng.choice(N, 101, replace=False))
+    A = inputs.rows_f16("uniform", (M, K), ri, 0, inputs.STREAM_A)
+    B = inputs.rows_f16("uniform", (N, K), rj, 0, inputs.STREAM_B)
+    ia = (A.astype(np.float64) * float(2 ** 24)).astype(np.int64)
+    ib = (B.astype(np.float64) * float(2 ** 24)).astype(np.int64)
+    assert np.abs(ia).max() <= 2 ** 24 and np.abs(ib).max() <= 2 ** 24
+    S = ia @ ib.T                                     # exact: |S| < 2^62
+    ij = np.stack(np.meshgrid(np.arange(100), np.arange(101), indexing="ij"), -1).reshape(-1, 2)
+    o16, o32 = oracle.gemm_nt_entries(A, B, ij)
+    assert ij.shape[0] >= 10000
+    want16 = np.array([exact_f16_bits(int(S[i, j]), 48) for i, j in ij], dtype=np.uint16)
+    want32 = np.array([exact_f32_bits(int(S[i, j]), 48) for i, j in ij], dtype=np.uint32)
+    assert np.array_equal(o16, want16)
+    assert np.array_equal(f32_bits(o32), want32)
