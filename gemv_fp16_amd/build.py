@@ -7,7 +7,9 @@ next to this file so that it travels with the source tree.
 """
 from __future__ import annotations
 
+import json
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -17,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgemvfp16.so")
+# Per-kernel register, scratch, LDS and occupancy figures from the compiler
+# (its kernel-resource-usage remarks), written at every build.
+RESOURCES = os.path.join(PKG, "kernel_resources.json")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 N_SHARDS = 8  # must match gf::kGemmShards
 
@@ -35,14 +40,46 @@ def _units():
     return units
 
 
+_REMARK = re.compile(r"remark:\s+(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]):\s*(\S+)")
+_KEYS = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch_bytes",
+         "Occupancy [waves/SIMD]": "occupancy_waves_per_simd", "SGPRs Spill": "sgpr_spills",
+         "VGPRs Spill": "vgpr_spills", "LDS Size [bytes/block]": "static_lds_bytes"}
+
+
+def parse_resource_remarks(text: str) -> dict:
+    """{mangled kernel name: {vgprs, agprs, sgprs, scratch_bytes, ...}} from
+    the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(text):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[_KEYS[key]] = int(val)
+    return out
+
+
 def _compile(unit):
     src, obj, extra = unit
     out = os.path.join(OBJ, obj)
-    cmd = [HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC] + FLAGS + extra + ["-Rpass-analysis=kernel-resource-usage", "-c",
+                                     os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
-    return out
+    return out, parse_resource_remarks(r.stderr)
+
+
+def _demangle(names):
+    try:
+        r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True, check=True)
+        dem = r.stdout.split("\n")
+        if len(dem) >= len(names):
+            return dem[:len(names)]
+    except (OSError, subprocess.CalledProcessError):
+        pass
+    return list(names)
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
@@ -50,7 +87,16 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, _units()))
+        results = list(ex.map(_compile, _units()))
+    objs = [o for o, _ in results]
+    res = {}
+    for _, r in results:
+        res.update(r)
+    names = sorted(res)
+    report = {m: dict(res[m], name=d) for m, d in zip(names, _demangle(names))}
+    with open(RESOURCES + ".tmp", "w") as f:
+        json.dump(report, f, indent=0, sort_keys=True)
+    os.replace(RESOURCES + ".tmp", RESOURCES)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -11,14 +11,22 @@ warmed up and timed, the lowest latency wins).  Here the candidates are the
 tile configs compiled into the library (the grid minus the ones whose LDS or
 wave layout does not fit a CU, reported as "unsupported").
 
-Gate: before timing, each candidate's output on integer inputs in {-2..2}
-must equal, bit for bit, the output of the library's default config (those
-results are exact, so every correct kernel agrees), and on uniform inputs it
-must stay within 1 fp16 ulp + 1e-3 of it.  Timing: HIP events around
-`--reps` back-to-back launches after `--warmup` launches; the median of
-`--trials` such batches is recorded.  Results are appended as JSON lines to
-`--out` as they are measured; a rerun skips (shape, config) records already
-present, so an interrupted sweep resumes.
+Gate: before timing, each candidate is checked against the CPU oracle's
+expected values for the same seeded inputs, read from a file that a
+committed script writes with the oracle alone (tests/golden/
+make_sweep_expected.py; the default path is that folder's file for the
+shape): sampled entries of C for the GEMMs, every output for the GEMV.
+Integer inputs in {-2..2} must match bit for bit, uniform inputs within
+1 fp16 ulp + 1e-3.  Without an expected file for the shape the sweep refuses
+to run.  Legality: like the grid filter of the autotune tutorial page,
+configs that do not fit (LDS, wave layout) are "unsupported", and configs
+whose compiled kernel spills registers to scratch memory (the build's
+resource report, gemv_fp16_amd/resources.py) are marked "spills" and not
+timed.  Timing: HIP events around `--reps` back-to-back launches after
+`--warmup` launches; the median of `--trials` such batches is recorded.
+Results are appended as JSON lines to `--out` as they are measured; a rerun
+skips (shape, config) records already present, so an interrupted sweep
+resumes.
 """
 from __future__ import annotations
 
@@ -31,9 +39,31 @@ import time
 import numpy as np
 
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
 def _u16(t):
     import torch
     return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def expected_path(op, shape):
+    return os.path.join(GOLDEN, "sweep_expected_%s_%s.txt" % (op, "x".join(str(v) for v in shape)))
+
+
+def load_expected(path, shape):
+    """(index columns, uniform fp16 bits, integer fp16 bits) from an expected
+    file written by tests/golden/make_sweep_expected.py for `shape`."""
+    if not path or not os.path.exists(path):
+        raise SystemExit("no oracle expected values for shape %s (%s); write them with "
+                         "tests/golden/make_sweep_expected.py" % (shape, path))
+    want = "shape " + " ".join(str(v) for v in shape)
+    head = [ln[1:].strip() for ln in open(path) if ln.startswith("#")]
+    if want not in head:
+        raise SystemExit("%s is not for shape %s" % (path, shape))
+    a = np.loadtxt(path, comments="#", dtype=np.int64, ndmin=2)
+    return a[:, :-2], a[:, -2].astype(np.uint16), a[:, -1].astype(np.uint16)
 
 
 def _ulp(bits):
@@ -102,21 +132,22 @@ def _parse_only(only):
     return out
 
 
-def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
+def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only="", expected=None):
     import torch
     import gemv_fp16_amd as gf
     import inputs
+    from gemv_fp16_amd import resources
+    shape = [M, N, K]
+    ij, ref_u, ref_i = load_expected(expected or expected_path("gemm", shape), shape)
+    ii, jj = ij[:, 0], ij[:, 1]
     A = torch.from_numpy(inputs.uniform_f16((M, K), 0, 0)).cuda()
     B = torch.from_numpy(inputs.uniform_f16((N, K), 0, 1)).cuda()
     Ai = torch.from_numpy(inputs.integer_f16((M, K), 0, 0)).cuda()
     Bi = torch.from_numpy(inputs.integer_f16((N, K), 0, 1)).cuda()
     C = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    ref_u = _u16(gf.gemm_f16_nt(A, B))
-    ref_i = _u16(gf.gemm_f16_nt(Ai, Bi))
     default = gf.gemm_default_config(M, N, K)
     seen = _done(out)
     flops = 2.0 * M * N * K
-    shape = [M, N, K]
     keep = _parse_only(only)
     for cfg, ok in gf.gemm_configs():
         if keep and (cfg["block_m"], cfg["block_n"], cfg["block_k"], cfg["stages"],
@@ -132,9 +163,14 @@ def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
                 rec["status"] = "unsupported"
                 _emit(out, rec)
                 continue
+            fig = resources.gemm(c)
+            if resources.spills(fig):
+                rec.update(status="spills", scratch_bytes=fig["scratch_bytes"], vgpr_spills=fig["vgpr_spills"])
+                _emit(out, rec)
+                continue
             try:
-                ci = _u16(gf.gemm_f16_nt(Ai, Bi, cfg=c))
-                cu = _u16(gf.gemm_f16_nt(A, B, cfg=c))
+                ci = _u16(gf.gemm_f16_nt(Ai, Bi, cfg=c))[ii, jj]
+                cu = _u16(gf.gemm_f16_nt(A, B, cfg=c))[ii, jj]
             except RuntimeError as e:
                 rec["status"] = "error: %s" % e
                 _emit(out, rec)
@@ -149,12 +185,15 @@ def sweep_gemm(M, N, K, reps, warmup, trials, out, rasters=(0, 1), only=""):
             _emit(out, rec)
 
 
-def sweep_sparse(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
+def sweep_sparse(M, N, K, reps, warmup, trials, out, rasters=(0, 1), expected=None):
     """The 2:4 sparse product's tile configs: A uniform (dense, pruned by the
     compression) and 2:4 integer inputs for the bit-exact gate."""
     import torch
     import gemv_fp16_amd as gf
     import inputs
+    shape = [M, N, K]
+    ij, ref_u, ref_i = load_expected(expected or expected_path("sparse", shape), shape)
+    ii, jj = ij[:, 0], ij[:, 1]
     A = torch.from_numpy(inputs.uniform_f16((M, K), 0, 0)).cuda()
     B = torch.from_numpy(inputs.uniform_f16((N, K), 0, 1)).cuda()
     Ai = torch.from_numpy(inputs.sparse24("integer", (M, K), 0, 0)).cuda()
@@ -163,12 +202,9 @@ def sweep_sparse(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
     Aspi, Ei = gf.sp24_compress_f16(Ai)
     del A, Ai
     C = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    ref_u = _u16(gf.gemm_sp_f16_nt(Asp, E, B))
-    ref_i = _u16(gf.gemm_sp_f16_nt(Aspi, Ei, Bi))
     default = gf.sp_default_config(M, N, K)
     seen = _done(out)
     flops = 2.0 * M * N * K
-    shape = [M, N, K]
     for cfg in gf.sp_configs():
         for raster in rasters:
             c = dict(cfg, raster=raster)
@@ -176,8 +212,8 @@ def sweep_sparse(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
             if key in seen:
                 continue
             rec = {"op": "sparse", "shape": shape, "config": c}
-            ci = _u16(gf.gemm_sp_f16_nt(Aspi, Ei, Bi, cfg=c))
-            cu = _u16(gf.gemm_sp_f16_nt(Asp, E, B, cfg=c))
+            ci = _u16(gf.gemm_sp_f16_nt(Aspi, Ei, Bi, cfg=c))[ii, jj]
+            cu = _u16(gf.gemm_sp_f16_nt(Asp, E, B, cfg=c))[ii, jj]
             if not np.array_equal(ci, ref_i) or not _close(cu, ref_u):
                 rec["status"] = "mismatch"
                 _emit(out, rec)
@@ -188,10 +224,13 @@ def sweep_sparse(M, N, K, reps, warmup, trials, out, rasters=(0, 1)):
             _emit(out, rec)
 
 
-def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,)):
+def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,), expected=None):
     import torch
     import gemv_fp16_amd as gf
     import inputs
+    shape = [N, K]
+    nn, ref_u, ref_i = load_expected(expected or expected_path("gemv", shape), shape)
+    nn = nn[:, 0]
     wbytes = N * K * 2
     copies = max(1, min(64, -(-(640 << 20) // max(wbytes, 1))))
     Ws = [torch.from_numpy(inputs.uniform_f16((N, K), i, 0)).cuda() for i in range(copies)]
@@ -199,11 +238,8 @@ def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,)):
     Wi = torch.from_numpy(inputs.integer_f16((N, K), 0, 0)).cuda()
     xi = torch.from_numpy(inputs.integer_f16((K,), 0, 1)).cuda()
     y = torch.empty((N,), dtype=torch.float16, device="cuda")
-    ref_u = _u16(gf.gemv_f16(Ws[0], x))
-    ref_i = _u16(gf.gemv_f16(Wi, xi))
     default = gf.gemv_default_config(N, K)
     seen = _done(out)
-    shape = [N, K]
     nbytes = 2.0 * N * K + 2.0 * K + 2.0 * N
     cands = [dict(c0, blocks=nb) for c0 in gf.gemv_configs() for nb in blocks]
     for c in cands:
@@ -211,8 +247,8 @@ def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,)):
         if key in seen:
             continue
         rec = {"op": "gemv", "shape": shape, "config": c}
-        yi = _u16(gf.gemv_f16(Wi, xi, cfg=c))
-        yu = _u16(gf.gemv_f16(Ws[0], x, cfg=c))
+        yi = _u16(gf.gemv_f16(Wi, xi, cfg=c))[nn]
+        yu = _u16(gf.gemv_f16(Ws[0], x, cfg=c))[nn]
         if not np.array_equal(yi, ref_i) or not _close(yu, ref_u):
             rec["status"] = "mismatch"
             _emit(out, rec)
@@ -243,14 +279,16 @@ def main(argv=None):
     ap.add_argument("--out", default="")
     ap.add_argument("--only", default="", help="gemm configs 'bm,bn,bk,stages,threads[,schedule];...'")
     ap.add_argument("--blocks", type=int, nargs="*", default=[0], help="gemv grid bounds (0 = none)")
+    ap.add_argument("--expected", default="",
+                    help="oracle expected-values file (default: tests/golden/sweep_expected_<op>_<shape>.txt)")
     a = ap.parse_args(argv)
     t = time.time()
     if a.op == "gemm":
-        sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster), a.only)
+        sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster), a.only, a.expected)
     elif a.op == "sparse":
-        sweep_sparse(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster))
+        sweep_sparse(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster), a.expected)
     else:
-        sweep_gemv(a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.blocks))
+        sweep_gemv(a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.blocks), a.expected)
     print("sweep done in %.1f s" % (time.time() - t), file=sys.stderr, flush=True)
 
 
