@@ -3,26 +3,36 @@
 split-K on their workloads, with roofline fractions and the CPU oracle timed
 on the host cores.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100]
 
 One step is one C = A . B^T call at 8192^3 (fp16 in, fp32 accumulate, fp16
 out) on torch's current stream with A and B already resident in HBM.  The
-headline value is whole-job TFLOP/s over the timed steps (wall clock,
-bracketed by device synchronisation).  The GEMV (N = K = 8192 and 1024),
-split-K (M = N = 1024, K = 16384) and 2:4 sparse GEMM (8192^3, plus the
-compression of its A) figures are reported in "extra", each
-timed with HIP events on the launching stream around batches of
-back-to-back launches; GEMV rotates over enough W
-copies (> 512 MiB) that every call streams W from HBM, not from the 256 MiB
-MALL.  Prints exactly one JSON line on stdout; progress goes to stderr.
+steps rotate over three copies of the seed-0 operands (768 MiB, three times
+the 256 MiB MALL), so every step reads A and B from HBM; the same steps on
+one copy are timed too, as the cache-warm figure.  The headline value is
+whole-job TFLOP/s over the timed steps (wall clock, bracketed by device
+synchronisation); each step is also bracketed by its own HIP events on the
+launching stream (median, min, p90, mean).  The shader clock is sampled
+from the driver (from the warmup on, since its reading lags the load) and
+reported over the timed steps.
+
+The other workloads are reported in "extra", each timed the same way: at
+least 10 warmup calls, then at least 100 calls each bracketed by its own
+events (median primary, min, p90), rotating over input copies larger than
+the MALL where the workload allows.  Prints exactly one JSON line on stdout;
+progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -33,6 +43,7 @@ sys.path.insert(0, ROOT)
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 PEAK_F16_SPARSE_TFLOPS = 5000.0   # MI355X fp16 MFMA with 2:4 structured sparsity, published
+MALL_BYTES = 256 << 20
 
 
 def log(msg):
@@ -74,41 +85,420 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def time_batch(torch, fn, reps, warmup, trials=3):
-    """Seconds per call: HIP events on the current stream around `reps`
-    back-to-back calls (median of `trials` batches), after `warmup` calls."""
-    for _ in range(warmup):
-        fn()
+# ---------------------------------------------------------------------------
+# clocks and ceilings
+# ---------------------------------------------------------------------------
+
+class ClockSampler:
+    """Samples the GPU's current shader clock from the driver's DPM table
+    (the line marked '*' of pp_dpm_sclk) every few milliseconds on a host
+    thread.  Only used when the host shows exactly one GPU."""
+
+    def __init__(self, period_s=0.002):
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if len(paths) == 1 else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self):
+        try:
+            for line in open(self.path):
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                    if m:
+                        return int(m.group(1))
+        except OSError:
+            return None
+        return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append((time.perf_counter(), v))
+            time.sleep(self.period)
+
+    def start(self):
+        if self.path:
+            self.samples = []
+            self._stop.clear()
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self, t0=None, t1=None):
+        """Stop sampling; MHz statistics of the samples taken between host
+        times t0 and t1 (all samples when not given)."""
+        if not self._thread:
+            return None
+        self._stop.set()
+        self._thread.join()
+        self._thread = None
+        s = np.array([v for t, v in self.samples
+                      if (t0 is None or t >= t0) and (t1 is None or t <= t1)], dtype=np.float64)
+        if s.size == 0:
+            return None
+        return {"median": float(np.median(s)), "mean": round(float(s.mean()), 1), "min": float(s.min()),
+                "max": float(s.max()), "samples": int(s.size), "source": self.path}
+
+
+def mfma_ceiling():
+    """The dense MFMA ceiling on this machine: the mfmapeak probe (independent
+    MFMAs on uniform[-1,1] operands, no memory traffic) run as a child
+    process before this process touches the GPU.  TFLOP/s and clock, or None."""
+    probe = os.path.join(ROOT, "gemv_fp16_amd", "mfmapeak")
+    if not os.path.exists(probe):
+        return None
+    try:
+        r = subprocess.run([probe], capture_output=True, text=True, timeout=120)
+    except (OSError, subprocess.TimeoutExpired):
+        return None
+    m = re.search(r"([\d.]+) TFLOP/s.*mean shader clock ([\d.]+) GHz", r.stdout)
+    if r.returncode != 0 or not m:
+        return None
+    return {"tflops": float(m.group(1)), "sclk_ghz": float(m.group(2)), "line": r.stdout.strip()}
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def time_reps(torch, fns, reps=100, warmup=10):
+    """Per-call seconds: `warmup` calls, then `reps` calls each bracketed by
+    its own HIP events on the current stream, rotating over `fns`."""
+    if callable(fns):
+        fns = [fns]
+    for i in range(warmup):
+        fns[i % len(fns)]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    res = []
-    for _ in range(trials):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for i, (s, e) in enumerate(evs):
         s.record(stream)
-        for _ in range(reps):
-            fn()
+        fns[i % len(fns)]()
         e.record(stream)
-        torch.cuda.synchronize()
-        res.append(s.elapsed_time(e) * 1e-3 / reps)
-    return float(np.median(res))
+    torch.cuda.synchronize()
+    return np.array([s.elapsed_time(e) for s, e in evs]) * 1e-3
+
+
+def time_batch(torch, fns, reps=100, warmup=10):
+    """Seconds per call over one event-bracketed batch of `reps` back-to-back
+    calls (rotating over `fns`), after `warmup` calls."""
+    if callable(fns):
+        fns = [fns]
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e-3 / reps
+
+
+def stats(t, work=None, unit_scale=1e12):
+    """median / min / p90 / mean of per-call seconds, in us, plus the rate
+    (work / median) when `work` is given."""
+    out = {"median_us": round(float(np.median(t)) * 1e6, 3), "min_us": round(float(t.min()) * 1e6, 3),
+           "p90_us": round(float(np.percentile(t, 90)) * 1e6, 3),
+           "mean_us": round(float(t.mean()) * 1e6, 3), "reps": int(t.size)}
+    if work is not None:
+        out["rate_median"] = round(work / float(np.median(t)) / unit_scale, 2)
+    return out
+
+
+def copies_for(bytes_each, budget=3 * MALL_BYTES, cap=8):
+    """How many copies of an input set of `bytes_each` to rotate so that the
+    rotation exceeds the MALL (3x its size), capped."""
+    return int(max(1, min(cap, -(-budget // max(1, bytes_each)))))
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(A_np, B_np, rows, one_core_rows):
+    """The oracle on the host cores: the bounded sample of the headline
+    product (rows 0..rows-1) on every thread OpenMP uses, a 1-thread rate on
+    a smaller row sample, and per-config oracle seconds (full outputs where
+    they are small; a row sample extrapolated to the full output otherwise)."""
+    import inputs
+    import oracle
+    M, K = A_np.shape
+    N = B_np.shape[0]
+    threads = oracle.threads()
+    t = time.perf_counter()
+    oracle.gemm_nt_f16(A_np, B_np, rows=(0, rows))
+    dt = time.perf_counter() - t
+    tflops = 2.0 * rows * N * K / dt / 1e12
+    oracle.set_threads(1)
+    t = time.perf_counter()
+    oracle.gemm_nt_f16(A_np, B_np, rows=(0, one_core_rows))
+    dt1 = time.perf_counter() - t
+    oracle.set_threads(threads)
+    per_config = {}
+    # config 1: 256^3, both input kinds, full output
+    t = time.perf_counter()
+    for kind in ("uniform", "integer"):
+        oracle.gemm_nt_f16(inputs.make(kind, (256, 256), 0, 0), inputs.make(kind, (256, 256), 0, 1))
+    per_config["gemm_256^3_uniform+integer_full_s"] = round(time.perf_counter() - t, 4)
+    # config 2: M = N = 8192, K = 1024 .. 16384 -- 256 rows each, scaled to 8192 rows
+    est = 0.0
+    for k2 in (1024, 4096, 16384):
+        a2 = inputs.uniform_f16((256, k2), 0, 0)
+        b2 = inputs.uniform_f16((8192, k2), 0, 1)
+        t = time.perf_counter()
+        oracle.gemm_nt_f16(a2, b2)
+        est += (time.perf_counter() - t) * 8192 / 256
+    est += dt * 8192 / rows                            # K = 8192: the headline sample
+    per_config["gemm_8192^2_xK_1024+4096+8192+16384_est_s"] = round(est, 1)
+    # config 3: split-K 1024^2 x 16384, full fp32 output
+    a3 = inputs.uniform_f16((1024, 16384), 0, 0)
+    b3 = inputs.uniform_f16((1024, 16384), 0, 1)
+    t = time.perf_counter()
+    oracle.gemm_nt_f32(a3, b3)
+    per_config["splitk_1024^2x16384_full_s"] = round(time.perf_counter() - t, 3)
+    # config 5: GEMV 8192^2 and 1024^2, full output
+    t = time.perf_counter()
+    for nk in (8192, 1024):
+        oracle.gemv_f16(inputs.uniform_f16((nk, nk), 0, 0), inputs.uniform_f16((nk,), 0, 1))
+    per_config["gemv_8192^2+1024^2_full_s"] = round(time.perf_counter() - t, 3)
+    return {
+        "value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": "rows 0..%d of C = A.B^T at M=N=K=8192 (%d x 8192 outputs, double accumulation), "
+                  "%.1f s wall on %d threads" % (rows - 1, rows, dt, threads),
+        "hardware_concurrency": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "one_core": {"value": round(2.0 * one_core_rows * N * K / dt1 / 1e12, 6), "unit": "TFLOP/s",
+                     "sample": "rows 0..%d of the same product on 1 thread, %.1f s" % (one_core_rows - 1, dt1)},
+        "per_config_oracle_seconds": per_config,
+    }
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------
+
+def gpu_operands(torch, inputs, shape_a, shape_b, copies, seed=0):
+    """`copies` device copies of the seeded uniform operands (same values)."""
+    a = torch.from_numpy(inputs.uniform_f16(shape_a, seed, inputs.STREAM_A)).cuda()
+    b = torch.from_numpy(inputs.uniform_f16(shape_b, seed, inputs.STREAM_B)).cuda()
+    return [a] + [a.clone() for _ in range(copies - 1)], [b] + [b.clone() for _ in range(copies - 1)]
+
+
+def extras(torch, gf, inputs, A, B, C):
+    M, N, K = A.shape[0], B.shape[0], A.shape[1]
+    flops = 2.0 * M * N * K
+    extra = {}
+
+    # ---- GEMM, K swept (A, B rotated over copies larger than the MALL) ----
+    sweep = {}
+    for k2 in (256, 512, 1024, 4096, 16384):
+        n = copies_for(2 * (M + N) * k2)
+        As, Bs = gpu_operands(torch, inputs, (M, k2), (N, k2), n)
+        t = time_reps(torch, [gf.prepare_gemm_f16_nt(a, b, C) for a, b in zip(As, Bs)])
+        sweep[str(k2)] = dict(stats(t, 2.0 * M * N * k2), copies=n)
+        log("gemm 8192x8192x%d: %.1f TFLOP/s (median)" % (k2, sweep[str(k2)]["rate_median"]))
+        del As, Bs
+    extra["gemm_k_sweep"] = sweep
+
+    # ---- GEMM at cube sizes whose 256 x 256 tiles leave the last round of
+    # workgroups mostly empty: the default call (leading rows in whole
+    # rounds, the rest with a smaller tile) vs one launch of the big tile,
+    # alternating batch by batch so that both see the same clock
+    quant = {}
+    for n3 in (7168, 6144):
+        As, Bs = gpu_operands(torch, inputs, (n3, n3), (n3, n3), 2)
+        c3 = torch.empty((n3, n3), dtype=torch.float16, device="cuda")
+        f3 = 2.0 * n3 ** 3
+        cfg1 = gf.gemm_default_config(n3, n3, n3)
+        plans = ([gf.prepare_gemm_f16_nt(a, b, c3) for a, b in zip(As, Bs)],
+                 [gf.prepare_gemm_f16_nt(a, b, c3, cfg=cfg1) for a, b in zip(As, Bs)])
+        times = ([], [])
+        for _ in range(5):
+            for i, p in enumerate(plans):
+                times[i].append(time_reps(torch, p, reps=20, warmup=2))
+        t_def, t_one = np.concatenate(times[0]), np.concatenate(times[1])
+        quant["%d^3" % n3] = {"default": stats(t_def, f3), "one_launch": stats(t_one, f3)}
+        del As, Bs, c3
+    log("gemm wave-quantised cubes (median TFLOP/s): %s" % {
+        k: (v["default"]["rate_median"], v["one_launch"]["rate_median"]) for k, v in quant.items()})
+    extra["gemm_row_split"] = quant
+
+    # ---- GEMM at mid-size shapes (fewer than 256 tiles of 256 x 256) ----
+    mid = {}
+    for (m4, n4, k4) in ((2048, 4096, 8192), (2048, 2048, 8192), (1024, 4096, 8192)):
+        n = copies_for(2 * (m4 + n4) * k4)
+        As, Bs = gpu_operands(torch, inputs, (m4, k4), (n4, k4), n)
+        c4 = torch.empty((m4, n4), dtype=torch.float16, device="cuda")
+        t = time_reps(torch, [gf.prepare_gemm_f16_nt(a, b, c4) for a, b in zip(As, Bs)])
+        d4 = gf.gemm_default_config(m4, n4, k4)
+        mid["%dx%dx%d" % (m4, n4, k4)] = dict(
+            stats(t, 2.0 * m4 * n4 * k4), copies=n,
+            tile="%dx%d/%d stages/schedule %d" % (d4["block_m"], d4["block_n"], d4["stages"], d4["schedule"]))
+        del As, Bs, c4
+    log("gemm mid-size shapes (median TFLOP/s): %s" % {k: v["rate_median"] for k, v in mid.items()})
+    extra["gemm_mid_shapes"] = mid
+
+    # ---- other operand layouts at 8192^3: B stored K x N (and A K x M), 2 copies
+    lay = {}
+    Bt = [B.t().contiguous() for _ in range(2)]
+    At = [A.t().contiguous() for _ in range(2)]
+    Ac = [A, A.clone()]
+    t = time_reps(torch, [lambda a=a, b=b: gf.gemm_f16(a, b, C, False, True) for a, b in zip(Ac, Bt)])
+    lay["nn"] = stats(t, flops)
+    t = time_reps(torch, [lambda a=a, b=b: gf.gemm_f16(a, b, C, True, True) for a, b in zip(At, Bt)])
+    lay["tn"] = stats(t, flops)
+    del At, Bt, Ac
+    log("gemm 8192^3 other layouts (median TFLOP/s): nn %.1f, tn %.1f" %
+        (lay["nn"]["rate_median"], lay["tn"]["rate_median"]))
+    extra["gemm_layouts_8192"] = lay
+
+    # ---- GEMV: W rotated over copies that exceed the MALL three times ----
+    gemv = {}
+    for nk in (8192, 1024):
+        wbytes = nk * nk * 2
+        copies = copies_for(wbytes, cap=256)
+        Ws = [torch.from_numpy(inputs.uniform_f16((nk, nk), 0, 0)).cuda()]
+        Ws += [Ws[0].clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(inputs.uniform_f16((nk,), 0, 1)).cuda()
+        y = torch.empty((nk,), dtype=torch.float16, device="cuda")
+        calls = [gf.prepare_gemv_f16(w, x, y) for w in Ws]
+        bytes_ = 2.0 * nk * nk + 2.0 * nk + 2.0 * nk
+        # A GEMV call lasts ~20 us, so an event pair around each call adds the
+        # event's own dispatch to it; the kernel's duration is the per-call
+        # time inside batches of back-to-back calls (which agrees with the
+        # kernel trace's average).  Both are reported; the batch is primary.
+        t_b = np.array([time_batch(torch, calls, reps=200, warmup=20 if i == 0 else 0) for i in range(7)])
+        t = time_reps(torch, calls, reps=200, warmup=20)
+        t_warm = time_batch(torch, calls[:1], reps=200, warmup=20)
+        bst = stats(t_b, bytes_, 1e9)
+        gbs = bst["rate_median"]
+        gemv[str(nk)] = {
+            "us": bst["median_us"], "GB/s": gbs, "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "batches": dict(bst, calls_per_batch=200),
+            "per_call_events": stats(t, bytes_, 1e9),
+            "w_copies_rotated": copies, "w_bytes_rotated": copies * wbytes,
+            "cache_warm_GB/s_not_hbm": round(bytes_ / t_warm / 1e9, 1),
+            "launch": gf.gemv_default_config(nk, nk)}
+        log("gemv %d: %.2f us = %.1f GB/s per call back to back (median of 7 batches); %.2f us with "
+            "events around each call; warm %.1f GB/s" % (
+                nk, bst["median_us"], gbs, gemv[str(nk)]["per_call_events"]["median_us"],
+                gemv[str(nk)]["cache_warm_GB/s_not_hbm"]))
+        del Ws
+    g8 = gemv["8192"]
+    gemv["roofline"] = {"bound": "hbm", "achieved": g8["GB/s"], "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": g8["frac_hbm_peak"],
+                        "traffic": measured_traffic("gemv_kernel", "8192^2")}
+    extra["gemv"] = gemv
+
+    # ---- skinny GEMM: M = 2..64 rows against an 8192 x 8192 B from HBM ----
+    Bsk = [torch.from_numpy(inputs.uniform_f16((8192, 8192), 0, 1)).cuda()]
+    Bsk += [Bsk[0].clone() for _ in range(5)]
+    sk_res = {}
+    for mm in (2, 4, 8, 16, 32, 64):
+        Ask = torch.from_numpy(inputs.uniform_f16((mm, 8192), 0, 0)).cuda()
+        Csk = torch.empty((mm, 8192), dtype=torch.float16, device="cuda")
+        t = time_reps(torch, [gf.prepare_gemm_f16_nt(Ask, b, Csk) for b in Bsk])
+        byt = 2.0 * 8192 * 8192 + 2.0 * mm * 8192 * 2
+        sk_res["M%d" % mm] = dict(stats(t, byt, 1e9))
+    del Bsk
+    log("skinny M x 8192 x 8192 (median GB/s): %s" % {k: v["rate_median"] for k, v in sk_res.items()})
+    extra["skinny_8192"] = sk_res
+
+    # ---- split-K at 1024^2 x 16384, operands rotated over 4 copies ----
+    sm, sk_k = 1024, 16384
+    As, Bs = gpu_operands(torch, inputs, (sm, sk_k), (sm, sk_k), 4)
+    c32 = torch.empty((sm, sm), dtype=torch.float32, device="cuda")
+    c16 = torch.empty((sm, sm), dtype=torch.float16, device="cuda")
+    ws = torch.empty(16 * sm * sm, dtype=torch.float32, device="cuda")
+    f3 = 2.0 * sm * sm * sk_k
+    sk = {}
+    for split in (4, 8, 16):
+        for mode, name in ((gf.GF_SPLITK_ATOMIC, "atomic"), (gf.GF_SPLITK_TWOPASS, "twopass")):
+            t = time_reps(torch, [lambda a=a, b=b: gf.gemm_f16_nt_splitk_ex(a, b, c32, split, mode, ws)
+                                  for a, b in zip(As, Bs)])
+            sk["%s_s%d" % (name, split)] = stats(t, f3)
+        t = time_reps(torch, [lambda a=a, b=b: gf.gemm_f16_nt_splitk_f16(a, b, c16, split, ws)
+                              for a, b in zip(As, Bs)])
+        sk["twopass_f16out_s%d" % split] = stats(t, f3)
+    t = time_reps(torch, [lambda a=a, b=b: gf.gemm_f16_nt(a, b, c16) for a, b in zip(As, Bs)])
+    sk["no_split_fp16"] = stats(t, f3)
+    best = max(sk, key=lambda k: sk[k]["rate_median"])
+    sk["best"] = {"mode": best, "tflops": sk[best]["rate_median"],
+                  "frac_mfma_peak": round(sk[best]["rate_median"] / PEAK_F16_TFLOPS, 4)}
+    log("splitk 1024x1024x16384 (median TFLOP/s): %s" % {k: v["rate_median"] for k, v in sk.items()
+                                                          if "rate_median" in v})
+    extra["splitk_1024x1024x16384"] = sk
+    del As, Bs, ws
+
+    # ---- 2:4 structured-sparse GEMM at 8192^3: the headline A compressed
+    # (pruned to 2 of every 4 along K) on the GPU, then C = A_sparse . B^T ----
+    Asp, E = gf.sp24_compress_f16(A)
+    Bc = [B, B.clone(), B.clone()]
+    Aspc, Ec = [Asp, Asp.clone(), Asp.clone()], [E, E.clone(), E.clone()]
+    t = time_reps(torch, [gf.prepare_gemm_sp_f16_nt(a, e, b, C) for a, e, b in zip(Aspc, Ec, Bc)])
+    sp = stats(t, flops)
+    sp_eff = sp["rate_median"]
+    # compression, rotating 3 inputs (384 MiB > the 256 MiB MALL)
+    Acs = [A, A.clone(), A.clone()]
+    outs = [(torch.empty_like(Asp), torch.empty_like(E)) for _ in range(3)]
+    tc = time_reps(torch, [lambda a=a, o=o: gf.sp24_compress_f16(a, *o) for a, o in zip(Acs, outs)])
+    c_bytes = 2.0 * M * K + 2.0 * M * K / 2 + 2.0 * M * K / 16
+    cst = stats(tc, c_bytes, 1e9)
+    extra["sparse24_8192"] = {
+        "gemm": sp, "tile": gf.sp_default_config(M, N, K),
+        "roofline": {"bound": "mfma", "achieved": sp_eff, "peak": PEAK_F16_SPARSE_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(sp_eff / PEAK_F16_SPARSE_TFLOPS, 4),
+                     "traffic": measured_traffic("sp_gemm_kernel", "8192^3")},
+        "compress": cst, "compress_frac_hbm_peak": round(cst["rate_median"] / PEAK_HBM_GBS, 4),
+    }
+    log("sparse 2:4 8192^3: %.1f effective TFLOP/s; compress %.1f GB/s (medians)" % (sp_eff, cst["rate_median"]))
+    del Asp, E, Acs, outs, Aspc, Ec, Bc
+    return extra
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=6144,
-                    help="rows of the 8192^3 product the CPU oracle computes")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="rows of the 8192^3 product the CPU oracle computes on all threads")
+    ap.add_argument("--cpu-rows-1t", type=int, default=48,
+                    help="rows of the 8192^3 product the CPU oracle computes on one thread")
     ap.add_argument("--no-extra", action="store_true", help="headline GEMM only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA ceiling probe")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+
+    ceiling = None
+    if not args.no_ceiling:
+        log("MFMA ceiling probe (child process, before this process uses the GPU)")
+        ceiling = mfma_ceiling()
+        log("ceiling: %s" % (ceiling["line"] if ceiling else "unavailable"))
 
     import torch
     import gemv_fp16_amd as gf
@@ -121,40 +511,54 @@ def main():
     torch.cuda.set_device(0)
 
     M = N = K = 8192
-    log("generating A, B %dx%d fp16 uniform[-1,1] seed 0" % (M, K))
+    log("generating A, B %dx%d fp16 uniform[-1,1] seed 0 (3 device copies)" % (M, K))
     A_np = inputs.uniform_f16((M, K), 0, inputs.STREAM_A)
     B_np = inputs.uniform_f16((N, K), 0, inputs.STREAM_B)
     A = torch.from_numpy(A_np).cuda()
     B = torch.from_numpy(B_np).cuda()
+    As, Bs = [A, A.clone(), A.clone()], [B, B.clone(), B.clone()]
     C = torch.empty((M, N), dtype=torch.float16, device="cuda")
     cfg = gf.gemm_default_config(M, N, K)
     flops = 2.0 * M * N * K
-
-    step = gf.prepare_gemm_f16_nt(A, B, C)
+    steps = [gf.prepare_gemm_f16_nt(a, b, C) for a, b in zip(As, Bs)]
 
     log("warmup %d" % args.warmup)
-    for _ in range(args.warmup):
-        step()
+    clock = ClockSampler().start()        # from the warmup on: the driver's reading lags the load
+    for i in range(args.warmup):
+        steps[i % 3]()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = []
-    log("timing %d steps" % args.steps)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        step()
-        e.record(stream)
-        evs.append((s, e))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    log("timing %d steps (operands rotated over 3 copies, 768 MiB)" % args.steps)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern_s = float(np.mean([s.elapsed_time(e) for s, e in evs])) * 1e-3
+    t0 = time.perf_counter()
+    for i, (s, e) in enumerate(evs):
+        s.record(stream)
+        steps[i % 3]()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    sclk = clock.stop(t0, t1)
+    t = np.array([s.elapsed_time(e) for s, e in evs]) * 1e-3
+    kern_s = float(t.mean())
     value = flops * args.steps / elapsed / 1e12
     achieved = flops / kern_s / 1e12
-    log("gemm 8192^3: %.1f TFLOP/s wall, %.1f TFLOP/s per launch (%.3f ms)" %
-        (value, achieved, kern_s * 1e3))
+    t_warm = time_reps(torch, steps[:1], reps=args.steps, warmup=2)
+    warm = stats(t_warm, flops)
+    log("gemm 8192^3: %.1f TFLOP/s wall, %.1f TFLOP/s per launch (mean %.3f ms, median %.3f ms); "
+        "cache-warm median %.1f TFLOP/s; sclk %s" % (
+            value, achieved, kern_s * 1e3, float(np.median(t)) * 1e3, warm["rate_median"],
+            sclk and "median %d MHz over %d samples" % (sclk["median"], sclk["samples"])))
 
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "traffic": measured_traffic("gemm_nt_kernel", "8192^3")}
+    if ceiling:
+        roof["measured_mfma_ceiling"] = ceiling["tflops"]
+        roof["measured_ceiling_sclk_ghz"] = ceiling["sclk_ghz"]
+        roof["frac_of_measured_ceiling"] = round(achieved / ceiling["tflops"], 4)
     out = {
         "metric": "fp16 GEMM TFLOP/s at M=N=K=8192 (% MFMA peak); GEMV GB/s (% HBM peak)",
         "value": round(value, 2),
@@ -168,207 +572,25 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "gemm_f16_nt C=A.B^T M=N=K=8192, A,B fp16 uniform[-1,1] seed 0",
+        "config": {"workload": "gemm_f16_nt C=A.B^T M=N=K=8192, A,B fp16 uniform[-1,1] seed 0, "
+                               "operands rotated over 3 device copies (768 MiB)",
                    "M": M, "N": N, "K": K, "tile": cfg},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                     "traffic": measured_traffic("gemm_nt_kernel", "8192^3")},
+        "roofline": roof,
+        "per_launch": dict(stats(t, flops), cache_warm=warm),
+        "sclk_mhz": sclk,
     }
 
-    extra = {}
     if not args.no_extra:
-        # ---- GEMM, K swept ----
-        sweep = {}
-        for k2 in (256, 512, 1024, 4096, 16384):
-            a2 = torch.from_numpy(inputs.uniform_f16((M, k2), 0, 0)).cuda()
-            b2 = torch.from_numpy(inputs.uniform_f16((N, k2), 0, 1)).cuda()
-            t2 = time_batch(torch, gf.prepare_gemm_f16_nt(a2, b2, C), 10, 3)
-            sweep[str(k2)] = round(2.0 * M * N * k2 / t2 / 1e12, 1)
-            log("gemm 8192x8192x%d: %.1f TFLOP/s" % (k2, sweep[str(k2)]))
-            del a2, b2
-        sweep[str(K)] = round(achieved, 1)
-        extra["gemm_k_sweep_tflops"] = sweep
-
-        # ---- GEMM at cube sizes whose 256 x 256 tiles leave the last round
-        # of workgroups mostly empty: the default call (leading rows in whole
-        # rounds, the rest with a smaller tile) vs one launch of the big tile
-        quant = {}
-        for n3 in (7168, 6144):
-            a3 = torch.from_numpy(inputs.uniform_f16((n3, n3), 0, 0)).cuda()
-            b3 = torch.from_numpy(inputs.uniform_f16((n3, n3), 0, 1)).cuda()
-            c3 = torch.empty((n3, n3), dtype=torch.float16, device="cuda")
-            f3 = 2.0 * n3 ** 3
-            # the two launch plans alternate batch by batch, so that both see
-            # the same clock and power state
-            plans = (gf.prepare_gemm_f16_nt(a3, b3, c3),
-                     gf.prepare_gemm_f16_nt(a3, b3, c3, cfg=gf.gemm_default_config(n3, n3, n3)))
-            times = ([], [])
-            for p in plans:
-                time_batch(torch, p, 1, 5, trials=1)
-            for _ in range(5):
-                for i, p in enumerate(plans):
-                    times[i].append(time_batch(torch, p, 10, 0, trials=1))
-            t_def, t_one = float(np.median(times[0])), float(np.median(times[1]))
-            quant["%d^3" % n3] = {"default_tflops": round(f3 / t_def / 1e12, 1),
-                                  "one_launch_tflops": round(f3 / t_one / 1e12, 1)}
-            del a3, b3, c3
-        log("gemm wave-quantised cubes: %s" % quant)
-        extra["gemm_row_split"] = quant
-
-        # ---- GEMM at mid-size shapes (fewer than 256 tiles of 256 x 256)
-        mid = {}
-        for (m4, n4, k4) in ((2048, 4096, 8192), (2048, 2048, 8192), (1024, 4096, 8192)):
-            a4 = torch.from_numpy(inputs.uniform_f16((m4, k4), 0, 0)).cuda()
-            b4 = torch.from_numpy(inputs.uniform_f16((n4, k4), 0, 1)).cuda()
-            c4 = torch.empty((m4, n4), dtype=torch.float16, device="cuda")
-            t4 = time_batch(torch, gf.prepare_gemm_f16_nt(a4, b4, c4), 20, 5)
-            d4 = gf.gemm_default_config(m4, n4, k4)
-            mid["%dx%dx%d" % (m4, n4, k4)] = {"tflops": round(2.0 * m4 * n4 * k4 / t4 / 1e12, 1),
-                                              "tile": "%dx%d/%d stages/schedule %d" % (
-                                                  d4["block_m"], d4["block_n"], d4["stages"], d4["schedule"])}
-            del a4, b4, c4
-        log("gemm mid-size shapes: %s" % mid)
-        extra["gemm_mid_shapes"] = mid
-
-        # other operand layouts at 8192^3: B stored K x N (and A K x M)
-        lay = {}
-        Bt = B.t().contiguous()
-        lay["nn"] = round(flops / time_batch(torch, lambda: gf.gemm_f16(A, Bt, C, False, True), 10, 3) / 1e12, 1)
-        At = A.t().contiguous()
-        lay["tn"] = round(flops / time_batch(torch, lambda: gf.gemm_f16(At, Bt, C, True, True), 10, 3) / 1e12, 1)
-        del At, Bt
-        log("gemm 8192^3 other layouts TFLOP/s: %s" % lay)
-        extra["gemm_layouts_8192_tflops"] = lay
-
-        # ---- GEMV ----
-        gemv = {}
-        for nk in (8192, 1024):
-            wbytes = nk * nk * 2
-            copies = max(1, -(-(640 << 20) // wbytes))
-            copies = min(copies, 64)
-            Ws = [torch.from_numpy(inputs.uniform_f16((nk, nk), i, 0)).cuda() for i in range(copies)]
-            x = torch.from_numpy(inputs.uniform_f16((nk,), 0, 1)).cuda()
-            y = torch.empty((nk,), dtype=torch.float16, device="cuda")
-            calls = [gf.prepare_gemv_f16(w, x, y) for w in Ws]
-            state = [0]
-
-            def cold(calls=calls, state=state):
-                calls[state[0] % len(calls)]()
-                state[0] += 1
-
-            t_cold = time_batch(torch, cold, 200, 20)
-            t_warm = time_batch(torch, calls[0], 200, 20)
-            bytes_ = 2.0 * nk * nk + 2.0 * nk + 2.0 * nk
-            gbs = bytes_ / t_cold / 1e9
-            gemv[str(nk)] = {
-                "us": round(t_cold * 1e6, 3), "GB/s": round(gbs, 1),
-                "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                "w_copies_rotated": copies,
-                "cache_warm_GB/s_not_hbm": round(bytes_ / t_warm / 1e9, 1),
-                "launch": gf.gemv_default_config(nk, nk),
-            }
-            log("gemv %d: %.2f us, %.1f GB/s (warm %.1f)" %
-                (nk, t_cold * 1e6, gbs, gemv[str(nk)]["cache_warm_GB/s_not_hbm"]))
-            del Ws
-        g8 = gemv["8192"]
-        gemv["roofline"] = {"bound": "hbm", "achieved": g8["GB/s"], "peak": PEAK_HBM_GBS,
-                            "unit": "GB/s", "frac": g8["frac_hbm_peak"],
-                            "traffic": measured_traffic("gemv_kernel", "8192^2")}
-        extra["gemv"] = gemv
-
-        # ---- skinny GEMM: M = 2..64 rows against an 8192 x 8192 B (decode batches;
-        # gemm_f16_nt takes the skinny kernel for all of them) ----
-        Bsk = [torch.from_numpy(inputs.uniform_f16((8192, 8192), i, 1)).cuda() for i in range(5)]
-        sk_res = {}
-        for mm in (2, 4, 8, 16, 32, 64):
-            Ask = torch.from_numpy(inputs.uniform_f16((mm, 8192), 0, 0)).cuda()
-            Csk = torch.empty((mm, 8192), dtype=torch.float16, device="cuda")
-            state = [0]
-
-            def skinny(Ask=Ask, Csk=Csk, state=state):
-                gf.gemm_f16_nt(Ask, Bsk[state[0] % len(Bsk)], Csk)
-                state[0] += 1
-
-            t = time_batch(torch, skinny, 100, 10)
-            byt = 2.0 * 8192 * 8192 + 2.0 * mm * 8192 * 2
-            sk_res["M%d" % mm] = {"us": round(t * 1e6, 2), "GB/s": round(byt / t / 1e9, 1)}
-        del Bsk
-        log("skinny M x 8192 x 8192 (B from HBM): %s" % sk_res)
-        extra["skinny_8192"] = sk_res
-
-        # ---- split-K ----
-        sm, sk_k = 1024, 16384
-        a3 = torch.from_numpy(inputs.uniform_f16((sm, sk_k), 0, 0)).cuda()
-        b3 = torch.from_numpy(inputs.uniform_f16((sm, sk_k), 0, 1)).cuda()
-        c3 = torch.empty((sm, sm), dtype=torch.float32, device="cuda")
-        ws = torch.empty(16 * sm * sm, dtype=torch.float32, device="cuda")
-        sk = {}
-        f3 = 2.0 * sm * sm * sk_k
-        for split in (4, 8, 16):
-            for mode, name in ((gf.GF_SPLITK_ATOMIC, "atomic"), (gf.GF_SPLITK_TWOPASS, "twopass")):
-                t3 = time_batch(torch, lambda: gf.gemm_f16_nt_splitk_ex(
-                    a3, b3, c3, split, mode, ws), 50, 5)
-                sk["%s_s%d" % (name, split)] = round(f3 / t3 / 1e12, 1)
-        c16 = torch.empty((sm, sm), dtype=torch.float16, device="cuda")
-        for split in (4, 8, 16):
-            t3 = time_batch(torch, lambda: gf.gemm_f16_nt_splitk_f16(a3, b3, c16, split, ws), 50, 5)
-            sk["twopass_f16out_s%d" % split] = round(f3 / t3 / 1e12, 1)
-        t3 = time_batch(torch, lambda: gf.gemm_f16_nt(a3, b3, c16), 50, 5)
-        sk["no_split_fp16"] = round(f3 / t3 / 1e12, 1)
-        log("splitk 1024x1024x16384 TFLOP/s: %s" % sk)
-        extra["splitk_1024x1024x16384_tflops"] = sk
-        del a3, b3, c3, ws
-
-        # ---- 2:4 structured-sparse GEMM at 8192^3: the headline A compressed
-        # (pruned to 2 of every 4 along K) on the GPU, then C = A_sparse . B^T ----
-        Asp, E = gf.sp24_compress_f16(A)
-        t_sp = time_batch(torch, gf.prepare_gemm_sp_f16_nt(Asp, E, B, C), 20, 5)
-        sp_eff = flops / t_sp / 1e12
-        # compression, rotating 3 inputs (384 MiB > the 256 MiB MALL)
-        Acs = [A] + [torch.from_numpy(inputs.uniform_f16((M, K), i, 0)).cuda() for i in (1, 2)]
-        outs = [(torch.empty_like(Asp), torch.empty_like(E)) for _ in range(3)]
-        state = [0]
-
-        def comp(state=state):
-            j = state[0] % 3
-            gf.sp24_compress_f16(Acs[j], *outs[j])
-            state[0] += 1
-
-        t_c = time_batch(torch, comp, 60, 6)
-        c_bytes = 2.0 * M * K + 2.0 * M * K / 2 + 2.0 * M * K / 16
-        extra["sparse24_8192"] = {
-            "gemm_ms": round(t_sp * 1e3, 4),
-            "gemm_tflops_effective": round(sp_eff, 1),
-            "tile": gf.sp_default_config(M, N, K),
-            "roofline": {"bound": "mfma", "achieved": round(sp_eff, 2), "peak": PEAK_F16_SPARSE_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(sp_eff / PEAK_F16_SPARSE_TFLOPS, 4),
-                         "traffic": measured_traffic("sp_gemm_kernel", "8192^3")},
-            "compress_us": round(t_c * 1e6, 2),
-            "compress_GB/s": round(c_bytes / t_c / 1e9, 1),
-            "compress_frac_hbm_peak": round(c_bytes / t_c / 1e9 / PEAK_HBM_GBS, 4),
-        }
-        log("sparse 2:4 8192^3: %.1f effective TFLOP/s (%.3f ms); compress %.1f us, %.1f GB/s" %
-            (sp_eff, t_sp * 1e3, t_c * 1e6, c_bytes / t_c / 1e9))
-        del Asp, E, Acs, outs
+        out["extra"] = extras(torch, gf, inputs, A, B, C)
 
     if not args.no_cpu:
-        import oracle
         rows = max(1, min(args.cpu_rows, M))
-        log("cpu oracle: %d rows of the 8192^3 product" % rows)
-        t = time.perf_counter()
-        oracle.gemm_nt_f16(A_np, B_np, rows=(0, rows))
-        dt = time.perf_counter() - t
-        out["cpu_baseline"] = {
-            "value": round(2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.threads(), "kind": "oracle",
-            "sample": "rows 0..%d of C = A.B^T at M=N=K=8192 (%d x 8192 outputs, double "
-                      "accumulation), %.1f s wall" % (rows - 1, rows, dt),
-        }
-        log("cpu oracle: %.3g TFLOP/s on %d threads (%.1f s)" %
-            (out["cpu_baseline"]["value"], oracle.threads(), dt))
+        log("cpu oracle: %d rows of the 8192^3 product, a 1-thread sample, per-config seconds" % rows)
+        out["cpu_baseline"] = cpu_baseline(A_np, B_np, rows, max(1, min(args.cpu_rows_1t, M)))
+        log("cpu oracle: %.3g TFLOP/s on %d threads, %.3g on one" % (
+            out["cpu_baseline"]["value"], out["cpu_baseline"]["cores"],
+            out["cpu_baseline"]["one_core"]["value"]))
 
-    if extra:
-        out["extra"] = extra
     print(json.dumps(out), flush=True)
 
 

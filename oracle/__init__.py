@@ -83,6 +83,8 @@ def _load():
     lib.oracle_f16_decode_array.restype = None
     lib.oracle_sp24_compress.argtypes = [u16p, u16p, u16p, c_int, c_int]
     lib.oracle_sp24_decompress.argtypes = [u16p, u16p, u16p, c_int, c_int]
+    lib.oracle_set_threads.argtypes = [c_int]
+    lib.oracle_set_threads.restype = None
     for name in ("oracle_gemm_nt_f16_rows", "oracle_gemm_nt_f16", "oracle_gemm_nt_f32",
                  "oracle_gemm_nt_entries", "oracle_gemv_f16", "oracle_threads",
                  "oracle_sp24_compress", "oracle_sp24_decompress"):
@@ -107,6 +109,11 @@ def _u16(a) -> np.ndarray:
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n OpenMP threads in the oracle's parallel loops from now on."""
+    _load().oracle_set_threads(int(n))
 
 
 def f16_to_double(h: int) -> float:

@@ -154,6 +154,17 @@ int oracle_threads(void)
 #endif
 }
 
+/* Threads for the parallel loops that follow (n >= 1); timing only. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---- GEMM, fp16 out: rows [row_begin, row_end) of C ------------------ */
 int oracle_gemm_nt_f16_rows(const uint16_t* A, const uint16_t* B, uint16_t* C,
                             int M, int N, int K, int row_begin, int row_end)

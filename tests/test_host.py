@@ -100,3 +100,95 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_clock_sampler_reads_the_marked_dpm_level(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1487Mhz *\n2: 2400Mhz\n")
+    cs = bench.ClockSampler(period_s=0.001)
+    cs.path = str(f)
+    assert cs._read() == 1487
+    import time
+    t0 = time.perf_counter()
+    cs.start()
+    time.sleep(0.05)
+    r = cs.stop(t0, time.perf_counter())
+    assert r["median"] == 1487 and r["min"] == 1487 and r["samples"] >= 1
+    f.write_text("0: 500Mhz\n1: 158Mhz\n")          # no marked level
+    assert cs._read() is None
+    cs.path = None                                    # several or no GPUs: not sampled
+    assert cs.start().stop() is None
+
+
+def test_stats_and_copy_rotation():
+    t = np.array([3.0, 1.0, 2.0, 4.0, 10.0]) * 1e-6
+    s = bench.stats(t, work=2e-6 * 1e12)
+    assert s["median_us"] == 3.0 and s["min_us"] == 1.0 and s["reps"] == 5
+    assert s["p90_us"] == round(float(np.percentile(t, 90)) * 1e6, 3)
+    assert s["mean_us"] == 4.0
+    assert s["rate_median"] == round(2e6 / 3e-6 / 1e12, 2)
+    # rotations exceed three MALLs where the cap allows
+    assert bench.copies_for(256 << 20) == 3
+    assert bench.copies_for(2 << 20, cap=256) == 256
+    assert bench.copies_for(1 << 30) == 1
+
+
+def test_sweep_expected_files_load_and_check_their_shape(tmp_path):
+    """The committed oracle expected values are read with their shape; a
+    file for another shape, or none, stops the sweep instead of gating on
+    the wrong values."""
+    ij, u, i = sweep.load_expected(sweep.expected_path("gemm", [8192, 8192, 8192]), [8192, 8192, 8192])
+    assert ij.shape[1] == 2 and ij.shape[0] == u.size == i.size >= 3000
+    assert ij.min() >= 0 and ij[:, 0].max() == 8191 and ij[:, 1].max() == 8191
+    n, gu, gi = sweep.load_expected(sweep.expected_path("gemv", [8192, 8192]), [8192, 8192])
+    assert np.array_equal(n[:, 0], np.arange(8192))
+    with pytest.raises(SystemExit):
+        sweep.load_expected(sweep.expected_path("gemm", [8192, 8192, 8192]), [4096, 8192, 8192])
+    with pytest.raises(SystemExit):
+        sweep.load_expected(str(tmp_path / "none.txt"), [1, 1, 1])
+
+
+def test_sweep_expected_values_are_the_oracles():
+    """Spot-check the stored GEMM entries against the oracle recomputed here
+    from the same seeded rows."""
+    import inputs
+    import oracle
+    ij, u, i = sweep.load_expected(sweep.expected_path("gemm", [8192, 8192, 8192]), [8192, 8192, 8192])
+    pick = np.arange(0, ij.shape[0], 97)
+    rows = sorted(set(ij[pick, 0]) | set(ij[pick, 1]))
+    pos = {r: t for t, r in enumerate(rows)}
+    for kind, want in (("uniform", u), ("integer", i)):
+        A = inputs.rows_f16(kind, (8192, 8192), rows, 0, inputs.STREAM_A)
+        B = inputs.rows_f16(kind, (8192, 8192), rows, 0, inputs.STREAM_B)
+        sub = np.array([[pos[a], pos[b]] for a, b in ij[pick]], dtype=np.int64)
+        got, _ = oracle.gemm_nt_entries(A, B, sub)
+        assert np.array_equal(got, want[pick])
+
+
+def test_resource_remarks_parse():
+    from gemv_fp16_amd import build
+    text = """x.hpp:3:1: remark: Function Name: _Z3foov [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     TotalSGPRs: 36 [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     VGPRs: 20 [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     AGPRs: 4 [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     Occupancy [waves/SIMD]: 8 [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     SGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     VGPRs Spill: 2 [-Rpass-analysis=kernel-resource-usage]
+x.hpp:3:1: remark:     LDS Size [bytes/block]: 0 [-Rpass-analysis=kernel-resource-usage]
+y.hpp:9:1: remark: Function Name: _Z3barv [-Rpass-analysis=kernel-resource-usage]
+y.hpp:9:1: remark:     VGPRs: 7 [-Rpass-analysis=kernel-resource-usage]
+"""
+    r = build.parse_resource_remarks(text)
+    assert r["_Z3foov"] == {"sgprs": 36, "vgprs": 20, "agprs": 4, "scratch_bytes": 12,
+                            "occupancy_waves_per_simd": 8, "sgpr_spills": 0, "vgpr_spills": 2,
+                            "static_lds_bytes": 0}
+    assert r["_Z3barv"] == {"vgprs": 7}
+    from gemv_fp16_amd import resources
+    assert resources.spills(r["_Z3foov"]) and not resources.spills({"scratch_bytes": 0, "vgpr_spills": 0})
+    assert not resources.spills(None)
+    cfg = {"block_m": 256, "block_n": 256, "block_k": 64, "stages": 2, "threads": 256, "schedule": 2}
+    assert resources.gemm_kernel_name(cfg) == (
+        "void gf::gemm_nt_kernel<gf::GemmCfg<256, 256, 64, 2, 256, 2, 0, 0>, 0, true>(gf::GemmArgs)")
+    # the epilogue's per-wave transpose (4 waves x 128 x (128 + 8) fp16) outgrows the 2-stage ring
+    assert resources.gemm_lds_bytes(cfg) == max(2 * (256 + 256) * 64 * 2, 4 * 128 * 136 * 2) == 139264
