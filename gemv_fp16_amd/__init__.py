@@ -13,7 +13,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemvfp16.so")
 
-GF_OK, GF_ERR_INVALID_ARG, GF_ERR_HIP, GF_ERR_UNSUPPORTED = 0, 1, 2, 3
+GF_OK, GF_ERR_INVALID_ARG, GF_ERR_HIP, GF_ERR_UNSUPPORTED, GF_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 GF_SPLITK_ATOMIC, GF_SPLITK_TWOPASS, GF_SPLITK_F16 = 0, 1, 2
 
 EXPORTS = (
@@ -21,7 +21,7 @@ EXPORTS = (
     "gemm_f16_nt_splitk_workspace_bytes", "gemm_f16_nt_splitk_ex", "gemm_f16_nt_splitk_f16",
     "gemm_f16_nt_cfg", "gemv_f16_cfg", "gemm_f16", "gemm_f16_nn", "gemm_f16_tn", "gemm_f16_cfg",
     "gemm_f16_nt_skinny", "gf_skinny_config_count", "gf_skinny_config_get", "gf_skinny_default_config",
-    "gemm_f16_nt_splitk_cfg",
+    "gemm_f16_nt_splitk_cfg", "gemm_f16_nt_splitk_noalloc", "gf_noalloc_scratch_bytes",
     "gf_gemm_config_count", "gf_gemm_config_get", "gf_gemv_config_count", "gf_gemv_config_get",
     "gf_gemm_default_config", "gf_gemv_default_config", "gf_status_string",
     "sp24_compress_f16", "gemm_sp_f16_nt", "gemm_sp_f16_nt_cfg", "gf_sp_config_count",
@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_nt_splitk_workspace_bytes.restype = sz
     L.gemm_f16_nt_splitk_ex.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, vp]
     L.gemm_f16_nt_splitk_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, sz, vp]
+    L.gemm_f16_nt_splitk_noalloc.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp]
+    L.gf_noalloc_scratch_bytes.argtypes = []
+    L.gf_noalloc_scratch_bytes.restype = sz
     L.gemm_f16.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
     L.gemm_f16_nt_skinny.argtypes = [vp, vp, vp, ci, ci, ci, ctypes.POINTER(SkinnyCfg), vp]
     L.gemm_f16_nt_splitk_cfg.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp, sz, ctypes.POINTER(GemmCfg), vp]
@@ -96,7 +99,7 @@ def lib() -> ctypes.CDLL:
     L.gf_status_string.argtypes = [ci]
     L.gf_status_string.restype = ctypes.c_char_p
     for name in EXPORTS:
-        if name not in ("gemm_f16_nt_splitk_workspace_bytes", "gf_status_string"):
+        if name not in ("gemm_f16_nt_splitk_workspace_bytes", "gf_noalloc_scratch_bytes", "gf_status_string"):
             getattr(L, name).restype = ci
     _lib = L
     return L
@@ -313,6 +316,20 @@ def gemm_f16_nt_splitk_ex(A, B, C32=None, split_k: int = 4, mode: int = GF_SPLIT
     return C32
 
 
+
+
+def gemm_f16_nt_splitk_noalloc(A, B, C32, split_k: int = 4, stream=None):
+    """Two-pass split-K into the caller's C32 (fp32, M x N) with the slice
+    partials in the library's fixed scratch: neither the library nor this
+    binding allocates anything.  Calls that overlap on one GPU race."""
+    import torch
+    M, N, K = _gemm_shapes(A, B)
+    if tuple(C32.shape) != (M, N):
+        raise ValueError("C32 must be (M, N)")
+    _check(lib().gemm_f16_nt_splitk_noalloc(_dev(A, torch.float16, "A"), _dev(B, torch.float16, "B"),
+                                            _dev(C32, torch.float32, "C32"), M, N, K, split_k,
+                                            _stream(stream)), "gemm_f16_nt_splitk_noalloc")
+    return C32
 
 
 def gemm_f16_nt_splitk_cfg(A, B, C, split_k: int, mode: int, cfg: dict, workspace, stream=None):

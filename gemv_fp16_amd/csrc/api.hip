@@ -310,6 +310,35 @@ int zero_f32(float* p, int64_t n, hipStream_t stream)
     return launch_status(hipGetLastError());
 }
 
+// Scratch for the entry point that allocates nothing: the two-pass slice
+// partials of gemm_f16_nt_splitk_noalloc.  A file-scope device array, so the
+// code object carries it and each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host that name is only a stand-in for the symbol): it takes
+// the device address hipGetSymbolAddress returns, once per device, and uses
+// that.  Every call on one GPU shares the array.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with the device current) and kept.
+int scratch_for_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GF_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GF_ERR_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GF_ERR_HIP;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return GF_OK;
+}
+
 // The slice sums of a two-pass workspace into C32 (fp32) or C16 (fp16).
 int splitk_reduce(const void* ws, void* C, bool out_f16, int64_t mn, int slices, hipStream_t stream)
 {
@@ -748,6 +777,25 @@ int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N
                        default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));
 }
 
+int gemm_f16_nt_splitk_noalloc(const void* A, const void* B, float* C32, int M, int N, int K,
+                               int split_k, void* stream)
+{
+    if (split_k < 1) return GF_ERR_INVALID_ARG;
+    if (M < 0 || N < 0) return GF_ERR_INVALID_ARG;
+    if ((uint64_t)split_k * (uint64_t)M * (uint64_t)N * sizeof(float) > kScratchBytes)
+        return GF_ERR_TOO_LARGE;
+    int rc = validate_gemm(A, B, C32, M, N, K, 4);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return GF_OK;
+    void* ws = nullptr;
+    rc = scratch_for_current_device(&ws);
+    if (rc) return rc;
+    return splitk_impl(A, B, C32, M, N, K, split_k, GF_SPLITK_TWOPASS, ws, kScratchBytes,
+                       default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));
+}
+
+size_t gf_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
 int gemv_f16_cfg(const void* W, const void* x, void* y, int N, int K, const gf_gemv_cfg* cfg,
                  void* stream)
 {
@@ -805,6 +853,8 @@ const char* gf_status_string(int status)
     case GF_ERR_INVALID_ARG: return "GF_ERR_INVALID_ARG: invalid argument";
     case GF_ERR_HIP: return "GF_ERR_HIP: HIP runtime error at launch";
     case GF_ERR_UNSUPPORTED: return "GF_ERR_UNSUPPORTED: no compiled kernel for this config";
+    case GF_ERR_TOO_LARGE:
+        return "GF_ERR_TOO_LARGE: split_k * M * N * 4 bytes exceed the 64 MiB no-allocation scratch";
     default: return "unknown status";
     }
 }

@@ -37,7 +37,8 @@ enum {
     GF_OK = 0,
     GF_ERR_INVALID_ARG = 1,   /* bad size, NULL or misaligned pointer, bad mode */
     GF_ERR_HIP = 2,           /* the HIP runtime reported an error at launch */
-    GF_ERR_UNSUPPORTED = 3    /* no compiled kernel for the requested config */
+    GF_ERR_UNSUPPORTED = 3,   /* no compiled kernel for the requested config */
+    GF_ERR_TOO_LARGE = 4      /* the problem exceeds the library's fixed scratch (no-allocation call) */
 };
 
 enum { GF_SPLITK_ATOMIC = 0, GF_SPLITK_TWOPASS = 1, GF_SPLITK_F16 = 2 };
@@ -126,6 +127,29 @@ size_t gemm_f16_nt_splitk_workspace_bytes(int M, int N, int split_k);
 int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N, int K,
                           int split_k, int mode, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * Two-pass split-K (GF_SPLITK_TWOPASS semantics: fp32 C32 = A . B^T, the
+ * slices summed in ascending order, bitwise reproducible, the same bits as
+ * gemm_f16_nt_splitk_ex in that mode) that allocates nothing and takes no
+ * workspace: for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The slice partials go to a scratch array that the library holds in device
+ * memory, gf_noalloc_scratch_bytes() = 64 MiB on each GPU it runs on, until
+ * the process ends.  The caller still passes A, B and C32.
+ * Limit: split_k * M * N * 4 bytes must fit the scratch (GF_ERR_TOO_LARGE
+ * otherwise, checked on the host before anything is enqueued; 1024 x 1024
+ * fits split_k <= 16).  Every call on one GPU shares that GPU's scratch: two
+ * calls that overlap on one GPU (on different streams or host threads) race
+ * and must be serialised by the caller.  The first call on a device looks up
+ * the scratch's device address (hipGetSymbolAddress; GF_ERR_HIP if that
+ * fails).  Other errors as gemm_f16_nt_splitk_ex.
+ */
+int gemm_f16_nt_splitk_noalloc(const void* A, const void* B, float* C32, int M, int N, int K,
+                               int split_k, void* stream);
+
+/* Bytes of the no-allocation scratch of gemm_f16_nt_splitk_noalloc (64 MiB). */
+size_t gf_noalloc_scratch_bytes(void);
 
 /*
  * Split-K with an fp16 output: C = A . B^T, A M x K fp16, B N x K fp16,

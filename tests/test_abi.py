@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for rc in (0, 1, 2, 3):
+    for rc in (0, 1, 2, 3, 4):
         assert gf.status_string(rc).startswith(("GF_OK", "GF_ERR"))
     assert gf.status_string(99) == "unknown status"
 
@@ -98,6 +98,16 @@ def test_splitk_validation(L):
     assert ex(FAKE, FAKE, FAKE, 4, 0, 4, 2, gf.GF_SPLITK_TWOPASS, NULL, 0, s) == gf.GF_OK
     assert L.gemm_f16_nt_splitk_workspace_bytes(-1, 4, 2) == 0
     assert L.gemm_f16_nt_splitk_workspace_bytes(4, 4, 0) == 0
+    # the entry point that allocates nothing: its scratch limit, checked on the host
+    na = L.gemm_f16_nt_splitk_noalloc
+    assert L.gf_noalloc_scratch_bytes() == 64 << 20
+    assert na(FAKE, FAKE, FAKE, 4096, 4096, 64, 2, s) == gf.GF_ERR_TOO_LARGE       # 128 MiB of partials
+    assert na(FAKE, FAKE, FAKE, 1024, 1024, 64, 17, s) == gf.GF_ERR_TOO_LARGE
+    assert na(FAKE, FAKE, FAKE, 4, 4, 4, 0, s) == gf.GF_ERR_INVALID_ARG
+    assert na(FAKE, FAKE, FAKE, -1, 4, 4, 2, s) == gf.GF_ERR_INVALID_ARG
+    assert na(FAKE, FAKE, ctypes.c_void_p(0x10002), 4, 4, 4, 2, s) == gf.GF_ERR_INVALID_ARG
+    assert na(FAKE, FAKE, FAKE, 0, 4, 4, 2, s) == gf.GF_OK                          # empty C
+    assert "64 MiB" in gf.status_string(gf.GF_ERR_TOO_LARGE)
 
 
 def test_layout_validation(L):
