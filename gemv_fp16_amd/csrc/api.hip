@@ -134,25 +134,34 @@ gf_gemm_cfg tail_gemm_cfg(int M, int N)
 }
 
 // Split-K tile: the largest tile (among the configs compiled with the fp32
-// epilogues) whose tiles x slices still give every CU a workgroup.  The
-// sweep at M = N = 1024, K = 16384 found exactly that: 128 x 128 / 3 stages
-// at split 4, 128 x 256 at split 8, 256 x 256 at split 16, each with
-// 256 workgroups.
-gf_gemm_cfg default_splitk_cfg(int M, int N, int K, int split_k)
+// epilogues) whose tiles x slices still give every CU a workgroup.  Sweeps
+// of every such config at M = N = 1024, K = 16384 with the operands rotated
+// through HBM found exactly that for the two-pass combines: 128 x 128 with
+// 3 stages at split 4 (714-727 TFLOP/s), 256 x 128 with one wave per SIMD
+// at split 8 (711-715, against 562-567 for the 128 x 256 tile it
+// replaces), 256 x 256 at split 16 (609-635), each with 256 workgroups.
+// The atomic combine gathers 16 partial tiles on every output tile at split
+// 16 when those tiles are 256 x 256, and their adds arrive together; there
+// the 64 x 64 tile spreads them over 16 rounds of workgroups (455 against
+// 393 TFLOP/s).  So with atomics, wherever the big tiles would stack 16 or
+// more slices, the 64 x 64 tile is taken.
+gf_gemm_cfg default_splitk_cfg(int M, int N, int K, int split_k, bool atomic = false)
 {
     constexpr int kCus = 256;
     const gf_gemm_cfg cands[] = {
-        make_cfg(256, 256, 64, 2, 512, 1), make_cfg(128, 256, 64, 2, 256, 1),
-        make_cfg(128, 128, 64, 3, 256, 1), make_cfg(64, 64, 64, 2, 256, 1),
+        make_cfg(256, 256, 64, 2, 512, 1), make_cfg(256, 128, 64, 3, 256, 1, 2),
+        make_cfg(128, 128, 64, 3, 256, 1), make_cfg(64, 64, 64, 3, 256, 1),
     };
-    for (const gf_gemm_cfg& c : cands) {
+    constexpr int kLast = sizeof(cands) / sizeof(cands[0]) - 1;
+    for (int i = 0; i <= kLast; ++i) {
+        const gf_gemm_cfg& c = cands[i];
         const int64_t tiles = (int64_t)ceil_div(M, c.block_m) * ceil_div(N, c.block_n);
         const int nkt = ceil_div(K, c.block_k);
         const int per = nkt > 0 ? ceil_div(nkt, max(1, split_k)) : 0;
         const int slices = per > 0 ? ceil_div(nkt, per) : 1;
-        if (tiles * slices >= kCus) return c;
+        if (tiles * slices >= kCus) return atomic && slices >= 16 ? cands[kLast] : c;
     }
-    return cands[3];
+    return cands[kLast];
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GF_OK : GF_ERR_HIP; }
@@ -740,7 +749,7 @@ int gemm_f16_nt_splitk(const void* A, const void* B, float* C32, int M, int N, i
                        void* stream)
 {
     return splitk_impl(A, B, C32, M, N, K, split_k, GF_SPLITK_ATOMIC, nullptr, 0,
-                       default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));
+                       default_splitk_cfg(M, N, K, split_k, true), static_cast<hipStream_t>(stream));
 }
 
 int gemm_f16_nt_splitk_cfg(const void* A, const void* B, void* C, int M, int N, int K, int split_k,
@@ -774,7 +783,8 @@ int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N
                           int mode, void* workspace, size_t workspace_bytes, void* stream)
 {
     return splitk_impl(A, B, C32, M, N, K, split_k, mode, workspace, workspace_bytes,
-                       default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));
+                       default_splitk_cfg(M, N, K, split_k, mode == GF_SPLITK_ATOMIC),
+                       static_cast<hipStream_t>(stream));
 }
 
 int gemm_f16_nt_splitk_noalloc(const void* A, const void* B, float* C32, int M, int N, int K,

@@ -91,17 +91,22 @@ def defaults_table() -> str:
     for lay, label in (((0, 1), "GEMM NN 8192^3"), ((1, 1), "GEMM TN 8192^3")):
         name = gemm_kernel_name(big, layout=lay)
         lines.append(_row(label, name, rep.get(name), gemm_lds_bytes(big)))
+    cands = ({"block_m": 256, "block_n": 256, "block_k": 64, "stages": 2, "threads": 512, "schedule": 0},
+             {"block_m": 256, "block_n": 128, "block_k": 64, "stages": 3, "threads": 256, "schedule": 2},
+             {"block_m": 128, "block_n": 128, "block_k": 64, "stages": 3, "threads": 256, "schedule": 0},
+             {"block_m": 64, "block_n": 64, "block_k": 64, "stages": 3, "threads": 256, "schedule": 0})
     for split in (4, 8, 16):
-        # the split-K default tile: the first candidate whose tiles x slices fill the CUs
-        for c in ({"block_m": 256, "block_n": 256, "block_k": 64, "stages": 2, "threads": 512, "schedule": 0},
-                  {"block_m": 128, "block_n": 256, "block_k": 64, "stages": 2, "threads": 256, "schedule": 0},
-                  {"block_m": 128, "block_n": 128, "block_k": 64, "stages": 3, "threads": 256, "schedule": 0}):
+        # the split-K default tile (the library's rule): the first candidate
+        # whose tiles x slices fill the CUs; the 64 x 64 tile for atomics at
+        # 16 slices
+        for c in cands:
             if (1024 // c["block_m"]) * (1024 // c["block_n"]) * split >= 256:
                 break
         for epi, what in ((2, "two-pass store"), (1, "atomic")):
-            name = gemm_kernel_name(c, epi=epi)
+            cc = cands[-1] if epi == 1 and split >= 16 else c
+            name = gemm_kernel_name(cc, epi=epi)
             lines.append(_row("split-K 1024^2x16384 s=%d %s" % (split, what), name, rep.get(name),
-                              gemm_lds_bytes(c)))
+                              gemm_lds_bytes(cc)))
     for n, k in ((8192, 8192), (1024, 1024)):
         g = gf.gemv_default_config(n, k)
         if g["blocks"] > 0 and k % (8 * g["waves"] * 64 * g["unroll"]) == 0:
