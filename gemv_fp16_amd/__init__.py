@@ -11,7 +11,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgemvfp16.so")
+# GEMVFP16_LIB names another build of the same library (the diagnostic
+# variants of build.py); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("GEMVFP16_LIB") or os.path.join(_HERE, "libgemvfp16.so")
 
 GF_OK, GF_ERR_INVALID_ARG, GF_ERR_HIP, GF_ERR_UNSUPPORTED, GF_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 GF_SPLITK_ATOMIC, GF_SPLITK_TWOPASS, GF_SPLITK_F16 = 0, 1, 2

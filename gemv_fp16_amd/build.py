@@ -82,6 +82,30 @@ def _demangle(names):
     return list(names)
 
 
+# Diagnostic variants: the same library built with one feature switched off,
+# into gemv_fp16_amd/variants/<variant>/libgemvfp16.so (load it with
+# GEMVFP16_LIB=<path>).  Only for counter comparisons; the product is the
+# default build.
+VARIANTS = {"noswizzle": ["-DGF_DIAG_NO_LDS_SWIZZLE"], "timeline": ["-DGF_DIAG_TIMELINE"]}
+
+
+def build_variant(name: str, jobs: int | None = None) -> str:
+    out_dir = os.path.join(OBJ, name)
+    os.makedirs(out_dir, exist_ok=True)
+    units = [(src, os.path.join(name, obj), extra + VARIANTS[name]) for src, obj, extra in _units()]
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = [o for o, _ in ex.map(_compile, units)]
+    lib_dir = os.path.join(PKG, "variants", name)
+    os.makedirs(lib_dir, exist_ok=True)
+    lib = os.path.join(lib_dir, "libgemvfp16.so")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    return lib
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library.  Always rebuilds."""
     os.makedirs(OBJ, exist_ok=True)
@@ -119,5 +143,8 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) == 3 and sys.argv[1] == "--variant" and sys.argv[2] in VARIANTS:
+        print("built", build_variant(sys.argv[2]))
+    else:
+        build(verbose=True)
     sys.exit(0)

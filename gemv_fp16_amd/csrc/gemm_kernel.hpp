@@ -115,9 +115,28 @@ struct OperandGeom {
     static constexpr int CR = ROWS / 8;                        // layout 1: chunks per k-row
 };
 
+// Diagnostic build only (build.py --variant timeline): each workgroup of a
+// two-pass split-K launch notes the shader's real-time counter (100 MHz) on
+// entry, once its first K tile has landed, when its main loop ends and after
+// its partial stores, and writes them with its XCC id over the first words of
+// its own partial tile -- the results are then wrong by design.  Compiled out
+// of the library.
+#ifdef GF_DIAG_TIMELINE
+#define GF_STAMP(t) ((t) = __builtin_amdgcn_s_memrealtime())
+#else
+#define GF_STAMP(t) ((void)0)
+#endif
+
 __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
 {
+#ifdef GF_DIAG_NO_LDS_SWIZZLE
+    // Diagnostic build only (build.py --variant noswizzle): the unswizzled
+    // layout, kept so that its bank conflicts can be counted.
+    (void)row; (void)rows_per_key; (void)ch;
+    return 0;
+#else
     return (row / rows_per_key) % ch;
+#endif
 }
 
 // Where the 16-byte LDS slot s of an operand tile (0 <= s < rows * BK / 8)
@@ -625,6 +644,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
     typedef typename MF::acc_t acc_t;
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     GF_LDS char* smem = (GF_LDS char*)smem_raw;
+    [[maybe_unused]] uint64_t ts0 = 0, ts1 = 0, ts2 = 0;
+    GF_STAMP(ts0);
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -781,6 +802,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         }
         wait_vmcnt<Cfg::LPS * (S - 2)>();       // tile 0 landed
         lds_barrier();
+        GF_STAMP(ts1);
         if (nk > 0) ld.template issue_range<0, H>(a, stage_ptr(S - 1), k0_of(S - 1), wave);
         fr.template load_all<0>(stage_ptr(0), af[0], bf[0]);
         // Steady state: tiles t + S - 1 and t + S lie wholly inside K, so
@@ -861,6 +883,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
     }
 
     // ---- epilogue ----
+    GF_STAMP(ts2);
     const int wrow0 = m0 + wm * Cfg::WTM, wcol0 = n0 + wn * Cfg::WTN;
     constexpr int MT = Cfg::MT;
 
@@ -930,6 +953,16 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
                     if (grow < a.M && gcol < a.N)
                         W[(size_t)grow * a.N + gcol] = acc[fm][fn][i];
                 }
+#ifdef GF_DIAG_TIMELINE
+        __builtin_amdgcn_s_waitcnt(0);
+        uint64_t ts3;
+        GF_STAMP(ts3);
+        if (tid == 0 && n0 + 10 <= a.N) {   // five 8-byte words inside the tile's first row
+            uint64_t* t = (uint64_t*)(W + (size_t)m0 * a.N + n0);
+            t[0] = ts0; t[1] = ts1; t[2] = ts2; t[3] = ts3;
+            t[4] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+        }
+#endif
     }
 #endif
 }

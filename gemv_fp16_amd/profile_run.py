@@ -7,7 +7,8 @@ Ops (inputs are the seeded uniform[-1,1] fp16 workloads):
   gemm    C = A . B^T at M = N = K = 8192 (default tile config); --layout nn / tn
           stores B as K x N (and A as K x M) and runs gemm_f16 on them
   gemv    y = W . x at N = K = 8192, rotating 5 W copies (640 MiB)
-  splitk  M = N = 1024, K = 16384, split 8: fp32 atomic, fp32 two-pass, fp16 two-pass
+  splitk  M = N = 1024, K = 16384, split --split (default 8): fp32 atomic, fp32 two-pass, fp16
+          two-pass, operands rotated over 4 copies (256 MiB)
   skinny  C = A . B^T with M = 4 and M = 16 rows of A against an 8192 x 8192 B (5 B copies
           rotated, 640 MiB); the library's default form for each M
   sparse  2:4 sparse C = decompress(A_sparse, E) . B^T at M = N = K = 8192 (A compressed
@@ -35,6 +36,7 @@ def main(argv=None):
     ap.add_argument("--n", type=int, default=8192)
     ap.add_argument("--k", type=int, default=8192)
     ap.add_argument("--layout", choices=["nt", "nn", "tn"], default="nt")
+    ap.add_argument("--split", type=int, default=8, help="split-K slices (op splitk)")
     ap.add_argument("--cfg", default="",
                     help="gemm tile config block_m,block_n,block_k,stages,threads,raster[,schedule] "
                          "(default: the library's choice)")
@@ -75,13 +77,15 @@ def main(argv=None):
     elif a.op == "splitk":
         A = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, 0)).cuda()
         B = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, 1)).cuda()
+        As, Bs = [A] + [A.clone() for _ in range(3)], [B] + [B.clone() for _ in range(3)]
         C = torch.empty((1024, 1024), dtype=torch.float32, device="cuda")
         C16 = torch.empty((1024, 1024), dtype=torch.float16, device="cuda")
-        ws = torch.empty(8 * 1024 * 1024, dtype=torch.float32, device="cuda")
-        for _ in range(a.iters):
-            gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_ATOMIC, ws)
-            gf.gemm_f16_nt_splitk_ex(A, B, C, 8, gf.GF_SPLITK_TWOPASS, ws)
-            gf.gemm_f16_nt_splitk_f16(A, B, C16, 8, ws)
+        ws = torch.empty(a.split * 1024 * 1024, dtype=torch.float32, device="cuda")
+        for i in range(a.iters):
+            j = i % 4
+            gf.gemm_f16_nt_splitk_ex(As[j], Bs[j], C, a.split, gf.GF_SPLITK_ATOMIC, ws)
+            gf.gemm_f16_nt_splitk_ex(As[j], Bs[j], C, a.split, gf.GF_SPLITK_TWOPASS, ws)
+            gf.gemm_f16_nt_splitk_f16(As[j], Bs[j], C16, a.split, ws)
     elif a.op == "skinny":
         Bs = [torch.from_numpy(inputs.uniform_f16((a.n, a.k), i, 1)).cuda() for i in range(5)]
         for m in (4, 16):

@@ -1,0 +1,96 @@
+"""Per-workgroup timeline of the split-K GEMM pass (diagnostic build).
+
+    python -m gemv_fp16_amd.build --variant timeline     # once, on any machine
+    python -m gemv_fp16_amd.timeline [--split 8 --cfg 256,128,64,3,256,2]
+
+Loads gemv_fp16_amd/variants/timeline/libgemvfp16.so, in which every
+workgroup of a two-pass split-K launch stamps the shader's 100 MHz real-time
+counter at four points and writes the stamps over the first words of its own
+partial tile (so that build's results are wrong by design; it is never the
+library).  The run is M = N = 1024, K = 16384 on the seeded uniform[-1,1]
+operands, rotated over 4 copies (256 MiB, past the 256 MiB MALL together with
+the workspace), 12 launches; the stamps of the last launch are read back.
+
+Per launch it prints, over the workgroups: the span from the first entry to
+the last partial store, the skew of the entries (a second wave of workgroups
+starts when the first one leaves), the prologue (entry until the first K tile
+has landed: only the schedule-2 pipeline notes that point), the main loop,
+the epilogue (partial stores until they have left the CU), and the main
+loop's matrix-core share at a stated clock: its MFMA cycles (32 per 32 x 32
+MFMA, per SIMD) over the loop's duration.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(_HERE)
+VARIANT = os.path.join(_HERE, "variants", "timeline", "libgemvfp16.so")
+
+CONFIGS = ((8, (256, 128, 64, 3, 256, 2)), (4, (256, 128, 64, 3, 256, 2)), (16, (256, 128, 64, 3, 256, 2)),
+           (4, (128, 128, 64, 4, 256, 2)), (8, (128, 128, 64, 4, 256, 2)))
+
+
+def run(split, cfg, As, Bs, C32, clock_ghz):
+    import numpy as np
+    import torch
+    import gemv_fp16_amd as gf
+    M, N, K = 1024, 1024, 16384
+    keys = ("block_m", "block_n", "block_k", "stages", "threads", "schedule")
+    c = dict(zip(keys, cfg), raster=1)
+    ws = torch.zeros(split * M * N, dtype=torch.float32, device="cuda")
+    for i in range(12):
+        gf.gemm_f16_nt_splitk_cfg(As[i % 4], Bs[i % 4], C32, split, gf.GF_SPLITK_TWOPASS, c, ws)
+    torch.cuda.synchronize()
+    w = ws.view(split, M, N).cpu().numpy()
+    bm, bn, bk = cfg[0], cfg[1], cfg[2]
+    rec = np.array([w[s, tm * bm, tn * bn:tn * bn + 10].view(np.uint64).astype(np.int64)
+                    for s in range(split) for tm in range(M // bm) for tn in range(N // bn)])
+    t0 = rec[:, 0].min()
+    start, first, mend, end = ((rec[:, j] - t0) / 100.0 for j in range(4))   # microseconds
+    xcc = rec[:, 4]
+    loop = mend - first if rec[:, 1].min() > 0 else mend - start
+    ksteps = K // split // bk
+    waves = cfg[4] // 64
+    mfma_cycles = (bm * bn * bk) // (32 * 32 * 16) // waves * 32 * ksteps   # per SIMD (one wave each)
+    busy = mfma_cycles / (np.median(loop) * 1e-6 * clock_ghz * 1e9)
+    row = "| %d | %s | %d | %.1f | %.1f | %s | %.1f (%.1f-%.1f) | %.2f | %.0f %% | %s |" % (
+        split, "x".join(map(str, cfg[:3])) + " S%d sched %d" % (cfg[3], cfg[5]), len(rec), end.max(), start.max(),
+        "%.2f" % np.median(first - start) if rec[:, 1].min() > 0 else "-", np.median(loop), loop.min(), loop.max(),
+        np.median(end - mend), 100 * busy, " ".join("%d:%.1f" % (x, end[xcc == x].max()) for x in range(8)
+                                                    if (xcc == x).any()))
+    return row
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--split", type=int, default=0, help="one run at this split (with --cfg)")
+    ap.add_argument("--cfg", default="", help="block_m,block_n,block_k,stages,threads,schedule")
+    ap.add_argument("--clock-ghz", type=float, default=2.2,
+                    help="shader clock used for the matrix-core share (the split-K pass runs near 2.2 GHz)")
+    a = ap.parse_args(argv)
+    if not os.path.exists(VARIANT):
+        raise SystemExit("build the diagnostic library first: python -m gemv_fp16_amd.build --variant timeline")
+    os.environ["GEMVFP16_LIB"] = VARIANT
+    sys.path.insert(0, ROOT)
+    import torch
+    import gemv_fp16_amd as gf
+    import inputs
+    assert gf.LIB_PATH == VARIANT
+    A0 = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, inputs.STREAM_A)).cuda()
+    B0 = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, inputs.STREAM_B)).cuda()
+    As = [A0] + [A0.clone() for _ in range(3)]
+    Bs = [B0] + [B0.clone() for _ in range(3)]
+    C32 = torch.empty((1024, 1024), dtype=torch.float32, device="cuda")
+    runs = ((a.split, tuple(int(t) for t in a.cfg.split(","))),) if a.split else CONFIGS
+    print("| split | tile | WGs | span us | entry skew us | prologue us | main loop us median (min-max) "
+          "| epilogue us | MFMA share of loop at %.1f GHz | last store per XCC, us |" % a.clock_ghz)
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for split, cfg in runs:
+        print(run(split, cfg, As, Bs, C32, a.clock_ghz), flush=True)
+
+
+if __name__ == "__main__":
+    main()
