@@ -174,13 +174,15 @@ struct DmaLoader {
     uint32_t voff[Cfg::LPS];   // byte offset of load r's chunk at k = 0 (rows / columns clamped)
     int tid;
     uint32_t ska, skb;         // bytes per k step in A and in B
+    int klim;                  // K index where this workgroup's loads stop: K, or its split-K slice's end
     // Buffer descriptors of A and B (raw, byte-addressed): the tile's K
     // offset travels in the scalar offset, the row/chunk offset in voff.
     __amdgpu_buffer_rsrc_t ra, rb;
 
-    __device__ __forceinline__ void init(const GemmArgs& a, int m0, int n0, int tid_)
+    __device__ __forceinline__ void init(const GemmArgs& a, int m0, int n0, int tid_, int klim_)
     {
         tid = tid_;
+        klim = klim_;
         ska = Cfg::LA ? (uint32_t)a.M * 2u : 2u;
         skb = Cfg::LB ? (uint32_t)a.N * 2u : 2u;
 #pragma unroll
@@ -208,7 +210,7 @@ struct DmaLoader {
                                                kRawBufferWord3);
     }
 
-    // Whether load r of the K tile at k0 lies inside K (its chunk for
+    // Whether load r of the K tile at k0 lies before klim (its chunk for
     // layout 0, its k-row for layout 1).
     __device__ __forceinline__ bool in_k(const GemmArgs& a, int k0, int r) const
     {
@@ -218,7 +220,8 @@ struct DmaLoader {
         int kk, rr;
         if (is_a) slot_source<Cfg, Cfg::LA, Cfg::BM>(s, kk, rr);
         else slot_source<Cfg, Cfg::LB, Cfg::BN>(s, kk, rr);
-        return k0 + kk < a.K;
+        (void)a;
+        return k0 + kk < klim;
     }
 
     // Kernels with a K-major operand read it with transposing LDS reads,
@@ -250,7 +253,8 @@ struct DmaLoader {
         }
     }
 
-    // The same where the tile may run past K: chunks at k >= K read 16 zero bytes.
+    // The same where the tile may run past klim: chunks at k >= klim read 16
+    // zero bytes.
     __device__ __forceinline__ void issue_masked(const GemmArgs& a, GF_LDS char* stage, int k0, int r,
                                                  int wave) const
     {
@@ -275,14 +279,15 @@ struct DmaLoader {
         for (int r = 0; r < Cfg::LPS; ++r) issue(a, stage, k0, r, wave);
     }
 
-    // Loads R0 .. R1-1 of the K tile at k0; where the tile runs past K,
-    // chunks at k >= K read 16 zero bytes (so do all chunks of a tile that
-    // lies wholly beyond K).
+    // Loads R0 .. R1-1 of the K tile at k0; where the tile runs past klim,
+    // chunks at k >= klim read 16 zero bytes (so do all chunks of a tile
+    // that lies wholly beyond it: a split-K slice's pipeline tail then reads
+    // no operand bytes of the next slice).
     template <int R0, int R1>
     __device__ __forceinline__ void issue_range(const GemmArgs& a, GF_LDS char* stage, int k0,
                                                 int wave) const
     {
-        if (k0 + Cfg::BK <= a.K) {
+        if (k0 + Cfg::BK <= klim) {
             static_for<R1 - R0>([&](auto j) { issue(a, stage, k0, R0 + decltype(j)::value, wave); });
         } else {
             static_for<R1 - R0>([&](auto j) { issue_masked(a, stage, k0, R0 + decltype(j)::value, wave); });
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
     auto stage_ptr = [&](int s) { return smem + s * Cfg::STAGE_BYTES; };
     auto k0_of = [&](int kt) { return (kt_begin + kt) * Cfg::BK; };
     DmaLoader<Cfg> ld;
-    if constexpr (ALIGNED) ld.init(a, m0, n0, tid);
+    if constexpr (ALIGNED) ld.init(a, m0, n0, tid, min(a.K, kt_end * Cfg::BK));
     Frags<Cfg> fr;
     fr.init(wm, wn, lane);
     // Whole-tile load, used where nothing can overlap it (pipeline prologue,

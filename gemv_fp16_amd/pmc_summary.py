@@ -2,6 +2,12 @@
 
     python -m gemv_fp16_amd.pmc_summary table CSV [CSV ...]
         per kernel: dispatches and the mean value per dispatch of every counter
+    python -m gemv_fp16_amd.pmc_summary trace KERNEL_TRACE_CSV [--kernel SUBSTRING]
+        [--first N] [--skip N]
+        durations of the kernels of a rocprofv3 --kernel-trace run: per kernel
+        calls, mean / median / min / max in microseconds; with --kernel, the
+        launches of the matching kernel(s) in dispatch order, optionally only
+        launches skip .. skip + first - 1 of them, and each launch's duration
     python -m gemv_fp16_amd.pmc_summary traffic --fetch CSV --write CSV \
         --calib-fetch CSV --calib-write CSV --kernel SUBSTRING --key NAME \
         --algorithmic BYTES --command TEXT
@@ -50,6 +56,29 @@ def table(paths):
     return "\n".join(lines)
 
 
+def trace(a):
+    import statistics
+    with open(a.csv) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    dur = defaultdict(list)
+    for r in rows:
+        if a.kernel is None or a.kernel in r["Kernel_Name"]:
+            dur[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = ["| kernel | calls | mean us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        if a.kernel is not None:
+            v = v[a.skip:a.skip + a.first] if a.first else v[a.skip:]
+        if not v:
+            continue
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.2f |" % (
+            k[:110], len(v), sum(v) / len(v), statistics.median(v), min(v), max(v)))
+        if a.kernel is not None:
+            lines.append("")
+            lines.append("launch durations (us, dispatch order): " + ", ".join("%.1f" % x for x in v))
+            lines.append("")
+    return "\n".join(lines)
+
+
 def traffic(a):
     sys.path.insert(0, ROOT)
     import bench
@@ -77,6 +106,11 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("table")
     t.add_argument("csv", nargs="+")
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    tr.add_argument("--kernel", default=None)
+    tr.add_argument("--first", type=int, default=0)
+    tr.add_argument("--skip", type=int, default=0)
     r = sub.add_parser("traffic")
     for n in ("fetch", "write", "calib_fetch", "calib_write", "kernel", "key", "command"):
         r.add_argument("--" + n.replace("_", "-"), required=True)
@@ -84,6 +118,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "table":
         print(table(a.csv))
+    elif a.cmd == "trace":
+        print(trace(a))
     else:
         traffic(a)
 

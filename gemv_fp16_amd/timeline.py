@@ -73,12 +73,14 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if not os.path.exists(VARIANT):
         raise SystemExit("build the diagnostic library first: python -m gemv_fp16_amd.build --variant timeline")
-    os.environ["GEMVFP16_LIB"] = VARIANT
     sys.path.insert(0, ROOT)
     import torch
     import gemv_fp16_amd as gf
     import inputs
-    assert gf.LIB_PATH == VARIANT
+    # run as "python -m gemv_fp16_amd.timeline" the package is imported
+    # already; the library itself loads on first use
+    assert gf._lib is None
+    gf.LIB_PATH = VARIANT
     A0 = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, inputs.STREAM_A)).cuda()
     B0 = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, inputs.STREAM_B)).cuda()
     As = [A0] + [A0.clone() for _ in range(3)]
