@@ -557,11 +557,14 @@ int find_gemv(const gf_gemv_cfg& c)
 // calls, W rotated over more than the MALL) at N x K = 8192^2, 16384 x 8192,
 // 8192 x 16384, 4096 x 8192, 16384 x 4096, 14336 x 4096, 28672 x 4096,
 // 8192 x 4096, 4096^2, 4096 x 14336, 12288 x 6144 and 2048 x 8192:
-//  * the split form (a workgroup's 8 waves split K, one workgroup per CU,
-//    the grid streaming one band of W) where K is a multiple of 8192 and W
-//    has at least 4096 rows: two rows per task up to K = 8192 (8192^2:
-//    21.0 us = 6.39 TB/s, 4096 x 8192: 11.7 us), one row beyond (8192 x
-//    16384: 38.9 us = 6.91 TB/s, where two rows per task take 44.9);
+//  * the split form (a workgroup's waves split K, the grid streaming one
+//    band of W) where K is a multiple of 8192 and W has at least 4096 rows:
+//    at K = 8192 one row per task, 4 waves with 4 chunks in flight per
+//    lane, 512 workgroups (two per CU): 8192^2 20.8 us = 6.45 TB/s,
+//    4096 x 8192 11.6 us, 16384 x 8192 39.6 us, 1.3-2 % ahead of two rows
+//    per task on 8 waves and 256 workgroups at all three; beyond K = 8192
+//    one row per task on 8 waves with 2 chunks, 256 workgroups (8192 x
+//    16384: 39.1 us = 6.87 TB/s, first of the sweep);
 //  * else one row per wave: 8 chunks per lane in flight and 2-wave
 //    workgroups when each row splits into whole 512-chunk steps (K % 4096
 //    == 0; 1-2 % ahead of 4 chunks at every such shape), else 4 chunks and
@@ -576,7 +579,8 @@ gf_gemv_cfg default_gemv_cfg(int N, int K)
     c.rows_per_wave = 1;
     if (nk >= (int64_t)4096 * 4096) {
         if (N >= 4096 && K % 8192 == 0 && K <= kGemvXldsMaxK) {
-            c.rows_per_wave = K <= 8192 ? 2 : 1; c.unroll = 2; c.waves = 8; c.blocks = 256;
+            if (K == 8192) { c.unroll = 4; c.waves = 4; c.blocks = 512; }
+            else { c.unroll = 2; c.waves = 8; c.blocks = 256; }
         } else if (K % 4096 == 0) {
             c.unroll = 8; c.waves = 2;
         } else {

@@ -3,6 +3,8 @@
     python -m gemv_fp16_amd.sweep gemm --m 8192 --n 8192 --k 8192 --out sweep.json
     python -m gemv_fp16_amd.sweep gemv --n 8192 --k 8192 --out sweep_gemv.json
     python -m gemv_fp16_amd.sweep sparse --m 8192 --n 8192 --k 8192 --out sweep_sparse.json
+    python -m gemv_fp16_amd.sweep gemv --n 8192 --k 8192 --out sweep_gemv.json --table 25
+        (no GPU: a markdown table of the best 25 records of that shape in the file)
 
 A plain host loop in the spirit of the autotune grid on the TileLang FP16
 matmul benchmark page (section 2.1: block_M, block_N, block_K, pipeline
@@ -266,6 +268,47 @@ def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,), expected=None):
         _emit(out, rec)
 
 
+def table(op, shape, path, top):
+    """Markdown ranking of the timed records of one (op, shape) in a sweep file."""
+    recs, other = [], {}
+    for line in open(path):
+        try:
+            r = json.loads(line)
+        except ValueError:
+            continue
+        if r.get("op") != op or r.get("shape") != shape:
+            continue
+        if r.get("status") == "ok":
+            recs.append(r)
+        else:
+            other[r.get("status")] = other.get(r.get("status"), 0) + 1
+    t = "median_us" if op == "gemv" else "median_ms"
+    recs.sort(key=lambda r: r[t])
+    lines = ["%d timed; %s" % (len(recs), ", ".join("%d %s" % (n, k) for k, n in sorted(other.items())) or
+                                 "none untimed"), ""]
+    if op == "gemv":
+        nb = 2.0 * shape[0] * shape[1] + 2.0 * shape[1] + 2.0 * shape[0]
+        lines += ["| rank | rows/wave | unroll | waves | blocks | median us | min us | GB/s | % of 8000 |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for i, r in enumerate(recs[:top]):
+            c = r["config"]
+            lines.append("| %d | %d | %d | %d | %d | %.3f | %.3f | %.1f | %.1f%s |" % (
+                i + 1, c["rows_per_wave"], c["unroll"], c["waves"], c["blocks"], r["median_us"], r["min_us"],
+                nb / r["median_us"] / 1e3, nb / r["median_us"] / 8e4, " (default)" if r.get("is_default") else ""))
+        d = [i for i, r in enumerate(recs) if r.get("is_default")]
+    else:
+        key = "tflops" if op == "gemm" else "tflops_effective"
+        lines += ["| rank | config | median ms | min ms | TFLOP/s |", "|---|---|---|---|---|"]
+        for i, r in enumerate(recs[:top]):
+            lines.append("| %d | `%s` | %.4f | %.4f | %.1f%s |" % (
+                i + 1, json.dumps(r["config"], sort_keys=True), r["median_ms"], r["min_ms"], r[key],
+                " (default)" if r.get("is_default") else ""))
+        d = [i for i, r in enumerate(recs) if r.get("is_default")]
+    if d:
+        lines += ["", "Default: rank %d of %d." % (d[0] + 1, len(recs))]
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("op", choices=["gemm", "gemv", "sparse"])
@@ -281,7 +324,13 @@ def main(argv=None):
     ap.add_argument("--blocks", type=int, nargs="*", default=[0], help="gemv grid bounds (0 = none)")
     ap.add_argument("--expected", default="",
                     help="oracle expected-values file (default: tests/golden/sweep_expected_<op>_<shape>.txt)")
+    ap.add_argument("--table", type=int, default=0,
+                    help="print the best N records of this shape in --out as markdown, and run nothing")
     a = ap.parse_args(argv)
+    if a.table:
+        shape = [a.n, a.k] if a.op == "gemv" else [a.m, a.n, a.k]
+        print(table(a.op, shape, a.out, a.table))
+        return
     t = time.time()
     if a.op == "gemm":
         sweep_gemm(a.m, a.n, a.k, a.reps, a.warmup, a.trials, a.out, tuple(a.raster), a.only, a.expected)

@@ -1,6 +1,6 @@
 """Write the oracle's expected entries that gate the offline tile sweep.
 
-    python tests/golden/make_sweep_expected.py [--m 8192 --n 8192 --k 8192]
+    python tests/golden/make_sweep_expected.py [--m 8192 --n 8192 --k 8192] [--gemv-only]
 
 For one workload shape it draws the sweep's seeded inputs (inputs/: uniform
 [-1, 1] and integer {-2..2}, seed 0, streams A and B; 2:4-pruned A for the
@@ -60,8 +60,12 @@ def main(argv=None):
     ap.add_argument("--m", type=int, default=8192)
     ap.add_argument("--n", type=int, default=8192)
     ap.add_argument("--k", type=int, default=8192)
+    ap.add_argument("--gemv-only", action="store_true", help="only the GEMV file, at N x K")
     a = ap.parse_args(argv)
     M, N, K = a.m, a.n, a.k
+    if a.gemv_only:
+        write_gemv(N, K)
+        return
     ij = entries(M, N)
     Au = inputs.uniform_f16((M, K), 0, inputs.STREAM_A)
     Bu = inputs.uniform_f16((N, K), 0, inputs.STREAM_B)
@@ -86,6 +90,10 @@ def main(argv=None):
                "benchmark page, section 6): uniform A pruned by the 2:4 compression, integer A drawn 2:4"]
               + common + ["columns: i j fp16-bits(uniform inputs) fp16-bits(integer inputs)"],
               np.column_stack([ij, su, si]))
+    write_gemv(N, K)
+
+
+def write_gemv(N, K):
     # GEMV y = W . x with W = the N x K B-shaped draw of stream 0 and x of stream 1
     Wu = inputs.uniform_f16((N, K), 0, inputs.STREAM_A)
     xu = inputs.uniform_f16((K,), 0, inputs.STREAM_B)

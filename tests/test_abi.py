@@ -253,7 +253,7 @@ def test_config_tables(L):
     dg = gf.gemv_default_config(8192, 8192)
     assert {**dg, "blocks": 0} in gf.gemv_configs() and dg["blocks"] >= 0
     assert dg["blocks"] > 0                                # tall W, K % 8192 == 0: the split form
-    assert dg == {"rows_per_wave": 2, "unroll": 2, "waves": 8, "blocks": 256}
+    assert dg == {"rows_per_wave": 1, "unroll": 4, "waves": 4, "blocks": 512}
     dw = gf.gemv_default_config(4096, 16384)               # long rows: one row per split task
     assert dw == {"rows_per_wave": 1, "unroll": 2, "waves": 8, "blocks": 256}
     # K not a multiple of 8192: one row per wave, 8 chunks in flight when
