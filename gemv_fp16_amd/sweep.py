@@ -270,7 +270,7 @@ def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,), expected=None):
 
 def table(op, shape, path, top):
     """Markdown ranking of the timed records of one (op, shape) in a sweep file."""
-    recs, other = [], {}
+    recs, other, spilled = [], {}, []
     for line in open(path):
         try:
             r = json.loads(line)
@@ -282,6 +282,8 @@ def table(op, shape, path, top):
             recs.append(r)
         else:
             other[r.get("status")] = other.get(r.get("status"), 0) + 1
+            if r.get("status") == "spills":
+                spilled.append(r)
     t = "median_us" if op == "gemv" else "median_ms"
     recs.sort(key=lambda r: r[t])
     lines = ["%d timed; %s" % (len(recs), ", ".join("%d %s" % (n, k) for k, n in sorted(other.items())) or
@@ -306,6 +308,10 @@ def table(op, shape, path, top):
         d = [i for i, r in enumerate(recs) if r.get("is_default")]
     if d:
         lines += ["", "Default: rank %d of %d." % (d[0] + 1, len(recs))]
+    if spilled:
+        lines += ["", "Not timed because the compiled kernel spills registers (scratch bytes per lane, VGPRs spilled):", ""]
+        lines += ["- `%s`: %d B, %d" % (json.dumps(r["config"], sort_keys=True), r.get("scratch_bytes", 0),
+                                       r.get("vgpr_spills", 0)) for r in spilled]
     return "\n".join(lines)
 
 
