@@ -64,10 +64,16 @@ int find_sp(const gf_sp_cfg& c)
     return -1;
 }
 
-// The largest tile that still gives every CU a workgroup.  At 256 x 128 the
-// paired form (stages = 0) is the faster one; at 256 x 256 it trails three
-// stages by about 3 %, and with fewer tiles than CUs (the 128 x 128 case
-// here) its shallower B pipeline loses.
+// The largest tile that still gives every CU a workgroup: 256 x 256 with
+// three stages; where only half-size tiles fill the CUs, 128 x 256 with
+// three stages; else 128 x 128 with three stages.  The half-size case was
+// timed side by side with B rotated through HBM, alternating batch by batch,
+// at 2048 x 4096, 4096 x 2048, 3072 x 4096, 4096 x 3072, 1536 x 8192,
+// 1024 x 8192 and 8192 x 1024 (K = 8192; 2048 x 4096 also at K = 4096 and
+// 16384): 128 x 256 with three stages ran 7-36 % ahead of the paired form
+// of 256 x 128, and ahead of or within 2 % of the other half-size tiles.
+// Cache-warm sweeps had ranked the paired form first; with B streaming from
+// HBM its single-line A loads no longer pay for its two-deep B pipeline.
 gf_sp_cfg default_sp_cfg(int M, int N)
 {
     gf_sp_cfg c;
@@ -75,7 +81,7 @@ gf_sp_cfg default_sp_cfg(int M, int N)
     const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
     const int64_t t25612 = (int64_t)ceil_div(M, 256) * ceil_div(N, 128);
     if (t256 >= 256) { c.block_m = 256; c.block_n = 256; c.stages = 3; }
-    else if (t25612 >= 256) { c.block_m = 256; c.block_n = 128; c.stages = 0; }
+    else if (t25612 >= 256) { c.block_m = 128; c.block_n = 256; c.stages = 3; }
     else { c.block_m = 128; c.block_n = 128; c.stages = 3; }
     return c;
 }

@@ -5,6 +5,9 @@
     python -m gemv_fp16_amd.sweep sparse --m 8192 --n 8192 --k 8192 --out sweep_sparse.json
     python -m gemv_fp16_amd.sweep gemv --n 8192 --k 8192 --out sweep_gemv.json --table 25
         (no GPU: a markdown table of the best 25 records of that shape in the file)
+    python -m gemv_fp16_amd.sweep sparse --m 2048 --n 4096 --k 8192 --compare "default;128,256,3,1;256,128,0,1"
+        (side by side: the listed configs timed in alternating rounds, operands
+        rotated over copies that exceed the MALL; see compare())
 
 A plain host loop in the spirit of the autotune grid on the TileLang FP16
 matmul benchmark page (section 2.1: block_M, block_N, block_K, pipeline
@@ -268,6 +271,96 @@ def sweep_gemv(N, K, reps, warmup, trials, out, blocks=(0,), expected=None):
         _emit(out, rec)
 
 
+def _cfg_from(op, text, default):
+    """'default' or comma-separated values -> config dict.
+    gemm: bm,bn,bk,stages,threads,schedule,raster; sparse: bm,bn,stages,raster;
+    gemv: rows_per_wave,unroll,waves,blocks."""
+    if text.strip() == "default":
+        return dict(default)
+    v = [int(t) for t in text.split(",")]
+    keys = {"gemm": ("block_m", "block_n", "block_k", "stages", "threads", "schedule", "raster"),
+            "sparse": ("block_m", "block_n", "stages", "raster"),
+            "gemv": ("rows_per_wave", "unroll", "waves", "blocks")}[op]
+    if len(v) != len(keys):
+        raise SystemExit("config %r: %d values expected (%s)" % (text, len(keys), ",".join(keys)))
+    return dict(zip(keys, v))
+
+
+def compare(op, shape, specs, rounds=8, reps=20):
+    """Time the listed configs side by side: each round launches every
+    config `reps` times back to back between HIP events, in alternating
+    order from round to round, with the operands that stream from memory
+    (A and B for the GEMM, A_sparse, E and B for the sparse product, W for
+    the GEMV) rotated over enough copies to exceed the MALL three times.
+    Prints the median round per config in TFLOP/s (effective for sparse) or
+    GB/s.  This is how the library's default choices between close
+    candidates are made; a sequential sweep, one config after another on
+    warm operands, can rank them differently."""
+    import torch
+    import gemv_fp16_amd as gf
+    import inputs
+    mall = 256 << 20
+    if op == "gemm":
+        M, N, K = shape
+        copies = max(1, min(8, -(-3 * mall // (2 * (M + N) * K))))
+        A = torch.from_numpy(inputs.uniform_f16((M, K), 0, 0)).cuda()
+        B = torch.from_numpy(inputs.uniform_f16((N, K), 0, 1)).cuda()
+        ops = [(A, B)] + [(A.clone(), B.clone()) for _ in range(copies - 1)]
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        default = gf.gemm_default_config(M, N, K)
+        make = lambda c: [gf.prepare_gemm_f16_nt(a, b, C, cfg=c) for a, b in ops]
+        work, unit = 2.0 * M * N * K / 1e12, "TFLOP/s"
+    elif op == "sparse":
+        M, N, K = shape
+        copies = max(1, min(8, -(-3 * mall // (2 * N * K + M * K + M * K // 8))))
+        A = torch.from_numpy(inputs.uniform_f16((M, K), 0, 0)).cuda()
+        Asp, E = gf.sp24_compress_f16(A)
+        del A
+        B = torch.from_numpy(inputs.uniform_f16((N, K), 0, 1)).cuda()
+        ops = [(Asp, E, B)] + [(Asp.clone(), E.clone(), B.clone()) for _ in range(copies - 1)]
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        default = gf.sp_default_config(M, N, K)
+        make = lambda c: [gf.prepare_gemm_sp_f16_nt(a, e, b, C, cfg=c) for a, e, b in ops]
+        work, unit = 2.0 * M * N * K / 1e12, "effective TFLOP/s"
+    else:
+        N, K = shape
+        copies = max(1, min(256, -(-3 * mall // (2 * N * K))))
+        Ws = [torch.from_numpy(inputs.uniform_f16((N, K), 0, 0)).cuda()]
+        Ws += [Ws[0].clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(inputs.uniform_f16((K,), 0, 1)).cuda()
+        y = torch.empty((N,), dtype=torch.float16, device="cuda")
+        default = gf.gemv_default_config(N, K)
+        make = lambda c: [gf.prepare_gemv_f16(w, x, y, cfg=c) for w in Ws]
+        work, unit = (2.0 * N * K + 2.0 * K + 2.0 * N) / 1e9, "GB/s"
+    cfgs = [_cfg_from(op, t, default) for t in specs.split(";") if t.strip()]
+    calls = [make(c) for c in cfgs]
+    for cl in calls:
+        for i in range(max(reps // 2, 2)):
+            cl[i % copies]()
+    torch.cuda.synchronize()
+    times = [[] for _ in cfgs]
+    for r in range(rounds):
+        order = list(range(len(cfgs))) if r % 2 == 0 else list(reversed(range(len(cfgs))))
+        for j in order:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record()
+            for i in range(reps):
+                calls[j][i % copies]()
+            s1.record()
+            torch.cuda.synchronize()
+            times[j].append(s0.elapsed_time(s1) * 1e-3 / reps)
+    lines = ["%s %s, %d copies rotated, %d rounds of %d calls; median round" % (
+        op, "x".join(map(str, shape)), copies, rounds, reps), "",
+        "| config | median us | min us | max us | %s |" % unit, "|---|---|---|---|---|"]
+    for c, t in zip(cfgs, times):
+        med = float(np.median(t))
+        lines.append("| `%s`%s | %.2f | %.2f | %.2f | %.1f |" % (
+            json.dumps(c, sort_keys=True), " (default)" if c == default else "", med * 1e6, min(t) * 1e6,
+            max(t) * 1e6, work / med))
+    return "\n".join(lines)
+
+
 def table(op, shape, path, top):
     """Markdown ranking of the timed records of one (op, shape) in a sweep file."""
     recs, other, spilled = [], {}, []
@@ -332,7 +425,14 @@ def main(argv=None):
                     help="oracle expected-values file (default: tests/golden/sweep_expected_<op>_<shape>.txt)")
     ap.add_argument("--table", type=int, default=0,
                     help="print the best N records of this shape in --out as markdown, and run nothing")
+    ap.add_argument("--compare", default="",
+                    help="time these configs side by side instead of sweeping ('default' or values, ';'-separated)")
+    ap.add_argument("--rounds", type=int, default=8, help="rounds of --compare")
     a = ap.parse_args(argv)
+    if a.compare:
+        shape = [a.n, a.k] if a.op == "gemv" else [a.m, a.n, a.k]
+        print(compare(a.op, shape, a.compare, a.rounds, a.reps), flush=True)
+        return
     if a.table:
         shape = [a.n, a.k] if a.op == "gemv" else [a.m, a.n, a.k]
         print(table(a.op, shape, a.out, a.table))

@@ -289,11 +289,12 @@ def test_sparse_validation(L):
     assert len(cfgs) == L.gf_sp_config_count() >= 4
     d = gf.sp_default_config(8192, 8192, 8192)
     assert {**d, "raster": 1} in cfgs
-    # the paired form (stages = 0) is compiled for every tile shape, and is
-    # the choice where 256 x 128 tiles fill the chip but 256 x 256 ones do not
+    # the paired form (stages = 0) is compiled for every tile shape; where
+    # half-size tiles fill the chip but 256 x 256 ones do not, the default
+    # is 128 x 256 with three stages
     assert {(c["block_m"], c["block_n"]) for c in cfgs if c["stages"] == 0} == \
         {(256, 256), (256, 128), (128, 256), (128, 128)}
-    assert gf.sp_default_config(2048, 4096, 8192) == {"block_m": 256, "block_n": 128, "stages": 0, "raster": 1}
+    assert gf.sp_default_config(2048, 4096, 8192) == {"block_m": 128, "block_n": 256, "stages": 3, "raster": 1}
     assert gf.sp_default_config(4096, 4096, 8192)["stages"] == 3
     assert gf.sp_default_config(2048, 2048, 8192) == {"block_m": 128, "block_n": 128, "stages": 3, "raster": 1}
     out = gf.SpCfg()

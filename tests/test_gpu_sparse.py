@@ -253,15 +253,16 @@ def test_sparse_8192_integer_sampled():
     assert np.array_equal(got[ij[:, 0], ij[:, 1]], oracle.gemm_sp_nt_entries(Asp, E, B, ij))
 
 
-def test_sparse_default_paired_shape_sampled():
-    """A shape whose default tile is the paired form (256 x 128, stages 0):
-    integer inputs, the library's own launch configuration, sampled entries."""
+def test_sparse_default_half_tile_shape_sampled():
+    """A shape whose default is the half-size tile (128 x 256, three
+    stages): integer inputs, the library's own launch configuration, sampled
+    entries."""
     M, N, K = 2048, 4096, 8192
-    assert gf.sp_default_config(M, N, K)["stages"] == 0
+    assert (gf.sp_default_config(M, N, K)["block_m"], gf.sp_default_config(M, N, K)["block_n"]) == (128, 256)
     A = inputs.sparse24("integer", (M, K), seed=9)
     B = inputs.make("integer", (N, K), seed=9, stream_id=inputs.STREAM_B)
     Asp, E = oracle.sp24_compress(A)
-    _say("sparse default paired %dx%dx%d" % (M, N, K))
+    _say("sparse default half tile %dx%dx%d" % (M, N, K))
     got = sp_run(Asp, E, B)
     ij = sample_ij(M, N, 10000, seed=13)
     ij = np.concatenate([ij, [[M - 1, N - 1], [0, N - 1], [M - 1, 0]]]).astype(np.int64)
