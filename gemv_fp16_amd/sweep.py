@@ -332,8 +332,20 @@ def compare(op, shape, specs, rounds=8, reps=20):
         default = gf.gemv_default_config(N, K)
         make = lambda c: [gf.prepare_gemv_f16(w, x, y, cfg=c) for w in Ws]
         work, unit = (2.0 * N * K + 2.0 * K + 2.0 * N) / 1e9, "GB/s"
-    cfgs = [_cfg_from(op, t, default) for t in specs.split(";") if t.strip()]
-    calls = [make(c) for c in cfgs]
+    cfgs, calls, skipped = [], [], []
+    for t in specs.split(";"):
+        if not t.strip():
+            continue
+        c = _cfg_from(op, t, default)
+        try:
+            cl = make(c)
+            cl[0]()
+            torch.cuda.synchronize()
+        except RuntimeError as e:       # a config with no compiled kernel: listed, not timed
+            skipped.append((c, str(e)))
+            continue
+        cfgs.append(c)
+        calls.append(cl)
     for cl in calls:
         for i in range(max(reps // 2, 2)):
             cl[i % copies]()
@@ -358,6 +370,8 @@ def compare(op, shape, specs, rounds=8, reps=20):
         lines.append("| `%s`%s | %.2f | %.2f | %.2f | %.1f |" % (
             json.dumps(c, sort_keys=True), " (default)" if c == default else "", med * 1e6, min(t) * 1e6,
             max(t) * 1e6, work / med))
+    for c, e in skipped:
+        lines.append("| `%s` | not timed: %s ||||" % (json.dumps(c, sort_keys=True), e.split(": ", 1)[-1]))
     return "\n".join(lines)
 
 
