@@ -295,7 +295,10 @@ def compare(op, shape, specs, rounds=8, reps=20):
     Prints the median round per config in TFLOP/s (effective for sparse) or
     GB/s.  This is how the library's default choices between close
     candidates are made; a sequential sweep, one config after another on
-    warm operands, can rank them differently."""
+    warm operands, can rank them differently.  "default" is the default
+    tile or launch shape run as one launch with an explicit config, so a
+    shape the library would split into two launches (its row-split plan)
+    is compared here as one."""
     import torch
     import gemv_fp16_amd as gf
     import inputs
