@@ -332,16 +332,26 @@ static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBy
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 
-// The current device's address of `scratch`, looked up on the first call on
-// that device (with the device current) and kept.
-int scratch_for_current_device(void** out)
+// The address of `scratch` on the device that `stream` belongs to (the
+// current device for the null stream), looked up with that device current on
+// the first call there and kept.
+int scratch_for_stream(hipStream_t stream, void** out)
 {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return GF_ERR_HIP;
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return GF_ERR_HIP;
+    dev = cur;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return GF_ERR_HIP;
+        dev = (int)d;
+    }
     if (dev < 0 || dev >= kMaxDevices) return GF_ERR_HIP;
     void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
     if (!p) {
-        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GF_ERR_HIP;
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return GF_ERR_HIP;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return GF_ERR_HIP;
+        if (e != hipSuccess || !p) return GF_ERR_HIP;
         g_scratch_ptr[dev].store(p, std::memory_order_release);
     }
     *out = p;
@@ -802,7 +812,7 @@ int gemm_f16_nt_splitk_noalloc(const void* A, const void* B, float* C32, int M, 
     if (rc) return rc;
     if (M == 0 || N == 0) return GF_OK;
     void* ws = nullptr;
-    rc = scratch_for_current_device(&ws);
+    rc = scratch_for_stream(static_cast<hipStream_t>(stream), &ws);
     if (rc) return rc;
     return splitk_impl(A, B, C32, M, N, K, split_k, GF_SPLITK_TWOPASS, ws, kScratchBytes,
                        default_splitk_cfg(M, N, K, split_k), static_cast<hipStream_t>(stream));

@@ -141,9 +141,12 @@ int gemm_f16_nt_splitk_ex(const void* A, const void* B, float* C32, int M, int N
  * otherwise, checked on the host before anything is enqueued; 1024 x 1024
  * fits split_k <= 16).  Every call on one GPU shares that GPU's scratch: two
  * calls that overlap on one GPU (on different streams or host threads) race
- * and must be serialised by the caller.  The first call on a device looks up
- * the scratch's device address (hipGetSymbolAddress; GF_ERR_HIP if that
- * fails).  Other errors as gemm_f16_nt_splitk_ex.
+ * and must be serialised by the caller.  The scratch used is that of the
+ * device `stream` belongs to (the current device for the null stream); the
+ * first call on a device looks up its address there (hipGetSymbolAddress,
+ * with that device made current for the lookup and the caller's device
+ * restored; GF_ERR_HIP if that fails).  Other errors as
+ * gemm_f16_nt_splitk_ex.
  */
 int gemm_f16_nt_splitk_noalloc(const void* A, const void* B, float* C32, int M, int N, int K,
                                int split_k, void* stream);

@@ -70,6 +70,24 @@ def test_noalloc_equals_two_pass_twice_then_smaller():
             assert np.array_equal(got, oracle.gemm_nt_f32(A, B))
 
 
+def test_noalloc_on_a_side_stream():
+    """On a stream other than the null stream the scratch is found through
+    the stream's device; the result still equals the two-pass entry point's."""
+    L = gf.lib()
+    M, N, K, split = 256, 384, 4096, 8
+    A = inputs.make("integer", (M, K), 32, inputs.STREAM_A)
+    B = inputs.make("integer", (N, K), 32, inputs.STREAM_B)
+    dA, dB = dev(A), dev(B)
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    _say("noalloc %dx%dx%d split %d on a side stream" % (M, N, K, split))
+    rc = L.gemm_f16_nt_splitk_noalloc(_p(dA), _p(dB), _p(C), M, N, K, split, ctypes.c_void_p(side.cuda_stream))
+    assert rc == gf.GF_OK, gf.status_string(rc)
+    side.synchronize()
+    assert np.array_equal(C.cpu().numpy(), oracle.gemm_nt_f32(A, B))
+
+
 def test_noalloc_refuses_more_than_its_scratch():
     L = gf.lib()
     dA = torch.zeros((1024, 64), dtype=torch.float16, device="cuda")
