@@ -63,18 +63,32 @@ __device__ __forceinline__ void static_for(F&& f)
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Dynamic LDS above 64 KiB must be opted into, per kernel and per device.
-// `done` holds one bit per device id below 64 whose opt-in is made (the
-// caller keeps one per kernel); host threads that race only repeat the
-// idempotent call.
-inline hipError_t opt_in_lds(const void* kern, int bytes, std::atomic<uint64_t>& done)
+// Dynamic LDS above 64 KiB must be opted into, per kernel and per device:
+// here on the device the launch's stream belongs to (the current device for
+// the null stream), made current for the call if it is another.  `done`
+// holds one bit per device id below 64 whose opt-in is made (the caller
+// keeps one per kernel); host threads that race only repeat the idempotent
+// call.
+inline hipError_t opt_in_lds(const void* kern, int bytes, std::atomic<uint64_t>& done, hipStream_t stream)
 {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
     if (e != hipSuccess) return e;
+    dev = cur;
+    if (stream) {                       // the device the launch goes to: the stream's
+        hipDevice_t d;
+        e = hipStreamGetDevice(stream, &d);
+        if (e != hipSuccess) return e;
+        dev = (int)d;
+    }
     const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t(1) << dev) : 0;
     if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (dev != cur) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+    }
     if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
     return e;
 }

@@ -981,7 +981,7 @@ hipError_t launch_gemm(const GemmArgs& args, int slices, hipStream_t stream)
     auto kern = gemm_nt_kernel<Cfg, EPI, ALIGNED>;
     static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
     {
-        const hipError_t e = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in);
+        const hipError_t e = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in, stream);
         if (e != hipSuccess) return e;
     }
     const int tiles = ceil_div(a.M, Cfg::BM) * ceil_div(a.N, Cfg::BN);

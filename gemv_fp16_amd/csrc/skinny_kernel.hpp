@@ -258,7 +258,7 @@ hipError_t launch_skinny_lds_ma(const uint16_t* A, const uint16_t* B, uint16_t* 
     auto kern = skinny_lds_kernel<NB, S, W, MA>;
     static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
     {
-        const hipError_t e = opt_in_lds((const void*)kern, Cf::LDS_BYTES, lds_opt_in);
+        const hipError_t e = opt_in_lds((const void*)kern, Cf::LDS_BYTES, lds_opt_in, stream);
         if (e != hipSuccess) return e;
     }
     const int grid = ceil_div(N, NB * 16);
@@ -418,7 +418,7 @@ hipError_t launch_skinny_vec_mv(const uint16_t* A, const uint16_t* B, uint16_t* 
     auto kern = skinny_vec_kernel<MV, ROWS, UNROLL, WAVES>;
     static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
     {
-        const hipError_t e = opt_in_lds((const void*)kern, 160 * 1024, lds_opt_in);
+        const hipError_t e = opt_in_lds((const void*)kern, 160 * 1024, lds_opt_in, stream);
         if (e != hipSuccess) return e;
     }
     const int groups = ceil_div(N, ROWS);

@@ -709,7 +709,7 @@ hipError_t launch_sp_gemm(const SpArgs& a, hipStream_t stream)
     auto kern = sp_gemm_kernel<Cfg, ALIGNED>;
     static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
     {
-        const hipError_t err = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in);
+        const hipError_t err = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in, stream);
         if (err != hipSuccess) return err;
     }
     const int tiles = ceil_div(a.M, Cfg::BM) * ceil_div(a.N, Cfg::BN);
@@ -1122,7 +1122,7 @@ hipError_t launch_spp_gemm(const SpArgs& a, hipStream_t stream)
     auto kern = spp_gemm_kernel<Cfg>;
     static std::atomic<uint64_t> lds_opt_in{0};   // devices where the LDS size is opted into
     {
-        const hipError_t err = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in);
+        const hipError_t err = opt_in_lds((const void*)kern, Cfg::LDS_BYTES, lds_opt_in, stream);
         if (err != hipSuccess) return err;
     }
     const int tiles = ceil_div(a.M, Cfg::BM) * ceil_div(a.N, Cfg::BN);
