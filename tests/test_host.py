@@ -192,3 +192,16 @@ y.hpp:9:1: remark:     VGPRs: 7 [-Rpass-analysis=kernel-resource-usage]
         "void gf::gemm_nt_kernel<gf::GemmCfg<256, 256, 64, 2, 256, 2, 0, 0>, 0, true>(gf::GemmArgs)")
     # the epilogue's per-wave transpose (4 waves x 128 x (128 + 8) fp16) outgrows the 2-stage ring
     assert resources.gemm_lds_bytes(cfg) == max(2 * (256 + 256) * 64 * 2, 4 * 128 * 136 * 2) == 139264
+
+
+def test_compare_config_parsing():
+    """--compare reads each config as 'default' or the op's value list, and
+    refuses a list of the wrong length instead of guessing."""
+    d = {"block_m": 256, "block_n": 256, "block_k": 64, "stages": 2, "threads": 256, "raster": 0, "schedule": 2}
+    assert sweep._cfg_from("gemm", "default", d) == d
+    assert sweep._cfg_from("gemm", "256,128,64,3,256,2,1", d) == {
+        "block_m": 256, "block_n": 128, "block_k": 64, "stages": 3, "threads": 256, "schedule": 2, "raster": 1}
+    assert sweep._cfg_from("sparse", "128,256,3,1", {}) == {"block_m": 128, "block_n": 256, "stages": 3, "raster": 1}
+    assert sweep._cfg_from("gemv", "1,4,4,512", {}) == {"rows_per_wave": 1, "unroll": 4, "waves": 4, "blocks": 512}
+    with pytest.raises(SystemExit):
+        sweep._cfg_from("sparse", "128,256,3", {})
