@@ -450,18 +450,12 @@ int find_skinny(const gf_skinny_cfg& c)
     return -1;
 }
 
-// Launch shape of the skinny GEMM, from the offline sweep at N = K = 8192:
-// up to 8 rows the vector form (one row of B per wave, the GEMV's access
-// pattern) streams fastest where it fits: 5.8 TB/s at M = 2 (8 chunks per
-// row in flight), 5.4 at M = 4 and 4.8 at M = 8 (4 chunks), against 4.8,
-// 4.6 and 4.6 for the best MFMA form.  Elsewhere, up to 4 rows the direct
-// form (one 16-row block of B per workgroup, 4-step batches); from 5 rows
-// the LDS-staged form (three blocks of B share each A chunk, two chunks in
-// flight), when K is a multiple of its chunk.
 // Skinny launch shape, from sweeps of the compiled shapes for M = 1..16 at
 // N x K = 8192^2, 4096^2, 4096 x 14336, 2048 x 8192, 6144^2, 4096 x 11008,
 // 8192 x 4096, 14336 x 4096, 16384 x 4096, 28672 x 4096, 8192 x 2048,
-// 16384 x 2048 and 12288 x 6144:
+// 16384 x 2048 and 12288 x 6144, and side-by-side timings of the split form:
+//  * split form (M <= 8, K = 8192 or 16384, at least 4096 rows of B): the
+//    GEMV's split launch shape with A in registers (below);
 //  * vector form (M <= 8): 8-wave workgroups where rows are long (K >= 8192)
 //    or B is small; otherwise 16 waves with 4 chunks per lane in flight, for
 //    M <= 2 over at least 32 M elements of B and for M <= 4 from 8192 rows
@@ -489,6 +483,21 @@ gf_skinny_cfg default_skinny_cfg(int M, int N, int K)
             c.blocks = 1;
             c.stages = M <= 32 ? 3 : 2;
         }
+        return c;
+    }
+    // Split form (the GEMV's split launch shape, A in registers) where K is
+    // 8192 or 16384 and B has at least 4096 rows, timed side by side against
+    // the vector and LDS forms with B rotated through HBM at N x K = 8192^2,
+    // 16384 x 8192, 4096 x 16384 and 8192 x 16384 (M = 1, 2, 4, 8):
+    // 1.04-1.21x at K = 8192 (4 waves, 4 chunks per lane, 512 workgroups),
+    // 1.07-1.30x at K = 16384 for M <= 4 (4 waves, 8 chunks) and 1.03-1.09x
+    // there for M = 5..8 (8 waves, 4 chunks, 256 workgroups).  At K = 4096 it trails the vector
+    // form (shorter rows: more reduction and barrier per byte).
+    if (M <= kSkinnySplitMaxM && N >= 4096 && (K == 8192 || K == 16384)) {
+        if (K == 8192) { c.blocks = 512; c.unroll = 4; c.waves = 4; }
+        else if (M <= 4) { c.blocks = 512; c.unroll = 8; c.waves = 4; }
+        else { c.blocks = 256; c.unroll = 4; c.waves = 8; }
+        c.stages = -1;
         return c;
     }
     const bool small_n = N < 8192;
@@ -546,6 +555,7 @@ int skinny_impl(const void* A, const void* B, void* C, int M, int N, int K, cons
     if (idx < 0 || !g_skinny_table[idx]) return GF_ERR_UNSUPPORTED;
     const SkinnyDesc& d = kSkinnyConfigs[idx];
     if (d.stages == 1 && !skinny_vec_fits(M, K, d.unroll)) return GF_ERR_UNSUPPORTED;
+    if (d.stages < 0 && !skinny_split_fits(M, K, d.unroll, d.waves)) return GF_ERR_UNSUPPORTED;
     if (d.stages >= 2 && (K % kSkinnyKc != 0 || K == 0)) return GF_ERR_UNSUPPORTED;
     if (M > kSkinnyMaxM && (d.stages < 2 || M > skinny_lds_max_m(d.blocks, d.stages, d.waves)))
         return GF_ERR_UNSUPPORTED;

@@ -33,7 +33,9 @@ constexpr int kNumGemv = sizeof(kGemvConfigs) / sizeof(kGemvConfigs[0]);
 // in flight per wave).  stages >= 2: LDS-staged form (blocks as above, that
 // many 512-k chunks in the ring, unroll unused, 0).  stages = 1: vector form
 // for M <= 8 (blocks = rows of B per wave, unroll = 16-byte chunks per row
-// and lane per step).  waves: waves per workgroup.
+// and lane per step).  stages = -1: split form for M <= 8 and K = 512 *
+// unroll * waves (blocks = workgroups at most, unroll = 16-byte chunks per
+// lane and row).  waves: waves per workgroup.
 struct SkinnyDesc {
     int blocks, unroll, waves, stages;
 };
@@ -45,6 +47,7 @@ constexpr SkinnyDesc kSkinnyConfigs[] = {
     {2, 0, 8, 3},  {2, 0, 4, 3},  {3, 0, 8, 2},  {1, 0, 4, 3},
     {1, 4, 8, 1},  {2, 2, 8, 1},  {2, 4, 8, 1},  {4, 2, 8, 1},  {2, 2, 16, 1}, {4, 1, 8, 1},
     {1, 8, 8, 1},  {1, 4, 16, 1}, {1, 4, 4, 1},  {1, 2, 8, 1},  {1, 8, 4, 1},
+    {512, 4, 4, -1}, {512, 8, 2, -1}, {512, 8, 4, -1}, {256, 8, 4, -1}, {256, 4, 8, -1},
 };
 constexpr int kNumSkinny = sizeof(kSkinnyConfigs) / sizeof(kSkinnyConfigs[0]);
 

@@ -18,6 +18,8 @@ void register_from()
             g_skinny_table[I] = &launch_skinny<d.blocks, d.unroll, d.waves>;
         else if constexpr (d.stages == 1)
             g_skinny_table[I] = &launch_skinny_vec<d.blocks, d.unroll, d.waves>;
+        else if constexpr (d.stages < 0)
+            g_skinny_table[I] = &launch_skinny_split<d.blocks, d.unroll, d.waves>;
         else if constexpr (SkinnyLdsCfg<d.blocks, d.stages, d.waves>::kValid)
             g_skinny_table[I] = &launch_skinny_lds<d.blocks, d.stages, d.waves>;
         register_from<I + 1>();

@@ -318,8 +318,12 @@ constexpr int skinny_lds_max_m(int NB, int S, int W)
 // chunk of B meets the M matching chunks of A in v_dot2_f32_f16 (fp32
 // accumulation).  When a wave finishes its rows it folds each of its ROWS x MV
 // sums across the lanes with DPP and writes the fp16 results.  One workgroup
-// per CU walks the row groups grid-stride, so A is staged once per CU.
-// Requires K % (512 * UNROLL) == 0 and MV * K * 2 <= 160 KiB.
+// per CU walks the row groups grid-stride, so A is staged once per CU.  As
+// in the GEMV's split form, the loads of the next task are issued
+// unconditionally in the steady-state loop (a load under a branch would make
+// the compiler wait for every load in flight, the next task's included,
+// before each multiply).  Requires K % (512 * UNROLL) == 0 and
+// MV * K * 2 <= 160 KiB.
 template <int MV, int ROWS, int UNROLL, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* __restrict__ A,
                                                                 const uint16_t* __restrict__ B,
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* 
     half8* as = (half8*)vec_smem;                      // [MV][K / 8]
     constexpr int STEP = kWave * UNROLL;               // chunks of a row per step
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nch = K / 8;
     const int spg = nch / STEP;                        // steps per row group
     const int groups = ceil_div(N, ROWS);
@@ -387,13 +391,21 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* 
                 }
         }
     };
-    for (int i = 0; i < ntasks; i += 2) {
-        if (i + 1 < ntasks) load(i + 1, buf[1]);
+    int i = 0;
+    for (; i + 2 < ntasks; i += 2) {                   // tasks i + 1 and i + 2 exist
+        load(i + 1, buf[1]);
+        __builtin_amdgcn_sched_barrier(0);             // the loads leave before the multiply waits
         compute(i, buf[0]);
-        if (i + 1 < ntasks) {
-            if (i + 2 < ntasks) load(i + 2, buf[0]);
-            compute(i + 1, buf[1]);
-        }
+        load(i + 2, buf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i + 1, buf[1]);
+    }
+    if (i + 1 < ntasks) {
+        load(i + 1, buf[1]);
+        compute(i, buf[0]);
+        compute(i + 1, buf[1]);
+    } else if (i < ntasks) {
+        compute(i, buf[0]);
     }
 #endif
 }
@@ -439,6 +451,142 @@ hipError_t launch_skinny_vec(const uint16_t* A, const uint16_t* B, uint16_t* C, 
     case 2: return launch_skinny_vec_mv<2, ROWS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
     case 4: return launch_skinny_vec_mv<4, ROWS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
     default: return launch_skinny_vec_mv<8, ROWS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split form (M <= 8, K == 512 * UNROLL * WAVES): the GEMV's split form, M
+// vectors at once
+// ---------------------------------------------------------------------------
+//
+// The GEMV's fastest launch shape lets the waves of a workgroup split K and
+// the workgroups walk whole rows grid-stride, so that all of them together
+// read one band of rows at a time, the order HBM serves best.  Here the same
+// for up to 8 rows of A: wave w of a workgroup owns chunks [w * STEP,
+// (w + 1) * STEP) of every row of B, STEP = 64 * UNROLL (lane l the chunks
+// w * STEP + l + 64 u), and since K is exactly WAVES * STEP chunks of 8, a
+// lane meets the same M x UNROLL chunks of A in every row: they are loaded
+// once into registers, so the multiply reads nothing from LDS.  A task is
+// one row of B; the next row's loads are issued before the current one is
+// multiplied.  Per row, every lane's MV partial sums are folded across its
+// 16-lane DPP row; the 4 row leaders of each wave park them in LDS (slots
+// alternating between tasks), and after the task's one barrier thread q < MV
+// adds the 4 * WAVES partials of output m = q in a fixed order and writes
+// C[m][row] (deterministic).  Requires 16-byte aligned A and B.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
+    v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]: quads
+    v += dpp_f32<0x141>(v);   // row_half_mirror: 8 lanes
+    v += dpp_f32<0x140>(v);   // row_mirror: every lane holds its 16-lane row's sum
+    return v;
+}
+
+template <int MV, int UNROLL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void skinny_split_kernel(const uint16_t* __restrict__ A,
+                                                                  const uint16_t* __restrict__ B,
+                                                                  uint16_t* __restrict__ C, int M, int N,
+                                                                  int K)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int STEP = kWave * UNROLL;               // chunks of a row per wave
+    constexpr int NP = 4 * WAVES;                      // partial sums per output
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    extern __shared__ __attribute__((aligned(16))) char split_smem[];
+    GF_LDS float* red = (GF_LDS float*)split_smem;     // [2][MV][NP]
+    const int nch = K / 8;                             // == WAVES * STEP
+    const int cbase = wave * STEP + lane;
+    const int ntasks = (int)blockIdx.x < N ? (N - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+    if (ntasks == 0) return;                           // no rows for this workgroup
+    const half8* Bv = (const half8*)B;
+    auto load = [&](int i, half8 (&b)[UNROLL]) __attribute__((always_inline)) {
+        const half8* wr = Bv + (size_t)(blockIdx.x + i * gridDim.x) * nch + cbase;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) b[u] = __builtin_nontemporal_load(wr + u * kWave);
+    };
+    half8 buf0[UNROLL], buf1[UNROLL];
+    load(0, buf0);                                     // B traffic starts before A is fetched
+    half8 av[MV][UNROLL];
+    const half8* Av = (const half8*)A;
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) av[m][u] = m < M ? Av[(size_t)m * nch + cbase + u * kWave] : half8{};
+    float acc[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) acc[m] = 0.0f;
+    auto compute = [&](int i, const half8 (&b)[UNROLL]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int m = 0; m < MV; ++m) acc[m] = dot8(b[u], av[m][u], acc[m]);
+        GF_LDS float* slot = red + (i & 1) * MV * NP;
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+            const float s = row16_sum(acc[m]);
+            if (lane % 16 == 0) slot[m * NP + wave * 4 + lane / 16] = s;
+            acc[m] = 0.0f;
+        }
+        lds_barrier();
+        if (threadIdx.x < MV) {
+            const int m = threadIdx.x;
+            float t = 0.0f;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) t += slot[m * NP + p];
+            if (m < M) C[(size_t)m * N + blockIdx.x + i * gridDim.x] = f32_to_f16_bits(t);
+        }
+    };
+    // Steady state: the loads of tasks i + 1 and i + 2 are issued with no
+    // branch around them, so each multiply waits only for its own row.
+    int i = 0;
+    for (; i + 2 < ntasks; i += 2) {                   // tasks i + 1 and i + 2 exist
+        load(i + 1, buf1);
+        __builtin_amdgcn_sched_barrier(0);             // the loads leave before the multiply waits
+        compute(i, buf0);
+        load(i + 2, buf0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i + 1, buf1);
+    }
+    if (i + 1 < ntasks) {
+        load(i + 1, buf1);
+        compute(i, buf0);
+        compute(i + 1, buf1);
+    } else if (i < ntasks) {
+        compute(i, buf0);
+    }
+#endif
+}
+
+constexpr int kSkinnySplitMaxM = 8;
+
+// Whether the split form with `unroll` chunks and `waves` waves runs M x K.
+__host__ __device__ constexpr bool skinny_split_fits(int M, int K, int unroll, int waves)
+{
+    return M >= 1 && M <= kSkinnySplitMaxM && unroll > 0 && waves > 0 && K == 512 * unroll * waves;
+}
+
+template <int MV, int BLOCKS, int UNROLL, int WAVES>
+hipError_t launch_skinny_split_mv(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                                  hipStream_t stream)
+{
+    const int grid = N < BLOCKS ? N : BLOCKS;
+    hipLaunchKernelGGL((skinny_split_kernel<MV, UNROLL, WAVES>), dim3(grid), dim3(WAVES * kWave),
+                       (size_t)2 * MV * 4 * WAVES * 4, stream, A, B, C, M, N, K);
+    return hipGetLastError();
+}
+
+// The split-form launch for M rows (BLOCKS = workgroups at most); the caller
+// has checked skinny_split_fits.
+template <int BLOCKS, int UNROLL, int WAVES>
+hipError_t launch_skinny_split(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
+                               hipStream_t stream)
+{
+    switch (skinny_vec_mv(M)) {
+    case 1: return launch_skinny_split_mv<1, BLOCKS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    case 2: return launch_skinny_split_mv<2, BLOCKS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    case 4: return launch_skinny_split_mv<4, BLOCKS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
+    default: return launch_skinny_split_mv<8, BLOCKS, UNROLL, WAVES>(A, B, C, M, N, K, stream);
     }
 }
 

@@ -243,7 +243,11 @@ int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int
  *  - stages = 1, vector form for M <= 8: blocks = rows of B per wave, unroll
  *    = 16-byte chunks per row and lane in flight; B streamed as by gemv_f16,
  *    A staged in LDS (needs K % (512 * unroll) == 0 and M' * K * 2 <= 160 KiB,
- *    M' = M rounded up to 1, 2, 4 or 8).
+ *    M' = M rounded up to 1, 2, 4 or 8);
+ *  - stages = -1, split form for M <= 8: gemv_f16's split launch shape (the
+ *    waves of a workgroup split K, workgroups walk whole rows of B), A held
+ *    in registers; blocks = workgroups at most, unroll = 16-byte chunks per
+ *    lane and row (needs K == 512 * unroll * waves).
  * Defined by the TileLang GEMV page: GEMV as the degenerate GEMM with a
  * single row of A, here with up to 16 rows (C = A B^T of the TileLang FP16
  * matmul page, section 1).

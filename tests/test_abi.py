@@ -153,14 +153,21 @@ def test_skinny_default_rule():
     and the shape-dependent choices hold."""
     compiled = gf.skinny_configs()
     for n in (64, 2048, 4096, 6144, 8192, 28672):
-        for k in (64, 2048, 2560, 4096, 6144, 11008, 14336, 8192, 12288):
+        for k in (64, 2048, 2560, 4096, 6144, 11008, 14336, 8192, 12288, 16384):
             for m in range(1, 17):
                 assert gf.skinny_default_config(m, n, k) in compiled, (m, n, k)
     d = gf.skinny_default_config
-    # 8192 x 8192: vector form to M = 8, then three 16-row blocks through LDS
-    assert d(1, 8192, 8192) == {"blocks": 1, "unroll": 8, "waves": 8, "stages": 1}
-    assert d(8, 8192, 8192) == {"blocks": 1, "unroll": 4, "waves": 8, "stages": 1}
+    # 8192 x 8192: split form to M = 8, then three 16-row blocks through LDS
+    assert d(1, 8192, 8192) == {"blocks": 512, "unroll": 4, "waves": 4, "stages": -1}
+    assert d(8, 8192, 8192) == {"blocks": 512, "unroll": 4, "waves": 4, "stages": -1}
     assert d(16, 8192, 8192) == {"blocks": 3, "unroll": 0, "waves": 8, "stages": 2}
+    # K = 16384: 4 waves with 8 chunks per lane to M = 4, 8 waves with 4 beyond
+    assert d(4, 4096, 16384) == {"blocks": 512, "unroll": 8, "waves": 4, "stages": -1}
+    assert d(5, 8192, 16384) == {"blocks": 256, "unroll": 4, "waves": 8, "stages": -1}
+    # fewer than 4096 rows of B, or other K: the other forms
+    assert d(2, 2048, 8192)["stages"] == 1
+    assert d(8, 2048, 8192)["stages"] != -1
+    assert d(8, 8192, 4096)["stages"] != -1
     # fewer rows of B: one block per workgroup through LDS from M = 5
     assert d(8, 4096, 14336) == {"blocks": 1, "unroll": 0, "waves": 16, "stages": 4}
     assert d(16, 6144, 6144) == {"blocks": 1, "unroll": 0, "waves": 8, "stages": 3}

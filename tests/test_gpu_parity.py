@@ -345,6 +345,8 @@ def skinny_runs(cfg, M, K):
         return True
     if cfg["stages"] >= 2:
         return K > 0 and K % 512 == 0
+    if cfg["stages"] < 0:                              # split form
+        return M <= 8 and K == 512 * cfg["unroll"] * cfg["waves"]
     mv = 1 if M <= 1 else (2 if M <= 2 else (4 if M <= 4 else 8))
     return M <= 8 and K > 0 and K % (512 * cfg["unroll"]) == 0 and mv * K * 2 <= 160 * 1024
 
@@ -353,10 +355,11 @@ def skinny_runs(cfg, M, K):
                                    (4, 1000, 4096), (8, 333, 2048), (1, 513, 2048), (2, 64, 8192),
                                    (7, 130, 16384), (5, 9000, 2048)])
 def test_skinny_every_config(M, N, K):
-    """Every launch shape: direct, LDS-staged (K a multiple of 512) and vector
+    """Every launch shape: direct, LDS-staged (K a multiple of 512), vector
     form (M <= 8, K a multiple of 512 * unroll; (5, 9000, 2048) gives waves
-    more than one row group); shapes outside a form's limits must be
-    refused."""
+    more than one row group) and split form (M <= 8, K = 512 * unroll *
+    waves: (2, 64, 8192) and (7, 130, 16384)); shapes outside a form's
+    limits must be refused."""
     A, B = operands("integer", M, N, K, seed=6)
     ref = oracle.gemm_nt_f16(A, B)
     for cfg in gf.skinny_configs():
@@ -467,6 +470,20 @@ def test_skinny_default_shapes(M, N, K):
     assert np.array_equal(run_skinny(A, B), oracle.gemm_nt_f16(A, B))
     A, B = operands("uniform", M, N, K, seed=8)
     check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("N,K", [(8192, 8192), (4100, 16384), (5000, 8192)])
+def test_skinny_split_default_shapes(M, N, K):
+    """The split form where the library picks it (M <= 8, K = 8192 or 16384,
+    at least 4096 rows of B; 4100 and 5000 rows leave the grid-stride walk
+    ragged), all outputs: integers bit-exact, uniform within tolerance."""
+    assert gf.skinny_default_config(M, N, K)["stages"] == -1
+    A, B = operands("integer", M, N, K, seed=14)
+    _say("skinny split %dx%dx%d cfg %s" % (M, N, K, gf.skinny_default_config(M, N, K)))
+    assert np.array_equal(run_skinny(A, B), oracle.gemm_nt_f16(A, B))
+    A, B = operands("uniform", M, N, K, seed=14)
+    check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny split %dx%dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [4, 16])
