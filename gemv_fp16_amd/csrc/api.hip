@@ -367,7 +367,7 @@ int splitk_reduce(const void* ws, void* C, bool out_f16, int64_t mn, int slices,
     } else if (!out_f16) {
         hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(mn, 256)), dim3(256), 0, stream,
                            static_cast<const float*>(ws), static_cast<float*>(C), mn, slices);
-    } else if (aligned(ws, 16) && aligned(C, 16) && mn % 8 == 0) {
+    } else if (aligned(ws, 32) && aligned(C, 16) && mn % 8 == 0) {   // 8-float vectors of ws
         hipLaunchKernelGGL(splitk_reduce_f16x8_kernel, dim3(grid_for(mn / 8, 256)), dim3(256), 0,
                            stream, static_cast<const floatx4*>(ws), static_cast<u32x4*>(C), mn / 8,
                            slices);
