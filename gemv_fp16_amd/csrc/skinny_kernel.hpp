@@ -322,8 +322,12 @@ constexpr int skinny_lds_max_m(int NB, int S, int W)
 // in the GEMV's split form, the loads of the next task are issued
 // unconditionally in the steady-state loop (a load under a branch would make
 // the compiler wait for every load in flight, the next task's included,
-// before each multiply).  Requires K % (512 * UNROLL) == 0 and
-// MV * K * 2 <= 160 KiB.
+// before each multiply).  When K / 8 is not a multiple of STEP the last
+// step of a row runs past its end: those lanes load a chunk of the row that
+// exists and multiply zeros instead (A is staged with its rows padded by zero
+// chunks to a whole number of steps, and the B chunk is replaced by zeros,
+// so that an infinite B entry cannot turn the padding into a NaN).
+// Requires K % 8 == 0 and MV * (K / 8 rounded up to STEP) * 16 <= 160 KiB.
 template <int MV, int ROWS, int UNROLL, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* __restrict__ A,
                                                                 const uint16_t* __restrict__ B,
@@ -332,12 +336,14 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* 
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(ROWS * MV <= kWave, "one lane stores each result");
     extern __shared__ __attribute__((aligned(16))) char vec_smem[];
-    half8* as = (half8*)vec_smem;                      // [MV][K / 8]
+    half8* as = (half8*)vec_smem;                      // [MV][npad]
     constexpr int STEP = kWave * UNROLL;               // chunks of a row per step
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nch = K / 8;
-    const int spg = nch / STEP;                        // steps per row group
+    const int spg = ceil_div(nch, STEP);               // steps per row group
+    const int npad = spg * STEP;                       // A's row length in LDS, zero-padded
+    const bool ragged = npad != nch;
     const int groups = ceil_div(N, ROWS);
     const int g0 = blockIdx.x * WAVES + wave, gstride = gridDim.x * WAVES;
     const int my_groups = g0 < groups ? (groups - g0 + gstride - 1) / gstride : 0;
@@ -350,16 +356,17 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* 
         const int c0 = (i % spg) * STEP + lane;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
-            const half8* wr = Bv + (size_t)min(g * ROWS + r, N - 1) * nch + c0;
+            const half8* wr = Bv + (size_t)min(g * ROWS + r, N - 1) * nch;
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) b[r][u] = __builtin_nontemporal_load(wr + u * kWave);
+            for (int u = 0; u < UNROLL; ++u)
+                b[r][u] = __builtin_nontemporal_load(wr + min(c0 + u * kWave, nch - 1));
         }
     };
     if (ntasks > 0) load(0, buf[0]);                   // B traffic starts before A is staged
     const half8* Av = (const half8*)A;
-    for (int j = threadIdx.x; j < MV * nch; j += WAVES * kWave) {
-        const int m = j / nch;
-        as[j] = m < M ? Av[(size_t)m * nch + (j - m * nch)] : half8{};
+    for (int j = threadIdx.x; j < MV * npad; j += WAVES * kWave) {
+        const int m = j / npad, c = j - m * npad;
+        as[j] = m < M && c < nch ? Av[(size_t)m * nch + c] : half8{};
     }
     __syncthreads();
 
@@ -368,13 +375,20 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_vec_kernel(const uint16_t* 
     for (int r = 0; r < ROWS; ++r)
 #pragma unroll
         for (int m = 0; m < MV; ++m) acc[r][m] = 0.0f;
-    auto compute = [&](int i, const half8 (&b)[ROWS][UNROLL]) __attribute__((always_inline)) {
+    auto compute = [&](int i, half8 (&b)[ROWS][UNROLL]) __attribute__((always_inline)) {
         const int c0 = (i % spg) * STEP + lane;
+        if (ragged && i % spg == spg - 1) {            // wave-uniform: a row's last step
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r)
+                    if (c0 + u * kWave >= nch) b[r][u] = half8{};
+        }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
             for (int m = 0; m < MV; ++m) {
-                const half8 xv = as[m * nch + c0 + u * kWave];
+                const half8 xv = as[m * npad + c0 + u * kWave];
 #pragma unroll
                 for (int r = 0; r < ROWS; ++r) acc[r][m] = dot8(b[r][u], xv, acc[r][m]);
             }
@@ -416,12 +430,23 @@ constexpr int kSkinnyVecGrid = 256;                    // one workgroup per CU
 // A-row capacity of the vector form for M rows: 1, 2, 4 or 8.
 __host__ __device__ constexpr int skinny_vec_mv(int M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
 
+// Chunks of 8 per row of A in the vector form's LDS: K / 8 rounded up to a
+// whole number of 64 * unroll-chunk steps.
+__host__ __device__ constexpr long long skinny_vec_npad(int K, int unroll)
+{
+    return ((long long)K / 8 + 64LL * unroll - 1) / (64LL * unroll) * (64LL * unroll);
+}
+
 // Whether the vector form with `unroll` runs M x K.
 __host__ __device__ constexpr bool skinny_vec_fits(int M, int K, int unroll)
 {
-    return M >= 1 && M <= kSkinnyVecMaxM && K > 0 && unroll > 0 && K % (512 * unroll) == 0 &&
-           (long long)skinny_vec_mv(M) * K * 2 <= 160 * 1024;
+    return M >= 1 && M <= kSkinnyVecMaxM && K > 0 && K % 8 == 0 && unroll > 0 &&
+           (long long)skinny_vec_mv(M) * skinny_vec_npad(K, unroll) * 16 <= 160 * 1024;
 }
+
+// Whether its rows split into whole steps (the case the default rule was
+// measured on).
+__host__ __device__ constexpr bool skinny_vec_whole(int K, int unroll) { return K % (512 * unroll) == 0; }
 
 template <int MV, int ROWS, int UNROLL, int WAVES>
 hipError_t launch_skinny_vec_mv(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int N, int K,
@@ -436,7 +461,7 @@ hipError_t launch_skinny_vec_mv(const uint16_t* A, const uint16_t* B, uint16_t* 
     const int groups = ceil_div(N, ROWS);
     int grid = ceil_div(groups, WAVES);
     if (grid > kSkinnyVecGrid) grid = kSkinnyVecGrid;
-    const size_t lds = (size_t)MV * K * 2;
+    const size_t lds = (size_t)MV * skinny_vec_npad(K, UNROLL) * 16;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, stream, A, B, C, M, N, K);
     return hipGetLastError();
 }

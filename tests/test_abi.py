@@ -153,7 +153,7 @@ def test_skinny_default_rule():
     and the shape-dependent choices hold."""
     compiled = gf.skinny_configs()
     for n in (64, 2048, 4096, 6144, 8192, 28672):
-        for k in (64, 2048, 2560, 4096, 6144, 11008, 14336, 8192, 12288, 16384):
+        for k in (64, 2048, 2560, 4096, 5120, 6144, 11008, 13824, 14336, 8192, 12288, 15360, 16384):
             for m in range(1, 17):
                 assert gf.skinny_default_config(m, n, k) in compiled, (m, n, k)
     d = gf.skinny_default_config
@@ -164,6 +164,14 @@ def test_skinny_default_rule():
     # K = 16384: 4 waves with 8 chunks per lane to M = 4, 8 waves with 4 beyond
     assert d(4, 4096, 16384) == {"blocks": 512, "unroll": 8, "waves": 4, "stages": -1}
     assert d(5, 8192, 16384) == {"blocks": 256, "unroll": 4, "waves": 8, "stages": -1}
+    # rows that do not split into whole 2048-chunk steps: the vector form with
+    # a ragged last step for M <= 4 from K = 4096 (16 waves where N divides
+    # the grid's 4096 waves evenly), the direct form for short rows
+    assert d(1, 4096, 11008) == {"blocks": 1, "unroll": 4, "waves": 16, "stages": 1}
+    assert d(2, 5120, 13824) == {"blocks": 1, "unroll": 4, "waves": 8, "stages": 1}
+    assert d(4, 8192, 5120) == {"blocks": 1, "unroll": 4, "waves": 16, "stages": 1}
+    assert d(4, 4096, 2560)["stages"] == 0
+    assert d(8, 4096, 11008)["stages"] == 0
     # fewer than 4096 rows of B, or other K: the other forms
     assert d(2, 2048, 8192)["stages"] == 1
     assert d(8, 2048, 8192)["stages"] != -1

@@ -348,7 +348,9 @@ def skinny_runs(cfg, M, K):
     if cfg["stages"] < 0:                              # split form
         return M <= 8 and K == 512 * cfg["unroll"] * cfg["waves"]
     mv = 1 if M <= 1 else (2 if M <= 2 else (4 if M <= 4 else 8))
-    return M <= 8 and K > 0 and K % (512 * cfg["unroll"]) == 0 and mv * K * 2 <= 160 * 1024
+    step = 64 * cfg["unroll"]                          # the last step of a row may be ragged
+    npad = (K // 8 + step - 1) // step * step
+    return M <= 8 and K > 0 and mv * npad * 16 <= 160 * 1024
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 520, 1536), (3, 1000, 512), (9, 77, 2048), (6, 300, 1024),
@@ -356,10 +358,11 @@ def skinny_runs(cfg, M, K):
                                    (7, 130, 16384), (5, 9000, 2048)])
 def test_skinny_every_config(M, N, K):
     """Every launch shape: direct, LDS-staged (K a multiple of 512), vector
-    form (M <= 8, K a multiple of 512 * unroll; (5, 9000, 2048) gives waves
-    more than one row group) and split form (M <= 8, K = 512 * unroll *
-    waves: (2, 64, 8192) and (7, 130, 16384)); shapes outside a form's
-    limits must be refused."""
+    form (M <= 8, A's rows padded to whole steps within 160 KiB; K not a
+    multiple of 512 * unroll leaves a ragged last step; (5, 9000, 2048)
+    gives waves more than one row group) and split form (M <= 8, K = 512 *
+    unroll * waves: (2, 64, 8192) and (7, 130, 16384)); shapes outside a
+    form's limits must be refused."""
     A, B = operands("integer", M, N, K, seed=6)
     ref = oracle.gemm_nt_f16(A, B)
     for cfg in gf.skinny_configs():
@@ -377,10 +380,12 @@ def test_skinny_every_config(M, N, K):
 
 
 def test_skinny_lds_form_needs_k_multiple_of_512():
+    """K = 1000: the direct and vector forms run it (the vector form with a
+    ragged last step), the LDS-staged and split forms refuse."""
     A, B = operands("integer", 4, 64, 1000, seed=6)
     ref = oracle.gemm_nt_f16(A, B)
     for cfg in gf.skinny_configs():
-        if cfg["stages"] == 0:
+        if cfg["stages"] in (0, 1):
             assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
         else:
             with pytest.raises(RuntimeError, match="UNSUPPORTED"):
@@ -470,6 +475,47 @@ def test_skinny_default_shapes(M, N, K):
     assert np.array_equal(run_skinny(A, B), oracle.gemm_nt_f16(A, B))
     A, B = operands("uniform", M, N, K, seed=8)
     check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("K", [11008, 1000, 13824, 8])
+def test_skinny_vector_form_ragged_k(M, K):
+    """The vector form on K with a ragged last step, every launch shape of
+    it, all outputs; infinities in B's last chunks must not reach the
+    padding lanes (an infinite B entry times a padded zero would be NaN)."""
+    N = 300
+    A, B = (x.copy() for x in operands("integer", M, N, K, seed=15))
+    B[::7, -1] = np.float16(np.inf)
+    B[1::7, -1] = np.float16(-np.inf)
+    A[:, -1] = np.float16(1.0)
+    ref = oracle.gemm_nt_f16(A, B)
+    ran = 0
+    for cfg in gf.skinny_configs():
+        if cfg["stages"] != 1:
+            continue
+        _say("skinny vector ragged cfg %s %dx%dx%d" % (cfg, M, N, K))
+        if skinny_runs(cfg, M, K):
+            assert np.array_equal(run_skinny(A, B, cfg), ref), cfg
+            ran += 1
+        else:                                          # A's padded rows exceed the LDS
+            with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+                run_skinny(A, B, cfg)
+    mv = 1 if M <= 1 else (2 if M <= 2 else (4 if M <= 4 else 8))
+    assert ran >= 1 or mv * (K // 8 + 63) // 64 * 64 * 16 > 160 * 1024
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("N,K", [(4096, 11008), (5120, 13824), (8200, 5120)])
+def test_skinny_default_ragged_k(M, N, K):
+    """The vector form where the library picks it with a ragged last step
+    (K not a multiple of 2048), 16 and 8 waves, all outputs."""
+    cfg = gf.skinny_default_config(M, N, K)
+    assert cfg["stages"] == 1 and K % (512 * cfg["unroll"]) != 0
+    A, B = operands("integer", M, N, K, seed=16)
+    _say("skinny ragged default %dx%dx%d cfg %s" % (M, N, K, cfg))
+    assert np.array_equal(run_skinny(A, B), oracle.gemm_nt_f16(A, B))
+    A, B = operands("uniform", M, N, K, seed=16)
+    check_f16_tolerance(run_skinny(A, B), oracle.gemm_nt_f16(A, B), "skinny ragged %dx%dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
