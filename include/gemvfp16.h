@@ -242,8 +242,9 @@ int gemm_f16_cfg(const void* A, const void* B, void* C, int M, int N, int K, int
  *    512-k chunks (needs K % 512 == 0; unroll 0);
  *  - stages = 1, vector form for M <= 8: blocks = rows of B per wave, unroll
  *    = 16-byte chunks per row and lane in flight; B streamed as by gemv_f16,
- *    A staged in LDS (needs K % (512 * unroll) == 0 and M' * K * 2 <= 160 KiB,
- *    M' = M rounded up to 1, 2, 4 or 8);
+ *    A staged in LDS with its rows zero-padded to whole steps of 512 * unroll
+ *    k (needs M' * that padded K * 2 <= 160 KiB, M' = M rounded up to 1, 2,
+ *    4 or 8; a ragged last step multiplies zeros past K);
  *  - stages = -1, split form for M <= 8: gemv_f16's split launch shape (the
  *    waves of a workgroup split K, workgroups walk whole rows of B), A held
  *    in registers; blocks = workgroups at most, unroll = 16-byte chunks per
