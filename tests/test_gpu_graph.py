@@ -3,8 +3,9 @@
 Every entry point only launches kernels on the caller's stream: it allocates
 nothing and records no memset (the atomic split-K clears its output with a
 fill kernel), so a caller can capture it into a graph.  One graph here holds
-the NT and NN products, split-K in all three modes, the GEMV, the 2:4
-compression and the sparse product.  It is replayed three times, with new
+the NT and NN products, split-K in all three modes, the GEMV, the skinny
+GEMM in its split form and in its vector form with a ragged last step, the
+2:4 compression and the sparse product.  It is replayed three times, with new
 input contents copied into the captured buffers before each replay and the
 same calls made eagerly (into other outputs) between replays; each replay's
 outputs must equal the eager ones bit for bit.  Inputs are integers in
@@ -45,6 +46,10 @@ GM, GN, GK = 520, 392, 1024        # GEMM NT and NN
 SM, SN, SK, SPLIT = 264, 200, 4096, 4
 VN, VK = 4100, 2048                # GEMV
 PM, PN, PK = 300, 264, 1024        # 2:4
+KM, KN, KK = 4, 600, 8192          # skinny, split form
+RM, RN, RK = 3, 300, 11008         # skinny, vector form with a ragged last step
+SPLIT_CFG = {"blocks": 512, "unroll": 4, "waves": 4, "stages": -1}
+RAGGED_CFG = {"blocks": 1, "unroll": 4, "waves": 16, "stages": 1}
 
 
 class Buffers:
@@ -56,6 +61,8 @@ class Buffers:
         self.SA, self.SB = z((SM, SK)), z((SN, SK))
         self.W, self.x = z((VN, VK)), z((VK,))
         self.PA, self.PB = z((PM, PK)), z((PN, PK))
+        self.KA, self.KB = z((KM, KK)), z((KN, KK))
+        self.RA, self.RB = z((RM, RK)), z((RN, RK))
         ws_elems = gf.gemm_f16_nt_splitk_workspace_bytes(SM, SN, SPLIT) // 4
         self.ws = [torch.empty(ws_elems, dtype=torch.float32, device="cuda") for _ in range(2)]
         self.out = [self._outputs() for _ in range(2)]     # [0]: graph, [1]: eager
@@ -65,13 +72,15 @@ class Buffers:
         e = lambda shape, dt=torch.float16: torch.empty(shape, dtype=dt, device="cuda")
         return dict(nt=e((GM, GN)), nn=e((GM, GN)), atomic=e((SM, SN), torch.float32),
                     twopass=e((SM, SN), torch.float32), f16=e((SM, SN)), y=e((VN,)),
-                    asp=e((PM, PK // 2)), meta=e((PM, PK // 16), torch.int16), sp=e((PM, PN)))
+                    asp=e((PM, PK // 2)), meta=e((PM, PK // 16), torch.int16), sp=e((PM, PN)),
+                    ks=e((KM, KN)), kr=e((RM, RN)))
 
     def fill(self, seed):
         host = {}
         for name, shape, stream in (("A", (GM, GK), 0), ("B", (GN, GK), 1), ("SA", (SM, SK), 0),
                                     ("SB", (SN, SK), 1), ("W", (VN, VK), 0), ("x", (VK,), 1),
-                                    ("PA", (PM, PK), 0), ("PB", (PN, PK), 1)):
+                                    ("PA", (PM, PK), 0), ("PB", (PN, PK), 1), ("KA", (KM, KK), 0),
+                                    ("KB", (KN, KK), 1), ("RA", (RM, RK), 0), ("RB", (RN, RK), 1)):
             host[name] = inputs.integer_f16(shape, seed, stream)
             getattr(self, name).copy_(dev(host[name]))
         self.Bkn.copy_(dev(np.ascontiguousarray(host["B"].T)))
@@ -87,6 +96,8 @@ class Buffers:
                                  workspace=self.ws[k])
         gf.gemm_f16_nt_splitk_f16(self.SA, self.SB, o["f16"], split_k=SPLIT, workspace=self.ws[k])
         gf.gemv_f16(self.W, self.x, o["y"])
+        gf.gemm_f16_nt_skinny(self.KA, self.KB, o["ks"], cfg=SPLIT_CFG)
+        gf.gemm_f16_nt_skinny(self.RA, self.RB, o["kr"], cfg=RAGGED_CFG)
         gf.sp24_compress_f16(self.PA, o["asp"], o["meta"])
         gf.gemm_sp_f16_nt(o["asp"], o["meta"], self.PB, o["sp"])
 
@@ -125,6 +136,8 @@ def test_graph_capture_and_replay():
         # and the replay computed the new inputs' product, not a stale one
         assert np.array_equal(host_u16(b.out[0]["nt"]), oracle.gemm_nt_f16(host["A"], host["B"]))
         assert np.array_equal(host_u16(b.out[0]["y"]), oracle.gemv_f16(host["W"], host["x"]))
+        assert np.array_equal(host_u16(b.out[0]["ks"]), oracle.gemm_nt_f16(host["KA"], host["KB"]))
+        assert np.array_equal(host_u16(b.out[0]["kr"]), oracle.gemm_nt_f16(host["RA"], host["RB"]))
 
 
 def test_concurrent_streams():
