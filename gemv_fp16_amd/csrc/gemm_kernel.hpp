@@ -118,13 +118,16 @@ struct OperandGeom {
 // Diagnostic build only (build.py --variant timeline): each workgroup of a
 // two-pass split-K launch notes the shader's real-time counter (100 MHz) on
 // entry, once its first K tile has landed, when its main loop ends and after
-// its partial stores, and writes them with its XCC id over the first words of
-// its own partial tile -- the results are then wrong by design.  Compiled out
-// of the library.
+// its partial stores, the shader-clock cycle counter at the first three of
+// those points, and writes them with its XCC id over the first words of its
+// own partial tile -- the results are then wrong by design.  Compiled out of
+// the library.
 #ifdef GF_DIAG_TIMELINE
 #define GF_STAMP(t) ((t) = __builtin_amdgcn_s_memrealtime())
+#define GF_CYCLES(t) ((t) = __builtin_amdgcn_s_memtime())
 #else
 #define GF_STAMP(t) ((void)0)
+#define GF_CYCLES(t) ((void)0)
 #endif
 
 __device__ __forceinline__ int swz_key(int row, int rows_per_key, int ch)
@@ -649,8 +652,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
     typedef typename MF::acc_t acc_t;
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     GF_LDS char* smem = (GF_LDS char*)smem_raw;
-    [[maybe_unused]] uint64_t ts0 = 0, ts1 = 0, ts2 = 0;
+    [[maybe_unused]] uint64_t ts0 = 0, ts1 = 0, ts2 = 0, cy0 = 0, cy1 = 0, cy2 = 0;
     GF_STAMP(ts0);
+    GF_CYCLES(cy0);
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -808,6 +812,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         wait_vmcnt<Cfg::LPS * (S - 2)>();       // tile 0 landed
         lds_barrier();
         GF_STAMP(ts1);
+        GF_CYCLES(cy1);
         if (nk > 0) ld.template issue_range<0, H>(a, stage_ptr(S - 1), k0_of(S - 1), wave);
         fr.template load_all<0>(stage_ptr(0), af[0], bf[0]);
         // Steady state: tiles t + S - 1 and t + S lie wholly inside K, so
@@ -889,6 +894,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
 
     // ---- epilogue ----
     GF_STAMP(ts2);
+    GF_CYCLES(cy2);
     const int wrow0 = m0 + wm * Cfg::WTM, wcol0 = n0 + wn * Cfg::WTN;
     constexpr int MT = Cfg::MT;
 
@@ -962,10 +968,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
         __builtin_amdgcn_s_waitcnt(0);
         uint64_t ts3;
         GF_STAMP(ts3);
-        if (tid == 0 && n0 + 10 <= a.N) {   // five 8-byte words inside the tile's first row
+        if (tid == 0 && n0 + 16 <= a.N) {   // eight 8-byte words inside the tile's first row
             uint64_t* t = (uint64_t*)(W + (size_t)m0 * a.N + n0);
             t[0] = ts0; t[1] = ts1; t[2] = ts2; t[3] = ts3;
             t[4] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+            t[5] = cy0; t[6] = cy1; t[7] = cy2;
         }
 #endif
     }

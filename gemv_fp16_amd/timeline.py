@@ -15,9 +15,10 @@ Per launch it prints, over the workgroups: the span from the first entry to
 the last partial store, the skew of the entries (a second wave of workgroups
 starts when the first one leaves), the prologue (entry until the first K tile
 has landed: only the schedule-2 pipeline notes that point), the main loop,
-the epilogue (partial stores until they have left the CU), and the main
-loop's matrix-core share at a stated clock: its MFMA cycles (32 per 32 x 32
-MFMA, per SIMD) over the loop's duration.
+the epilogue (partial stores until they have left the CU), the shader clock
+over the main loop (shader-cycle counter over real time), the loop's shader
+cycles per K tile, and its matrix-core share: its MFMA cycles (32 per
+32 x 32 MFMA, per SIMD) over those cycles.
 """
 from __future__ import annotations
 
@@ -33,7 +34,7 @@ CONFIGS = ((8, (256, 128, 64, 3, 256, 2)), (4, (256, 128, 64, 3, 256, 2)), (16, 
            (4, (128, 128, 64, 4, 256, 2)), (8, (128, 128, 64, 4, 256, 2)))
 
 
-def run(split, cfg, As, Bs, C32, clock_ghz):
+def run(split, cfg, As, Bs, C32):
     import numpy as np
     import torch
     import gemv_fp16_amd as gf
@@ -46,21 +47,24 @@ def run(split, cfg, As, Bs, C32, clock_ghz):
     torch.cuda.synchronize()
     w = ws.view(split, M, N).cpu().numpy()
     bm, bn, bk = cfg[0], cfg[1], cfg[2]
-    rec = np.array([w[s, tm * bm, tn * bn:tn * bn + 10].view(np.uint64).astype(np.int64)
+    rec = np.array([w[s, tm * bm, tn * bn:tn * bn + 16].view(np.uint64).astype(np.int64)
                     for s in range(split) for tm in range(M // bm) for tn in range(N // bn)])
     t0 = rec[:, 0].min()
     start, first, mend, end = ((rec[:, j] - t0) / 100.0 for j in range(4))   # microseconds
     xcc = rec[:, 4]
-    loop = mend - first if rec[:, 1].min() > 0 else mend - start
+    staged = rec[:, 1].min() > 0
+    loop = mend - first if staged else mend - start
+    loop_cycles = (rec[:, 7] - rec[:, 6]) if staged else (rec[:, 7] - rec[:, 5])
+    clock = loop_cycles / (loop * 1e3)                                       # GHz
     ksteps = K // split // bk
-    waves = cfg[4] // 64
-    mfma_cycles = (bm * bn * bk) // (32 * 32 * 16) // waves * 32 * ksteps   # per SIMD (one wave each)
-    busy = mfma_cycles / (np.median(loop) * 1e-6 * clock_ghz * 1e9)
-    row = "| %d | %s | %d | %.1f | %.1f | %s | %.1f (%.1f-%.1f) | %.2f | %.0f %% | %s |" % (
+    # matrix-core cycles per SIMD and K tile: 2 bm bn bk flops at 1024 per cycle and SIMD, 4 SIMDs
+    mfma_cycles = 2 * bm * bn * bk / 1024 / 4
+    per_tile = np.median(loop_cycles) / ksteps
+    row = "| %d | %s | %d | %.1f | %.1f | %s | %.1f (%.1f-%.1f) | %.2f | %.2f (%.2f-%.2f) | %.0f | %.0f %% | %s |" % (
         split, "x".join(map(str, cfg[:3])) + " S%d sched %d" % (cfg[3], cfg[5]), len(rec), end.max(), start.max(),
-        "%.2f" % np.median(first - start) if rec[:, 1].min() > 0 else "-", np.median(loop), loop.min(), loop.max(),
-        np.median(end - mend), 100 * busy, " ".join("%d:%.1f" % (x, end[xcc == x].max()) for x in range(8)
-                                                    if (xcc == x).any()))
+        "%.2f" % np.median(first - start) if staged else "-", np.median(loop), loop.min(), loop.max(),
+        np.median(end - mend), np.median(clock), clock.min(), clock.max(), per_tile, 100 * mfma_cycles / per_tile,
+        " ".join("%d:%.1f" % (x, end[xcc == x].max()) for x in range(8) if (xcc == x).any()))
     return row
 
 
@@ -68,8 +72,6 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--split", type=int, default=0, help="one run at this split (with --cfg)")
     ap.add_argument("--cfg", default="", help="block_m,block_n,block_k,stages,threads,schedule")
-    ap.add_argument("--clock-ghz", type=float, default=2.2,
-                    help="shader clock used for the matrix-core share (the split-K pass runs near 2.2 GHz)")
     a = ap.parse_args(argv)
     if not os.path.exists(VARIANT):
         raise SystemExit("build the diagnostic library first: python -m gemv_fp16_amd.build --variant timeline")
@@ -88,10 +90,11 @@ def main(argv=None):
     C32 = torch.empty((1024, 1024), dtype=torch.float32, device="cuda")
     runs = ((a.split, tuple(int(t) for t in a.cfg.split(","))),) if a.split else CONFIGS
     print("| split | tile | WGs | span us | entry skew us | prologue us | main loop us median (min-max) "
-          "| epilogue us | MFMA share of loop at %.1f GHz | last store per XCC, us |" % a.clock_ghz)
-    print("|---|---|---|---|---|---|---|---|---|---|")
+          "| epilogue us | loop clock GHz median (min-max) | loop cycles per K tile | MFMA share of those cycles "
+          "| last store per XCC, us |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
     for split, cfg in runs:
-        print(run(split, cfg, As, Bs, C32, a.clock_ghz), flush=True)
+        print(run(split, cfg, As, Bs, C32), flush=True)
 
 
 if __name__ == "__main__":
