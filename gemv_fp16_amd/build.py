@@ -127,9 +127,9 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)
-    # Diagnostics (not linked into the library): the HBM streaming-read and
-    # the MFMA throughput ceiling probes.
-    for name in ("readbw", "mfmapeak"):
+    # Diagnostics (not linked into the library): the HBM streaming-read, the
+    # MFMA throughput and the LDS throughput ceiling probes.
+    for name in ("readbw", "mfmapeak", "ldsbw"):
         probe = os.path.join(PKG, name)
         cmd = [HIPCC] + [f for f in FLAGS if f != "-fPIC"] + [os.path.join(CSRC, name + ".hip"), "-o",
                                                             probe + ".tmp"]

@@ -116,12 +116,12 @@ struct OperandGeom {
 };
 
 // Diagnostic build only (build.py --variant timeline): each workgroup of a
-// two-pass split-K launch notes the shader's real-time counter (100 MHz) on
-// entry, once its first K tile has landed, when its main loop ends and after
-// its partial stores, the shader-clock cycle counter at the first three of
-// those points, and writes them with its XCC id over the first words of its
-// own partial tile -- the results are then wrong by design.  Compiled out of
-// the library.
+// two-pass split-K launch or an fp16 GEMM notes the shader's real-time
+// counter (100 MHz) on entry, once its first K tile has landed, when its main
+// loop ends and after its stores, the shader-clock cycle counter at the first
+// three of those points, and writes them with its XCC id over the first words
+// of its own partial or output tile -- the results are then wrong by design.
+// Compiled out of the library.
 #ifdef GF_DIAG_TIMELINE
 #define GF_STAMP(t) ((t) = __builtin_amdgcn_s_memrealtime())
 #define GF_CYCLES(t) ((t) = __builtin_amdgcn_s_memtime())
@@ -937,6 +937,19 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nt_kernel(GemmArgs a)
                         C[(size_t)grow * a.N + gcol + e] = (uint16_t)(parts[e / 2] >> (16 * (e % 2)));
             }
         }
+#ifdef GF_DIAG_TIMELINE
+        // The tile's first 32 outputs of row m0 are this wave's (wave 0's
+        // sub-tile); once its stores are done the stamps overwrite them.
+        __builtin_amdgcn_s_waitcnt(0);
+        uint64_t ts3;
+        GF_STAMP(ts3);
+        if (tid == 0 && n0 + 32 <= a.N && ((size_t)m0 * a.N + n0) % 4 == 0) {
+            uint64_t* t = (uint64_t*)(C + (size_t)m0 * a.N + n0);
+            t[0] = ts0; t[1] = ts1; t[2] = ts2; t[3] = ts3;
+            t[4] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+            t[5] = cy0; t[6] = cy1; t[7] = cy2;
+        }
+#endif
     } else if constexpr (EPI == EPI_F32_ATOMIC) {
         if (nk == 0) return;                     // an empty slice adds nothing
         float* C = (float*)a.C;

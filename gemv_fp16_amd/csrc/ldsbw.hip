@@ -1,0 +1,121 @@
+// LDS throughput ceiling probe: a diagnostic program, not part of the
+// library.  One workgroup of 4 waves on each of 256 CUs moves a fixed mix of
+// LDS traffic per iteration, with no matrix-core work.  The mix has three
+// parts:
+//   * 128-bit reads (ds_read_b128), conflict-free: 64 lanes x 16 consecutive
+//     bytes;
+//   * direct-to-LDS 128-bit loads (buffer_load_dwordx4 ... lds) from a 64 KiB
+//     global buffer that stays in L2;
+//   * 128-bit writes from registers (ds_write_b128).
+// Each wave waits per iteration for its LDS operations and for the previous
+// iteration's loads.  Cycles come from the shader-clock counter (s_memtime)
+// of wave 0: the median over workgroups, the median of 5 launches.
+// The mixes of interest are those of a GEMM K tile (64 deep) on a CU whose 4
+// waves form a 2 x 2 grid:
+//   * 256 x 128 tile: 96 KiB of fragment reads and 48 KiB of staged operands;
+//   * 256 x 256 tile: 128 KiB and 64 KiB.
+// Each mix is run both ways, staged by the direct path and by register
+// writes.  Usage: ./ldsbw
+#include <hip/hip_runtime.h>
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#define CK(x)                                                                            \
+    do {                                                                                 \
+        hipError_t e_ = (x);                                                             \
+        if (e_ != hipSuccess) {                                                          \
+            printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__);       \
+            exit(1);                                                                     \
+        }                                                                                \
+    } while (0)
+#define LDS_AS __attribute__((address_space(3)))
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLdsBytes = 160 * 1024;   // reads in [0, 32 KiB); each wave's stores in its own 32 KiB above
+constexpr int kSrcBytes = 64 * 1024;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+// Per iteration and wave: NR reads, ND direct-to-LDS loads, NW register writes (1 KiB each).
+template <int NR, int ND, int NW>
+__global__ __launch_bounds__(256) void lds_mix(const char* __restrict__ src, unsigned long long* out, int iters)
+{
+    static_assert(NR <= 32 && ND <= 32 && NW <= 32, "distinct 1 KiB slots per wave");
+    extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+    LDS_AS char* smem = (LDS_AS char*)smem_raw;
+    const int lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, kSrcBytes, 0x00020000);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const u32x4 wv = {(unsigned)lane, 1u, 2u, 3u};
+    LDS_AS char* rbase = smem + lane * 16;
+    LDS_AS char* sbase = smem + 32768 + wave * 32768;
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) acc ^= *(const LDS_AS u32x4*)(rbase + ((i + 8 * wave + it) % 32) * 1024);
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(sbase + i * 1024), 16, (uint32_t)(lane * 16),
+                                                     (uint32_t)(((i + it) % 64) * 1024), 0, 0);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) *(LDS_AS u32x4*)(sbase + i * 1024 + lane * 16) = wv + (unsigned)(i + it);
+        if (ND > 0) wait_vmcnt<ND>();   // the previous iteration's loads have landed
+        wait_lgkmcnt0();
+        asm volatile("" ::: "memory");
+    }
+    wait_vmcnt<0>();
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+    if (threadIdx.x == 0) out[blockIdx.x * 2] = c1 - c0;
+    if (acc.x == 0xdeadbeefu && acc.y == 1u) out[blockIdx.x * 2 + 1] = acc.z;   // keeps the reads live
+}
+
+template <int NR, int ND, int NW>
+void run(const char* label, const char* src, unsigned long long* dout, int iters)
+{
+    auto kern = lds_mix<NR, ND, NW>;
+    CK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
+    std::vector<double> per_launch;
+    for (int r = 0; r < 5; ++r) {
+        hipLaunchKernelGGL(kern, dim3(256), dim3(256), kLdsBytes, 0, src, dout, iters);
+        CK(hipGetLastError());
+        CK(hipDeviceSynchronize());
+        std::vector<unsigned long long> h(512);
+        CK(hipMemcpy(h.data(), dout, h.size() * 8, hipMemcpyDeviceToHost));
+        std::vector<double> c;
+        for (int i = 0; i < 256; ++i) c.push_back((double)h[2 * i]);
+        std::sort(c.begin(), c.end());
+        per_launch.push_back(c[128]);
+    }
+    std::sort(per_launch.begin(), per_launch.end());
+    const double cyc = per_launch[2] / iters;
+    const double rb = 4.0 * NR * 1024, db = 4.0 * ND * 1024, wb = 4.0 * NW * 1024;   // bytes per iteration and CU
+    printf("%-34s reads %3d KiB, direct %2d KiB, writes %2d KiB per CU: %7.1f cycles, %5.1f B per cycle\n", label,
+           (int)(rb / 1024), (int)(db / 1024), (int)(wb / 1024), cyc, (rb + db + wb) / cyc);
+    fflush(stdout);
+}
+
+int main()
+{
+    char* src;
+    unsigned long long* dout;
+    CK(hipMalloc(&src, kSrcBytes));
+    CK(hipMemset(src, 3, kSrcBytes));
+    CK(hipMalloc(&dout, 512 * sizeof(unsigned long long)));
+    const int iters = 2000;
+    run<24, 0, 0>("reads only", src, dout, iters);
+    run<0, 12, 0>("direct-to-LDS loads only", src, dout, iters);
+    run<0, 0, 12>("register writes only", src, dout, iters);
+    run<24, 12, 0>("256x128 K tile, direct staging", src, dout, iters);
+    run<24, 0, 12>("256x128 K tile, register staging", src, dout, iters);
+    run<32, 16, 0>("256x256 K tile, direct staging", src, dout, iters);
+    run<32, 0, 16>("256x256 K tile, register staging", src, dout, iters);
+    run<16, 8, 0>("128x128 K tile, direct staging", src, dout, iters);
+    return 0;
+}
