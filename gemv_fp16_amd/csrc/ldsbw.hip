@@ -6,7 +6,9 @@
 //     bytes;
 //   * direct-to-LDS 128-bit loads (buffer_load_dwordx4 ... lds) from a 64 KiB
 //     global buffer that stays in L2;
-//   * 128-bit writes from registers (ds_write_b128).
+//   * 128-bit writes from registers (ds_write_b128);
+//   * 128-bit loads of the same buffer into registers (buffer_load_dwordx4),
+//     consumed one iteration later.
 // Each wave waits per iteration for its LDS operations and for the previous
 // iteration's loads.  Cycles come from the shader-clock counter (s_memtime)
 // of wave 0: the median over workgroups, the median of 5 launches.
@@ -14,8 +16,9 @@
 // waves form a 2 x 2 grid:
 //   * 256 x 128 tile: 96 KiB of fragment reads and 48 KiB of staged operands;
 //   * 256 x 256 tile: 128 KiB and 64 KiB.
-// Each mix is run both ways, staged by the direct path and by register
-// writes.  Usage: ./ldsbw
+// Each mix is run with its operands staged by the direct path and by
+// register writes, and with one operand fed straight into registers (a 4 x 1
+// wave grid whose waves own their rows of A).  Usage: ./ldsbw
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <cstdio>
@@ -43,11 +46,12 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
-// Per iteration and wave: NR reads, ND direct-to-LDS loads, NW register writes (1 KiB each).
-template <int NR, int ND, int NW>
+// Per iteration and wave: NR reads, ND direct-to-LDS loads, NW register
+// writes, NV loads into registers (1 KiB each).
+template <int NR, int ND, int NW, int NV>
 __global__ __launch_bounds__(256) void lds_mix(const char* __restrict__ src, unsigned long long* out, int iters)
 {
-    static_assert(NR <= 32 && ND <= 32 && NW <= 32, "distinct 1 KiB slots per wave");
+    static_assert(NR <= 32 && ND <= 32 && NW <= 32 && NV <= 32, "distinct 1 KiB slots per wave");
     extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
     LDS_AS char* smem = (LDS_AS char*)smem_raw;
     const int lane = threadIdx.x % 64, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -56,6 +60,9 @@ __global__ __launch_bounds__(256) void lds_mix(const char* __restrict__ src, uns
     const u32x4 wv = {(unsigned)lane, 1u, 2u, 3u};
     LDS_AS char* rbase = smem + lane * 16;
     LDS_AS char* sbase = smem + 32768 + wave * 32768;
+    u32x4 g[NV > 0 ? NV : 1];
+#pragma unroll
+    for (int i = 0; i < (NV > 0 ? NV : 1); ++i) g[i] = wv;
     const unsigned long long c0 = __builtin_amdgcn_s_memtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -66,20 +73,27 @@ __global__ __launch_bounds__(256) void lds_mix(const char* __restrict__ src, uns
                                                      (uint32_t)(((i + it) % 64) * 1024), 0, 0);
 #pragma unroll
         for (int i = 0; i < NW; ++i) *(LDS_AS u32x4*)(sbase + i * 1024 + lane * 16) = wv + (unsigned)(i + it);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc ^= g[i];   // the previous iteration's register loads
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            g[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(lane * 16), (uint32_t)(((i + it + 32) % 64) * 1024), 0);
         if (ND > 0) wait_vmcnt<ND>();   // the previous iteration's loads have landed
         wait_lgkmcnt0();
         asm volatile("" ::: "memory");
     }
     wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc ^= g[i];
     const unsigned long long c1 = __builtin_amdgcn_s_memtime();
     if (threadIdx.x == 0) out[blockIdx.x * 2] = c1 - c0;
     if (acc.x == 0xdeadbeefu && acc.y == 1u) out[blockIdx.x * 2 + 1] = acc.z;   // keeps the reads live
 }
 
-template <int NR, int ND, int NW>
+template <int NR, int ND, int NW, int NV = 0>
 void run(const char* label, const char* src, unsigned long long* dout, int iters)
 {
-    auto kern = lds_mix<NR, ND, NW>;
+    auto kern = lds_mix<NR, ND, NW, NV>;
     CK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
     std::vector<double> per_launch;
     for (int r = 0; r < 5; ++r) {
@@ -95,9 +109,11 @@ void run(const char* label, const char* src, unsigned long long* dout, int iters
     }
     std::sort(per_launch.begin(), per_launch.end());
     const double cyc = per_launch[2] / iters;
-    const double rb = 4.0 * NR * 1024, db = 4.0 * ND * 1024, wb = 4.0 * NW * 1024;   // bytes per iteration and CU
-    printf("%-34s reads %3d KiB, direct %2d KiB, writes %2d KiB per CU: %7.1f cycles, %5.1f B per cycle\n", label,
-           (int)(rb / 1024), (int)(db / 1024), (int)(wb / 1024), cyc, (rb + db + wb) / cyc);
+    // bytes per iteration and CU
+    const double rb = 4.0 * NR * 1024, db = 4.0 * ND * 1024, wb = 4.0 * NW * 1024, vb = 4.0 * NV * 1024;
+    printf("%-40s reads %3d KiB, direct %2d KiB, writes %2d KiB, register loads %2d KiB per CU: %7.1f cycles, "
+           "%5.1f B per cycle\n", label, (int)(rb / 1024), (int)(db / 1024), (int)(wb / 1024), (int)(vb / 1024), cyc,
+           (rb + db + wb + vb) / cyc);
     fflush(stdout);
 }
 
@@ -117,5 +133,9 @@ int main()
     run<32, 16, 0>("256x256 K tile, direct staging", src, dout, iters);
     run<32, 0, 16>("256x256 K tile, register staging", src, dout, iters);
     run<16, 8, 0>("128x128 K tile, direct staging", src, dout, iters);
+    run<0, 0, 0, 12>("register loads only", src, dout, iters);
+    run<0, 6, 0, 6>("direct and register loads, half each", src, dout, iters);
+    run<24, 0, 0, 12>("reads and register loads", src, dout, iters);
+    run<16, 4, 0, 8>("256x128 K tile, 4x1 grid, A in registers", src, dout, iters);
     return 0;
 }
