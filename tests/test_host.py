@@ -1,6 +1,6 @@
 """Host-side logic on the CPU: the sweep's correctness gate, its resumable
-record file and config filter, and the benchmark's source hash, traffic
-lookup and refusal of more than one GPU."""
+record file and config filter, the benchmark's source hash, traffic lookup
+and refusal of more than one GPU, and the timeline tool's arithmetic."""
 import json
 import os
 import shutil
@@ -205,3 +205,27 @@ def test_compare_config_parsing():
     assert sweep._cfg_from("gemv", "1,4,4,512", {}) == {"rows_per_wave": 1, "unroll": 4, "waves": 4, "blocks": 512}
     with pytest.raises(SystemExit):
         sweep._cfg_from("sparse", "128,256,3", {})
+
+
+def test_timeline_row_reads_the_stamps():
+    """The timeline tool's row from synthetic stamps: two workgroups whose
+    main loops run 10 us (real-time counter, 100 MHz) over 15000 shader
+    cycles, i.e. 1.5 GHz, across 32 K tiles of a 256 x 128 x 64 tile."""
+    import numpy as np
+    from gemv_fp16_amd import timeline
+    rec = np.array([
+        # entry, first tile landed, loop end, stores done, XCC, cycles at entry, first tile, loop end
+        [1000, 1200, 2200, 2300, 3, 50000, 52000, 67000],
+        [1010, 1210, 2210, 2350, 5, 80000, 82000, 97000],
+    ], dtype=np.int64)
+    cfg = (256, 128, 64, 3, 256, 2)
+    cells = [c.strip() for c in timeline.row("8", cfg, rec, 32 * 64).strip("|").split("|")]
+    assert cells[0] == "8" and cells[1] == "256x128x64 S3 sched 2" and cells[2] == "2"
+    assert cells[3] == "13.5"                    # span: last store 2350 - first entry 1000, in us
+    assert cells[5] == "2.00"                    # prologue: entry to first tile, 200 ticks
+    assert cells[6].startswith("10.0 ")          # main loop 1000 ticks = 10 us
+    assert cells[8].startswith("1.50 ")          # 15000 cycles over 10 us
+    assert cells[9] == "469"                     # 15000 cycles / 32 K tiles
+    # 2 * 256 * 128 * 64 flops at 1024 per cycle and SIMD over 4 SIMDs = 1024 cycles per K tile
+    assert cells[10] == "%.0f %%" % (100 * 1024 / (15000 / 32))
+    assert cells[11] == "3:13.0 5:13.5"
