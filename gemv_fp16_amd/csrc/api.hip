@@ -60,8 +60,12 @@ gf_gemm_cfg make_cfg(int bm, int bn, int bk, int s, int t, int raster, int sched
 //    - K > 1536: 256 x 256 x 64, two stages, one wave per SIMD (schedule 2),
 //      first in the sweeps at M = N = 8192 for K = 4096 and 8192 and up to
 //      4 % ahead of the 8-wave kernel side by side; grouped, XCD-aware tile
-//      order up to K = 4096 (5 % ahead at K = 1024, tied at 4096), plain
-//      order above, where the two are within noise.
+//      order (panels of 10 tile-rows) up to K = 4096 (5 % ahead at K = 1024,
+//      tied at 4096), plain order up to K = 12288 (at 8192 panels of 2-10
+//      rows are 0.2-1.8 % behind it, at 12288 all within noise), and from
+//      K = 16384 the XCD-aware order with panels of 4 tile-rows, which makes
+//      each XCD's share one panel (1.7-2.0 % ahead of the plain order at
+//      16384 in three side-by-side runs; 0.3 % at 32768).
 //    - K <= 1536 (timed at K = 128 .. 4096 on 8192^2, and at 4096^2, 6144^2,
 //      8192 x 4096 and 16384 x 8192): 512-thread tiles.  Up to K = 512 the
 //      C write outweighs the operand reads (8x at K = 256), and tiles that
@@ -94,7 +98,7 @@ gf_gemm_cfg default_gemm_cfg(int M, int N, int K)
         if (K <= 256 && t12825 >= 1024) return make_cfg(128, 256, 32, 3, 512, 0);
         if (K <= 512) return make_cfg(256, 128, 64, 1, 512, 0);
         if (K <= 1536) return make_cfg(256, 256, 64, 2, 512, 0);
-        return make_cfg(256, 256, 64, 2, 256, K <= 4096 ? 1 : 0, 2);
+        return make_cfg(256, 256, 64, 2, 256, K <= 4096 ? 1 : (K < 16384 ? 0 : 4), 2);
     }
     if (t25612 >= 256 && K >= 2048) return make_cfg(256, 128, 64, 3, 256, 0, 2);
     if (t128 >= 128 && t128 <= 256)

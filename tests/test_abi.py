@@ -265,6 +265,10 @@ def test_config_tables(L):
         if c["schedule"] in (2, 3):
             assert c["threads"] == 256
     assert d["raster"] in (0, 1)
+    # tile order of the one-wave-per-SIMD 256 x 256 kernel: grouped (panels of
+    # 10 rows) to K = 4096, plain to K = 12288, panels of 4 rows from 16384
+    assert [gf.gemm_default_config(8192, 8192, k)["raster"] for k in (2048, 4096, 8192, 12288, 16384, 32768)] == \
+        [1, 1, 0, 0, 4, 4]
     dg = gf.gemv_default_config(8192, 8192)
     assert {**dg, "blocks": 0} in gf.gemv_configs() and dg["blocks"] >= 0
     assert dg["blocks"] > 0                                # tall W, K % 8192 == 0: the split form

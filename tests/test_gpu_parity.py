@@ -190,6 +190,21 @@ def test_gemm_8192_sampled(K):
     check_f16_tolerance(got[ij[:, 0], ij[:, 1]], ref16, "8192x8192x%d" % K)
 
 
+def test_gemm_tile_order_leaves_every_output_unchanged():
+    """The default at M = N = 8192, K = 16384 walks the tiles in panels of 4
+    tile-rows; every tile is computed the same way in any order, so every
+    output equals the plain order's bit for bit."""
+    M = N = 8192
+    K = 16384
+    A, B = operands("uniform", M, N, K)
+    d = gf.gemm_default_config(M, N, K)
+    assert d["raster"] == 4
+    _say("gemm 8192x8192x16384 default order against plain order")
+    got = run_gemm(A, B)
+    plain = run_gemm(A, B, cfg={**d, "raster": 0})
+    assert np.array_equal(got, plain)
+
+
 def test_gemm_8192_integer_sampled():
     M = N = K = 8192
     A, B = operands("integer", M, N, K)
