@@ -3,7 +3,7 @@
 
     python -m gemv_fp16_amd.build --variant timeline     # once, on any machine
     python -m gemv_fp16_amd.timeline [--split 8 --cfg 256,128,64,3,256,2]
-    python -m gemv_fp16_amd.timeline --gemm 8192,8192,8192 [--cfg ...,raster]
+    python -m gemv_fp16_amd.timeline --gemm 8192,8192,8192 [--cfg ...,raster] [--per-xcd]
 
 Loads gemv_fp16_amd/variants/timeline/libgemvfp16.so, in which every
 workgroup of a two-pass split-K launch stamps the shader's 100 MHz real-time
@@ -81,7 +81,27 @@ def run_gemm(shape, cfg):
     bm, bn = cfg[0], cfg[1]
     rec = np.array([w[tm * bm, tn * bn:tn * bn + 32].view(np.uint64).astype(np.int64)
                     for tm in range(M // bm) for tn in range(N // bn)])
-    return row("-", cfg, rec, K)
+    return row("-", cfg, rec, K), per_xcd(rec, K, cfg[2])
+
+
+def per_xcd(rec, kext, bk):
+    """Per-XCC lines from the same stamps: workgroups, last store, median main loop, median loop
+    clock and median loop cycles per K tile."""
+    import numpy as np
+    t0 = rec[:, 0].min()
+    start, first, mend, end = ((rec[:, j] - t0) / 100.0 for j in range(4))
+    staged = rec[:, 1].min() > 0
+    loop = mend - first if staged else mend - start
+    cyc = (rec[:, 7] - rec[:, 6]) if staged else (rec[:, 7] - rec[:, 5])
+    out = ["| XCC | WGs | last store us | main loop us (median) | loop clock GHz (median) | loop cycles per K tile (median) |",
+           "|---|---|---|---|---|---|"]
+    for x in range(8):
+        m = rec[:, 4] == x
+        if m.any():
+            out.append("| %d | %d | %.1f | %.1f | %.3f | %.0f |" % (
+                x, m.sum(), end[m].max(), np.median(loop[m]), np.median(cyc[m] / (loop[m] * 1e3)),
+                np.median(cyc[m]) / (kext // bk)))
+    return "\n".join(out)
 
 
 def row(split, cfg, rec, kext):
@@ -112,6 +132,7 @@ def main(argv=None):
     ap.add_argument("--split", type=int, default=0, help="one run at this split (with --cfg)")
     ap.add_argument("--cfg", default="", help="block_m,block_n,block_k,stages,threads,schedule[,raster]")
     ap.add_argument("--gemm", default="", help="M,N,K: time a plain fp16 GEMM instead of the split-K pass")
+    ap.add_argument("--per-xcd", action="store_true", help="with --gemm: also one line per XCC")
     a = ap.parse_args(argv)
     if not os.path.exists(VARIANT):
         raise SystemExit("build the diagnostic library first: python -m gemv_fp16_amd.build --variant timeline")
@@ -132,7 +153,10 @@ def main(argv=None):
         cfg = tuple(int(t) for t in a.cfg.split(",")) if a.cfg else None
         if cfg is not None and len(cfg) == 6:
             cfg = cfg + (0,)
-        print(run_gemm(shape, cfg), flush=True)
+        line, xcd = run_gemm(shape, cfg)
+        print(line, flush=True)
+        if a.per_xcd:
+            print("\n" + xcd, flush=True)
         return
     A0 = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, inputs.STREAM_A)).cuda()
     B0 = torch.from_numpy(inputs.uniform_f16((1024, 16384), 0, inputs.STREAM_B)).cuda()

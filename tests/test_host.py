@@ -229,3 +229,16 @@ def test_timeline_row_reads_the_stamps():
     # 2 * 256 * 128 * 64 flops at 1024 per cycle and SIMD over 4 SIMDs = 1024 cycles per K tile
     assert cells[10] == "%.0f %%" % (100 * 1024 / (15000 / 32))
     assert cells[11] == "3:13.0 5:13.5"
+
+
+def test_timeline_per_xcd_lines():
+    """One line per XCC from the same stamps: clock and cycles per K tile."""
+    import numpy as np
+    from gemv_fp16_amd import timeline
+    rec = np.array([
+        [1000, 1200, 2200, 2300, 3, 50000, 52000, 67000],
+        [1010, 1210, 2210, 2350, 5, 80000, 82000, 97000],
+    ], dtype=np.int64)
+    lines = timeline.per_xcd(rec, 32 * 64, 64).splitlines()
+    assert lines[2] == "| 3 | 1 | 13.0 | 10.0 | 1.500 | 469 |"
+    assert lines[3] == "| 5 | 1 | 13.5 | 10.0 | 1.500 | 469 |"
